@@ -1,0 +1,146 @@
+/*
+ * moe_w4a16.h — C ABI of the routed Mixture-of-Experts FFN under W4A16 on
+ * AMD MI355X (gfx950).
+ *
+ * What the library computes (the Chimera notebook "Qwen3.6-35B-A3B Decode on
+ * Chimera GPNPU", section 5 "Validate the MoE FFN block"): for every token x,
+ *
+ *     out = routed(x) + sigmoid(x . W_sg) * shared(x)
+ *
+ *   - router logits l = x . W_r^T over E experts; the router rows are stored
+ *     int8 with binary16 group-64 scales, stacked with the shared-gate row W_sg
+ *     as row E (the TensorFold PR "Qwen3.6-35B-A3B on Metal on the routed
+ *     path", section "Design");
+ *   - softmax over the E logits, keep the top k, renormalise the k kept
+ *     probabilities (the Chimera notebook, section 5.2); ties go to the lower
+ *     expert index;
+ *   - routed(x) = sum_i w_i * FFN_{e_i}(x) with SwiGLU experts
+ *     FFN(x) = (silu(x W_gate^T) * (x W_up^T)) W_down^T, int4 weights
+ *     (the Chimera notebook, pipeline intro: routed experts int4);
+ *   - shared(x) is a dense SwiGLU expert with int8 weights, applied to every
+ *     token (same notebook: shared expert int8, activations fp16).
+ *
+ * Storage format (every weight array is row-major, K-contiguous):
+ *   - int4 code: two's-complement nibble in [-8, 7]; element 2j of a row is
+ *     the low nibble of byte j, element 2j+1 the high nibble;
+ *   - int8 code: two's complement;
+ *   - scales: IEEE binary16 bit patterns, one per 64 consecutive K elements of
+ *     a row ([rows][K/64]); dequantised weight = code * scale (no zero point);
+ *   - activations x and out: IEEE binary16 [T][H].
+ *
+ * Conventions for every entry point:
+ *   - `dims` and `w` are host pointers to host structs; every array pointer
+ *     inside `w` and every other array argument is a DEVICE pointer of the
+ *     current HIP device, owned by the caller.  The library never allocates,
+ *     frees, copies host<->device or synchronises.
+ *   - Work is enqueued on `stream` (0 = the null stream) and the call returns
+ *     immediately; results are ready when the stream reaches that point.
+ *   - Every argument is validated before anything is enqueued: a call that
+ *     returns an error has enqueued nothing and changed nothing.
+ *   - T = 0 is a valid no-op (returns MOE_OK, enqueues nothing).
+ *   - Alignment: weight arrays, x and out 16 bytes; ids, routing weights,
+ *     sigma and logits 4 bytes; the workspace 256 bytes.
+ *   - Shape admission: G = 64; 1 <= k <= E <= 256 and k <= 8; each of H, I and
+ *     Is is 64 * 2^m or a multiple of 2048, and at most 4096; 0 <= T <= 65536.
+ *   - The workspace (`ws`, `ws_bytes` >= moe_workspace_bytes(dims, T)) is
+ *     scratch owned by the caller.  Its first 1024 bytes hold counters that
+ *     must be zero before the first call that uses the workspace (allocate it
+ *     zero-filled); every completed call leaves them zero.  Calls that share a
+ *     workspace must be ordered (same stream, or synchronised).
+ *   - Device-side routing ids outside [0, E) passed to moe_experts_w4a16
+ *     contribute nothing (they are never dereferenced).
+ */
+#ifndef MOE_W4A16_H
+#define MOE_W4A16_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#if defined(__GNUC__)
+#define MOE_API __attribute__((visibility("default")))
+#else
+#define MOE_API
+#endif
+
+/* status codes */
+#define MOE_OK 0
+#define MOE_ERR_NULL (-1)      /* a required pointer is NULL */
+#define MOE_ERR_SHAPE (-2)     /* dims or T outside the admitted shapes */
+#define MOE_ERR_ALIGN (-3)     /* a pointer is not aligned as required */
+#define MOE_ERR_WORKSPACE (-4) /* ws_bytes < moe_workspace_bytes(dims, T) */
+#define MOE_ERR_LAUNCH (-5)    /* the HIP runtime refused a launch */
+#define MOE_ERR_DEVICE (-6)    /* the current device is not gfx950 or cannot be queried */
+
+/* dims.flags: execution path (both compute the same result) */
+#define MOE_PATH_AUTO 0u   /* few tokens: persistent GEMV launch; otherwise grouped MFMA GEMMs */
+#define MOE_PATH_DECODE 1u /* force the few-token path (T <= 4) */
+#define MOE_PATH_CHUNK 2u  /* force the grouped-GEMM path */
+
+typedef struct {
+  int32_t hidden;       /* H */
+  int32_t num_experts;  /* E */
+  int32_t top_k;        /* k */
+  int32_t expert_inter; /* I: routed-expert intermediate width */
+  int32_t shared_inter; /* Is: shared-expert intermediate width */
+  int32_t group;        /* G: quantisation group along K, must be 64 */
+  uint32_t flags;       /* MOE_PATH_* */
+} moe_dims;
+
+typedef struct {
+  const int8_t* router_q;   /* [E+1][H] int8; row E is the shared-gate row */
+  const uint16_t* router_s; /* [E+1][H/G] binary16 */
+  const uint8_t* w13_q;     /* [E][2I][H/2] int4 pairs; rows 0..I-1 gate, I..2I-1 up */
+  const uint16_t* w13_s;    /* [E][2I][H/G] */
+  const uint8_t* w2_q;      /* [E][H][I/2] int4 pairs (down projection) */
+  const uint16_t* w2_s;     /* [E][H][I/G] */
+  const int8_t* sh13_q;     /* [2Is][H] int8; rows 0..Is-1 gate, Is..2Is-1 up */
+  const uint16_t* sh13_s;   /* [2Is][H/G] */
+  const int8_t* sh2_q;      /* [H][Is] int8 */
+  const uint16_t* sh2_s;    /* [H][Is/G] */
+} moe_weights;
+
+/* Bytes of workspace a call with these dims and T tokens needs (any entry
+ * point).  Returns 0 for inadmissible dims. */
+MOE_API size_t moe_workspace_bytes(const moe_dims* dims, int32_t T);
+
+/* Router alone (the Chimera notebook, section 5: the router validated on its
+ * own): logits of the E experts and of the shared gate, top-k selection,
+ * renormalised weights and the shared-expert gate value.
+ *   x            [T][H] binary16
+ *   ids          [T][k] int32, experts in descending logit order (ties: lower index)
+ *   w            [T][k] float, renormalised weights, same order
+ *   shared_gate  [T] float, sigmoid of the shared-gate logit
+ *   logits       [T][E+1] float (column E: shared-gate logit), or NULL */
+MOE_API int moe_route(const moe_dims* dims, const moe_weights* w, const uint16_t* x, int32_t T, int32_t* ids,
+                      float* weights, float* shared_gate, float* logits, void* ws, size_t ws_bytes,
+                      hipStream_t stream);
+
+/* Routed half alone, with caller-supplied routing (the Chimera notebook,
+ * section 5: routed experts without the shared expert):
+ *   out[t] = sum_i weights[t][i] * FFN_{ids[t][i]}(x[t])     binary16 [T][H]
+ * Ids outside [0, E) contribute nothing.  Router rows and shared-expert
+ * arrays in `w` are not read (they may be NULL). */
+MOE_API int moe_experts_w4a16(const moe_dims* dims, const moe_weights* w, const uint16_t* x, int32_t T,
+                              const int32_t* ids, const float* weights, uint16_t* out, void* ws, size_t ws_bytes,
+                              hipStream_t stream);
+
+/* The complete block: out = routed + sigmoid(x . W_sg) * shared, binary16
+ * [T][H].  ids [T][k], weights [T][k] and shared_gate [T] receive the routing
+ * when non-NULL. */
+MOE_API int moe_forward(const moe_dims* dims, const moe_weights* w, const uint16_t* x, int32_t T, uint16_t* out,
+                        int32_t* ids, float* weights, float* shared_gate, void* ws, size_t ws_bytes,
+                        hipStream_t stream);
+
+/* Static description of a status code. */
+MOE_API const char* moe_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_W4A16_H */

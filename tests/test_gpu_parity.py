@@ -1,0 +1,161 @@
+"""Parity of the HIP library (through the C ABI) with the float64 oracle."""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+import w4a16_routed_experts_amd as m  # noqa: E402
+from oracle import ref  # noqa: E402
+from tests import _fixtures, _gpu  # noqa: E402
+from workloads import gen  # noqa: E402
+from workloads.gen import Case  # noqa: E402
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _device():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    m.lib()  # raises if the library is missing
+
+
+@pytest.mark.parametrize("cfg", [0, 1, 2, 3, 4])
+def test_forward_configs(cfg):
+    case = _gpu.config_case(cfg)
+    _gpu.log(f"forward config {cfg} ({case.name}) T={case.T}")
+    r = _gpu.config_oracle(cfg)
+    g = _gpu.run_forward(case)
+    _gpu.check_forward(case, r, g, f"cfg{cfg}")
+
+
+@pytest.mark.parametrize("cfg", [0, 1])
+def test_forward_configs_chunk_path(cfg):
+    case = _gpu.config_case(cfg)
+    _gpu.log(f"forward config {cfg} on the grouped-GEMM path")
+    g = _gpu.run_forward(case, flags=m.PATH_CHUNK)
+    _gpu.check_forward(case, _gpu.config_oracle(cfg), g, f"cfg{cfg}-chunk")
+
+
+@pytest.mark.parametrize("cfg", [0, 1, 2, 3, 4])
+def test_route_configs(cfg):
+    case = _gpu.config_case(cfg)
+    _gpu.log(f"route config {cfg}")
+    r = _gpu.config_oracle(cfg)
+    g = _gpu.run_route(case)
+    _gpu.check_routing(case, r, g, f"route cfg{cfg}")
+    scale = np.abs(r["logits"]).max()
+    assert np.abs(g["logits"] - r["logits"]).max() <= 1e-5 * max(1.0, scale)
+
+
+@pytest.mark.parametrize("T", [2, 3, 4])
+@pytest.mark.parametrize("flags", [m.PATH_DECODE, m.PATH_CHUNK])
+def test_few_tokens_both_paths(T, flags):
+    case = gen.make_case(gen.REAL, T, seed=2000 + T, real_experts=True)
+    _gpu.log(f"few tokens T={T} flags={flags}")
+    r = ref.forward(case.x, case.weights, case.dims)
+    g = _gpu.run_forward(case, flags=flags)
+    _gpu.check_forward(case, r, g, f"T{T}-f{flags}")
+
+
+@pytest.mark.parametrize("T", [33, 70])
+def test_ragged_chunks_real_width(T):
+    case = gen.make_case(gen.REAL, T, seed=3000 + T, bias="normal0.5", c=8.0, real_experts=True)
+    _gpu.log(f"ragged chunk T={T}")
+    r = ref.forward(case.x, case.weights, case.dims)
+    g = _gpu.run_forward(case)
+    _gpu.check_forward(case, r, g, f"ragged T{T}")
+
+
+@pytest.mark.parametrize("T,flags", [(1, m.PATH_DECODE), (3, m.PATH_DECODE), (45, m.PATH_AUTO), (1, m.PATH_CHUNK)])
+def test_toy_widths(T, flags):
+    case = gen.make_case(gen.TOY, T, seed=4000 + T)
+    _gpu.log(f"toy widths T={T} flags={flags}")
+    r = ref.forward(case.x, case.weights, case.dims)
+    g = _gpu.run_forward(case, flags=flags)
+    _gpu.check_forward(case, r, g, f"toy T{T}")
+
+
+@pytest.mark.parametrize("flags", [m.PATH_DECODE, m.PATH_CHUNK])
+def test_hand_derived_case(flags):
+    dims, W, x, expect = _fixtures.load_hand_case()
+    case = Case(name="hand", dims=dims, weights=W, x=x)
+    g = _gpu.run_forward(case, flags=flags)
+    for (t, i), v in expect["ids"].items():
+        assert g["ids"][t, i] == int(v)
+    for (t, i), v in expect["w"].items():
+        assert abs(g["w"][t, i] - v) < 1e-6
+    for (t,), v in expect["sigma"].items():
+        assert abs(g["sigma"][t] - v) < 1e-6
+    want = np.zeros_like(g["out"])
+    for (t, n), v in expect["out"].items():
+        want[t, n] = v
+    assert np.abs(g["out"] - want).max() < 2e-3 * np.abs(want).max()
+
+
+@pytest.mark.parametrize("T,flags", [(1, m.PATH_AUTO), (3, m.PATH_AUTO), (40, m.PATH_AUTO), (2, m.PATH_CHUNK)])
+def test_experts_given_routing(T, flags):
+    """Caller routing with repeated and out-of-range ids; those contribute nothing."""
+    case = gen.make_case(gen.REAL, T, seed=5000 + T, real_experts=True)
+    d = case.dims
+    rng = np.random.default_rng(T)
+    ids = rng.integers(0, d.E, size=(T, d.k))
+    ids[0, 1] = ids[0, 0]  # an expert listed twice
+    ids[-1, -1] = -1       # out of range: dropped
+    ids[-1, -2] = d.E      # out of range: dropped
+    w = rng.uniform(0.05, 1.0, size=(T, d.k))
+    _gpu.log(f"experts with caller routing T={T} flags={flags}")
+    g = _gpu.run_experts(case, ids, w, flags=flags)
+    valid = (ids >= 0) & (ids < d.E)
+    want = np.zeros((T, d.H))
+    for t in range(T):
+        for i in range(d.k):
+            if valid[t, i]:
+                want[t] += ref.experts(case.x[t:t + 1], ids[t:t + 1, i:i + 1], w[t:t + 1, i:i + 1],
+                                       case.weights, d)[0]
+    err = _gpu.row_rel_l2(g, want)
+    _gpu.log(f"  rel L2 max {err.max():.3e}")
+    assert err.max() <= _gpu.ROW_TOL
+
+
+def test_zero_tokens_leaves_output_untouched():
+    case = _gpu.config_case(1)
+    d = case.dims
+    dims = _gpu.dims_of(d)
+    W = _gpu.device_weights(case)
+    out = torch.full((1, d.H), 1234, dtype=torch.int16, device="cuda")
+    assert m.moe_forward(dims, W.struct, _gpu.x_tensor(case), 0, out, ws=None) == 0
+    torch.cuda.synchronize()
+    assert bool((out == 1234).all())
+
+
+@pytest.mark.parametrize("cfg", [1, 4])
+def test_deterministic(cfg):
+    case = _gpu.config_case(cfg)
+    g = _gpu.run_forward(case, reps=3)
+    for o in g["out_raw"][1:]:
+        assert np.array_equal(o, g["out_raw"][0])
+
+
+def test_workspace_reused_across_token_counts():
+    """The counters a call leaves in the workspace let the next call run."""
+    case4 = gen.make_case(gen.REAL, 4, seed=6004, real_experts=True)
+    case1 = gen.make_case(gen.REAL, 1, seed=6001, real_experts=True)
+    d = case4.dims
+    dims = _gpu.dims_of(d)
+    W = _gpu.device_weights(_gpu.config_case(1))
+    ws = m.workspace(dims, 4)
+    res = []
+    for case in (case4, case1, case4):
+        out = torch.zeros((case.T, d.H), dtype=torch.int16, device="cuda")
+        m.moe_forward(dims, W.struct, _gpu.x_tensor(case), case.T, out, ws=ws)
+        torch.cuda.synchronize()
+        res.append(_gpu.half_to_f64(out))
+    W_host = _gpu.config_case(1).weights
+    for case, o in zip((case4, case1, case4), res):
+        want = ref.forward(case.x, W_host, d)["out"]
+        assert _gpu.row_rel_l2(o, want).max() <= _gpu.ROW_TOL
+    # the workspace's counters are back to zero
+    assert int(ws[:1024].view(torch.int32)[: 6 * 32 : 32][:5].abs().sum()) == 0

@@ -1,0 +1,330 @@
+// C ABI: argument validation, workspace layout, path choice and launches.
+//
+// Everything a call could refuse is checked before the first HIP call, so a
+// refused call enqueues nothing and can be exercised without a GPU.
+#include <hip/hip_runtime.h>
+
+#include <mutex>
+#include <string.h>
+
+#include "chunk.hpp"
+#include "decode.hpp"
+#include "moe_w4a16.h"
+
+namespace {
+
+using namespace moe;
+
+constexpr int kMaxT = 65536;
+constexpr int kMaxWidth = 4096;
+constexpr size_t kDecodeMaxLds = 64 * 1024;
+constexpr int kTileRows = 32;
+
+size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+bool width_ok(int v) {
+  if (v < 64 || v > kMaxWidth) return false;
+  if (v % 2048 == 0) return true;
+  if (v % 64) return false;
+  const int m = v / 64;
+  return (m & (m - 1)) == 0;
+}
+
+int check_dims(const moe_dims* d, int32_t T) {
+  if (!d) return MOE_ERR_NULL;
+  if (d->group != kGroup) return MOE_ERR_SHAPE;
+  if (d->num_experts < 1 || d->num_experts > kMaxExperts) return MOE_ERR_SHAPE;
+  if (d->top_k < 1 || d->top_k > kMaxTopK || d->top_k > d->num_experts) return MOE_ERR_SHAPE;
+  if (!width_ok(d->hidden) || !width_ok(d->expert_inter) || !width_ok(d->shared_inter)) return MOE_ERR_SHAPE;
+  if (d->flags > MOE_PATH_CHUNK) return MOE_ERR_SHAPE;
+  if (T < 0 || T > kMaxT) return MOE_ERR_SHAPE;
+  return MOE_OK;
+}
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+size_t decode_lds_bytes(const moe_dims* d, int T) {
+  const size_t act = (size_t)std::max(T * d->hidden, T * d->top_k * d->expert_inter);
+  return (act + (size_t)T * d->shared_inter) * 2;
+}
+
+bool decode_admissible(const moe_dims* d, int T) {
+  return T >= 1 && T <= kDecMaxT && decode_lds_bytes(d, T) <= kDecodeMaxLds;
+}
+
+bool use_decode(const moe_dims* d, int T) {
+  if (d->flags == MOE_PATH_CHUNK) return false;
+  return decode_admissible(d, T);  // AUTO and DECODE both take it when it fits
+}
+
+int max_route_tiles(const moe_dims* d, int T) {
+  const int P = T * d->top_k;
+  return std::min(d->num_experts, P) + P / kTileRows;
+}
+
+// --------------------------------------------------------------- workspace
+
+struct Carve {
+  char* base;
+  size_t off = 0;
+  template <typename P>
+  P* take(size_t bytes) {
+    P* p = base ? reinterpret_cast<P*>(base + off) : nullptr;
+    off = align_up(off + bytes, 256);
+    return p;
+  }
+};
+
+struct DecodeWs {
+  uint32_t* sync;
+  float* logits;
+  _Float16* h_e;
+  _Float16* h_s;
+  float* s_sh;
+};
+
+DecodeWs carve_decode(const moe_dims* d, int T, Carve& c) {
+  DecodeWs w;
+  w.sync = c.take<uint32_t>(kSyncBytes);
+  w.logits = c.take<float>((size_t)T * (d->num_experts + 1) * 4);
+  w.h_e = c.take<_Float16>((size_t)T * d->top_k * d->expert_inter * 2);
+  w.h_s = c.take<_Float16>((size_t)T * d->shared_inter * 2);
+  w.s_sh = c.take<float>((size_t)T * d->hidden * 4);
+  return w;
+}
+
+void carve_chunk(const moe_dims* d, int T, Carve& c, ChunkArgs& a) {
+  const size_t P = (size_t)T * d->top_k;
+  c.take<uint32_t>(kSyncBytes);
+  a.logits = c.take<float>((size_t)T * (d->num_experts + 1) * 4);
+  a.ids = c.take<int32_t>(P * 4);
+  a.wts = c.take<float>(P * 4);
+  a.sigma = c.take<float>((size_t)T * 4);
+  a.offsets = c.take<int32_t>((size_t)(d->num_experts + 1) * 4);
+  a.sorted_pair = c.take<int32_t>(P * 4);
+  a.pos_of_pair = c.take<int32_t>(P * 4);
+  a.tiles = c.take<int4>((size_t)max_route_tiles(d, T) * 16);
+  a.n_tiles = c.take<int32_t>(4);
+  a.h = c.take<_Float16>(P * d->expert_inter * 2);
+  a.hs = c.take<_Float16>((size_t)T * d->shared_inter * 2);
+  a.y = c.take<float>(P * d->hidden * 4);
+  a.ys = c.take<float>((size_t)T * d->hidden * 4);
+}
+
+size_t workspace_bytes(const moe_dims* d, int T) {
+  if (T == 0) return 0;
+  Carve c{nullptr};
+  ChunkArgs a{};
+  carve_chunk(d, T, c, a);
+  size_t bytes = c.off;
+  if (decode_admissible(d, T)) {
+    Carve c2{nullptr};
+    carve_decode(d, T, c2);
+    bytes = std::max(bytes, c2.off);
+  }
+  return bytes;
+}
+
+// --------------------------------------------------------------- device
+
+struct DeviceInfo {
+  bool checked = false;
+  bool ok = false;
+  int cus = 0;
+  int occ[2][17] = {};  // blocks per CU by mode and LDS (4 KiB steps up to 64 KiB)
+};
+
+std::mutex g_dev_mu;
+DeviceInfo g_dev[64];
+
+int device_info(DeviceInfo** out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return MOE_ERR_DEVICE;
+  std::lock_guard<std::mutex> lk(g_dev_mu);
+  DeviceInfo& di = g_dev[dev];
+  if (!di.checked) {
+    di.checked = true;
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) == hipSuccess && strncmp(prop.gcnArchName, "gfx950", 6) == 0) {
+      di.ok = true;
+      di.cus = prop.multiProcessorCount;
+      for (int m = 0; m < 2; ++m)
+        for (int s = 0; s <= 16; ++s) di.occ[m][s] = decode_blocks_per_cu(m, (size_t)s * 4096);
+    }
+  }
+  if (!di.ok) return MOE_ERR_DEVICE;
+  *out = &di;
+  return MOE_OK;
+}
+
+// --------------------------------------------------------------- launches
+
+void fill_weights(const moe_weights* w, int8_t const** rq, uint16_t const** rs, uint8_t const** w13q,
+                  uint16_t const** w13s, uint8_t const** w2q, uint16_t const** w2s, int8_t const** s13q,
+                  uint16_t const** s13s, int8_t const** s2q, uint16_t const** s2s) {
+  *rq = w->router_q; *rs = w->router_s; *w13q = w->w13_q; *w13s = w->w13_s; *w2q = w->w2_q; *w2s = w->w2_s;
+  *s13q = w->sh13_q; *s13s = w->sh13_s; *s2q = w->sh2_q; *s2s = w->sh2_s;
+}
+
+int run_decode(const moe_dims* d, const moe_weights* w, const uint16_t* x, int T, uint16_t* out, int mode,
+               int32_t* ids_out, float* w_out, float* sig_out, const int32_t* ids_in, const float* w_in, void* ws,
+               hipStream_t s) {
+  DeviceInfo* di = nullptr;
+  int st = device_info(&di);
+  if (st != MOE_OK) return st;
+  DecodeArgs a{};
+  a.H = d->hidden; a.E = d->num_experts; a.k = d->top_k; a.I = d->expert_inter; a.Is = d->shared_inter; a.T = T;
+  fill_weights(w, &a.router_q, &a.router_s, &a.w13_q, &a.w13_s, &a.w2_q, &a.w2_s, &a.sh13_q, &a.sh13_s, &a.sh2_q,
+               &a.sh2_s);
+  a.x = x; a.out = out;
+  a.ids_out = ids_out; a.w_out = w_out; a.sigma_out = sig_out; a.logits_out = nullptr;
+  a.ids_in = ids_in; a.w_in = w_in;
+  Carve c{static_cast<char*>(ws)};
+  DecodeWs dw = carve_decode(d, T, c);
+  a.sync = dw.sync; a.logits = dw.logits; a.h_e = dw.h_e; a.h_s = dw.h_s; a.s_sh = dw.s_sh;
+  // item counts; these mirror the per-item row arithmetic of the kernel
+  auto rpb = [](int K, int bits) { const int cpr = K * bits / 128; return 64 / std::min(cpr, 64); };
+  const int r8h = rpb(a.H, 8), r4h = rpb(a.H, 4), r8s = rpb(a.Is, 8), r4i = rpb(a.I, 4);
+  a.n_router = mode == DEC_FORWARD ? (a.E + 1 + 4 * r8h - 1) / (4 * r8h) : 0;
+  a.n_shup = mode == DEC_FORWARD ? (a.Is + 8 * r8h - 1) / (8 * r8h) : 0;
+  a.up_jblocks = (a.I + 16 * r4h - 1) / (16 * r4h);
+  a.n_up = T * a.k * a.up_jblocks;
+  a.n_sd = mode == DEC_FORWARD ? (a.H + 16 * r8s - 1) / (16 * r8s) : 0;
+  a.n_down = T * (a.H / r4i);
+  const size_t lds = decode_lds_bytes(d, T);
+  const int per_cu = di->occ[mode][(lds + 4095) / 4096];
+  if (per_cu < 1) return MOE_ERR_LAUNCH;
+  const int want = std::max(std::max(a.n_router + a.n_shup, a.n_up + a.n_sd), a.n_down);
+  const int grid = std::max(1, std::min(want, per_cu * di->cus));
+  return launch_decode(a, mode, grid, lds, s);
+}
+
+ChunkArgs chunk_args(const moe_dims* d, const moe_weights* w, const uint16_t* x, int T, uint16_t* out, void* ws) {
+  ChunkArgs a{};
+  a.H = d->hidden; a.E = d->num_experts; a.k = d->top_k; a.I = d->expert_inter; a.Is = d->shared_inter; a.T = T;
+  fill_weights(w, &a.router_q, &a.router_s, &a.w13_q, &a.w13_s, &a.w2_q, &a.w2_s, &a.sh13_q, &a.sh13_s, &a.sh2_q,
+               &a.sh2_s);
+  a.x = x; a.out = out;
+  Carve c{static_cast<char*>(ws)};
+  carve_chunk(d, T, c, a);
+  a.max_route_tiles = max_route_tiles(d, T);
+  return a;
+}
+
+int check_common(const moe_dims* d, const void* x, int32_t T, void* ws, size_t ws_bytes) {
+  int st = check_dims(d, T);
+  if (st != MOE_OK) return st;
+  if (T == 0) return MOE_OK;
+  if (!x || !ws) return MOE_ERR_NULL;
+  if (!aligned(x, 16) || !aligned(ws, 256)) return MOE_ERR_ALIGN;
+  if (ws_bytes < workspace_bytes(d, T)) return MOE_ERR_WORKSPACE;
+  if (d->flags == MOE_PATH_DECODE && !decode_admissible(d, T)) return MOE_ERR_SHAPE;
+  return MOE_OK;
+}
+
+bool all16(std::initializer_list<const void*> ps) {
+  for (const void* p : ps)
+    if (!aligned(p, 16)) return false;
+  return true;
+}
+bool all4(std::initializer_list<const void*> ps) {
+  for (const void* p : ps)
+    if (p && !aligned(p, 4)) return false;
+  return true;
+}
+bool any_null(std::initializer_list<const void*> ps) {
+  for (const void* p : ps)
+    if (!p) return true;
+  return false;
+}
+
+}  // namespace
+
+extern "C" {
+
+MOE_API size_t moe_workspace_bytes(const moe_dims* dims, int32_t T) {
+  if (check_dims(dims, T) != MOE_OK) return 0;
+  return workspace_bytes(dims, T);
+}
+
+MOE_API const char* moe_status_string(int status) {
+  switch (status) {
+    case MOE_OK: return "ok";
+    case MOE_ERR_NULL: return "a required pointer is NULL";
+    case MOE_ERR_SHAPE: return "dims or token count outside the admitted shapes";
+    case MOE_ERR_ALIGN: return "a pointer is not aligned as required";
+    case MOE_ERR_WORKSPACE: return "workspace smaller than moe_workspace_bytes()";
+    case MOE_ERR_LAUNCH: return "the HIP runtime refused a kernel launch";
+    case MOE_ERR_DEVICE: return "the current device is not gfx950 or cannot be queried";
+    default: return "unknown status";
+  }
+}
+
+MOE_API int moe_route(const moe_dims* dims, const moe_weights* w, const uint16_t* x, int32_t T, int32_t* ids,
+                      float* weights, float* shared_gate, float* logits, void* ws, size_t ws_bytes,
+                      hipStream_t stream) {
+  int st = check_common(dims, x, T, ws, ws_bytes);
+  if (st != MOE_OK || T == 0) return st;
+  if (!w) return MOE_ERR_NULL;
+  if (any_null({w->router_q, w->router_s, ids, weights})) return MOE_ERR_NULL;
+  if (!all16({w->router_q, w->router_s}) || !all4({ids, weights, shared_gate, logits})) return MOE_ERR_ALIGN;
+  DeviceInfo* di = nullptr;
+  if ((st = device_info(&di)) != MOE_OK) return st;
+  ChunkArgs a = chunk_args(dims, w, x, T, nullptr, ws);
+  a.ids = ids;
+  a.wts = weights;
+  if (shared_gate) a.sigma = shared_gate;
+  if (logits) a.logits = logits;
+  return launch_route_chunk(a, stream);
+}
+
+MOE_API int moe_experts_w4a16(const moe_dims* dims, const moe_weights* w, const uint16_t* x, int32_t T,
+                              const int32_t* ids, const float* weights, uint16_t* out, void* ws, size_t ws_bytes,
+                              hipStream_t stream) {
+  int st = check_common(dims, x, T, ws, ws_bytes);
+  if (st != MOE_OK || T == 0) return st;
+  if (!w) return MOE_ERR_NULL;
+  if (any_null({w->w13_q, w->w13_s, w->w2_q, w->w2_s, ids, weights, out})) return MOE_ERR_NULL;
+  if (!all16({w->w13_q, w->w13_s, w->w2_q, w->w2_s, out}) || !all4({ids, weights})) return MOE_ERR_ALIGN;
+  if (use_decode(dims, T))
+    return run_decode(dims, w, x, T, out, DEC_EXPERTS, nullptr, nullptr, nullptr, ids, weights, ws, stream);
+  DeviceInfo* di = nullptr;
+  if ((st = device_info(&di)) != MOE_OK) return st;
+  ChunkArgs a = chunk_args(dims, w, x, T, out, ws);
+  a.ids = const_cast<int32_t*>(ids);
+  a.wts = const_cast<float*>(weights);
+  a.route_tiles = 1;
+  a.shared_tiles = 0;
+  a.ys = nullptr;
+  return launch_experts_chunk(a, stream);
+}
+
+MOE_API int moe_forward(const moe_dims* dims, const moe_weights* w, const uint16_t* x, int32_t T, uint16_t* out,
+                        int32_t* ids, float* weights, float* shared_gate, void* ws, size_t ws_bytes,
+                        hipStream_t stream) {
+  int st = check_common(dims, x, T, ws, ws_bytes);
+  if (st != MOE_OK || T == 0) return st;
+  if (!w) return MOE_ERR_NULL;
+  if (any_null({w->router_q, w->router_s, w->w13_q, w->w13_s, w->w2_q, w->w2_s, w->sh13_q, w->sh13_s, w->sh2_q,
+                w->sh2_s, out}))
+    return MOE_ERR_NULL;
+  if (!all16({w->router_q, w->router_s, w->w13_q, w->w13_s, w->w2_q, w->w2_s, w->sh13_q, w->sh13_s, w->sh2_q,
+              w->sh2_s, out}) ||
+      !all4({ids, weights, shared_gate}))
+    return MOE_ERR_ALIGN;
+  if (use_decode(dims, T))
+    return run_decode(dims, w, x, T, out, DEC_FORWARD, ids, weights, shared_gate, nullptr, nullptr, ws, stream);
+  DeviceInfo* di = nullptr;
+  if ((st = device_info(&di)) != MOE_OK) return st;
+  ChunkArgs a = chunk_args(dims, w, x, T, out, ws);
+  if (ids) a.ids = ids;
+  if (weights) a.wts = weights;
+  if (shared_gate) a.sigma = shared_gate;
+  a.route_tiles = 1;
+  a.shared_tiles = (T + kTileRows - 1) / kTileRows;
+  int r = launch_route_chunk(a, stream);
+  if (r != MOE_OK) return r;
+  return launch_experts_chunk(a, stream);
+}
+
+}  // extern "C"

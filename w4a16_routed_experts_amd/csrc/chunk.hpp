@@ -1,0 +1,37 @@
+// Arguments and launchers of the multi-token (grouped-GEMM) path.
+#pragma once
+#include "common.hpp"
+
+namespace moe {
+
+struct ChunkArgs {
+  int H, E, k, I, Is, T;
+  const int8_t* router_q; const uint16_t* router_s;
+  const uint8_t* w13_q; const uint16_t* w13_s;
+  const uint8_t* w2_q; const uint16_t* w2_s;
+  const int8_t* sh13_q; const uint16_t* sh13_s;
+  const int8_t* sh2_q; const uint16_t* sh2_s;
+  const uint16_t* x;   // [T][H]
+  uint16_t* out;       // [T][H]
+  float* logits;       // [T][E+1]
+  int32_t* ids;        // [T][k]
+  float* wts;          // [T][k]
+  float* sigma;        // [T]
+  int32_t* offsets;    // [E+1]
+  int32_t* sorted_pair;  // [T*k]  pair index at each expert-major position
+  int32_t* pos_of_pair;  // [T*k]  expert-major position of each pair (-1: dropped)
+  int4* tiles;         // [max_route_tiles] (expert, first row, rows, 0)
+  int32_t* n_tiles;    // routed tiles written by the bucketing kernel
+  _Float16* h;         // [T*k][I]  expert-major rows
+  _Float16* hs;        // [T][Is]
+  float* y;            // [T*k][H]  weighted expert outputs, expert-major rows
+  float* ys;           // [T][H]    sigma * shared output, or null (routed half only)
+  int route_tiles;     // 1: routed tiles present
+  int shared_tiles;    // number of 32-token shared-expert tiles (0: routed half only)
+  int max_route_tiles; // bound on routed tiles for the grid
+};
+
+int launch_route_chunk(const ChunkArgs& a, hipStream_t s);
+int launch_experts_chunk(const ChunkArgs& a, hipStream_t s);
+
+}  // namespace moe

@@ -1,0 +1,145 @@
+// Wave-level dequant-in-register GEMV pieces for few-token (decode) work.
+//
+// A weight row of K codes is split into 16-byte chunks (32 int4 or 16 int8
+// codes).  With CPR = K*bits/128 chunks per row, a wave covers one row per
+// load when CPR >= 64 (each lane then owns CPR/64 chunks of every row) and
+// 64/CPR rows per load otherwise (groups of CPR lanes per row).  Every load is
+// a coalesced 128-bit load of packed codes; activations come from LDS.
+#pragma once
+#include "common.hpp"
+
+namespace moe {
+
+struct RowGeom {
+  int lpr;  // lanes per row (power of two, <= 64)
+  int rpb;  // rows per wave-load (64 / lpr)
+  int cpl;  // chunks per lane per row
+  int cpr;  // chunks per row
+};
+
+__device__ __forceinline__ RowGeom row_geom(int K, int bits) {
+  RowGeom g;
+  g.cpr = K * bits / 128;
+  g.lpr = g.cpr < 64 ? g.cpr : 64;
+  g.rpb = 64 / g.lpr;
+  g.cpl = g.cpr / g.lpr;
+  return g;
+}
+
+// 32 activations (one int4 chunk) from LDS, as 16 permuted pairs
+__device__ __forceinline__ void act32(const _Float16* a, h2 xp[16]) {
+  const uint4* p = reinterpret_cast<const uint4*>(a);
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const uint4 v = p[q];
+    const uint32_t x[4] = {v.x, v.y, v.z, v.w};
+    uint32_t o[4];
+    perm8_words(x, o);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) xp[4 * q + i] = as_h2(o[i]);
+  }
+}
+
+// 16 activations (one int8 chunk) from LDS, as 8 permuted pairs
+__device__ __forceinline__ void act16(const _Float16* a, h2 xp[8]) {
+  const uint4* p = reinterpret_cast<const uint4*>(a);
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    const uint4 v = p[q];
+    const uint32_t x[4] = {v.x, v.y, v.z, v.w};
+    uint32_t o[4];
+    perm8_words(x, o);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) xp[4 * q + i] = as_h2(o[i]);
+  }
+}
+
+// sum over one chunk of (code * activation); codes are exact integers
+__device__ __forceinline__ float chunk_dot4(uint4 wq, const h2 xp[16]) {
+  const uint32_t ws[4] = {wq.x, wq.y, wq.z, wq.w};
+  float acc = 0.f;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    h2 w[4];
+    int4x8_to_h2x4(ws[q], w);
+#pragma unroll
+    for (int p = 0; p < 4; ++p) acc = dot2(w[p], xp[4 * q + p], acc);
+  }
+  return acc;
+}
+
+__device__ __forceinline__ float chunk_dot8(uint4 wq, const h2 xp[8]) {
+  float acc = 0.f;
+  h2 w[4];
+  int8x8_to_h2x4(wq.x, wq.y, w);
+#pragma unroll
+  for (int p = 0; p < 4; ++p) acc = dot2(w[p], xp[p], acc);
+  int8x8_to_h2x4(wq.z, wq.w, w);
+#pragma unroll
+  for (int p = 0; p < 4; ++p) acc = dot2(w[p], xp[4 + p], acc);
+  return acc;
+}
+
+// Group index of chunk c: int4 chunks hold 32 codes (two per group), int8
+// chunks hold 16 codes (four per group).
+template <int BITS>
+__device__ __forceinline__ int chunk_group(int c) { return BITS == 4 ? (c >> 1) : (c >> 2); }
+
+// This lane's partial dot products for `nb` row-batches (one wave-load of
+// g.rpb rows each; rows[b] is this lane's row in batch b, or -1 when masked)
+// against TT activation vectors act + t*act_stride, scaled per group.  All
+// weight loads are issued before any arithmetic.  A lane's chunk index does
+// not depend on the batch, so each activation chunk is converted once.
+template <int BITS, int MAXB, int MAXCPL, int TT>
+__device__ __forceinline__ void lane_rows_dot(const uint8_t* __restrict__ W, const uint16_t* __restrict__ S, int K,
+                                              const int rows[MAXB], int nb, const RowGeom& g,
+                                              const _Float16* act, int act_stride, int T, float acc[MAXB][TT]) {
+  const int lane = threadIdx.x & 63;
+  const size_t row_bytes = (size_t)K * BITS / 8;
+  const int ngroups = K / kGroup;
+  constexpr int EPC = BITS == 4 ? 32 : 16;  // codes per 16-byte chunk
+  uint4 wq[MAXB][MAXCPL];
+  float sc[MAXB][MAXCPL];
+#pragma unroll
+  for (int b = 0; b < MAXB; ++b) {
+#pragma unroll
+    for (int m = 0; m < MAXCPL; ++m) {
+      wq[b][m] = make_uint4(0, 0, 0, 0);
+      sc[b][m] = 0.f;
+      if (b < nb && m < g.cpl && rows[b] >= 0) {
+        const int c = (lane % g.lpr) + g.lpr * m;
+        wq[b][m] = *reinterpret_cast<const uint4*>(W + (size_t)rows[b] * row_bytes + 16 * (size_t)c);
+        sc[b][m] = half_bits_to_float(S[(size_t)rows[b] * ngroups + chunk_group<BITS>(c)]);
+      }
+    }
+  }
+#pragma unroll
+  for (int b = 0; b < MAXB; ++b)
+#pragma unroll
+    for (int t = 0; t < TT; ++t) acc[b][t] = 0.f;
+#pragma unroll
+  for (int m = 0; m < MAXCPL; ++m) {
+    if (m >= g.cpl) break;
+    const int c = (lane % g.lpr) + g.lpr * m;
+#pragma unroll
+    for (int t = 0; t < TT; ++t) {
+      if (t >= T) break;
+      const _Float16* a = act + (size_t)t * act_stride + EPC * c;
+      if (BITS == 4) {
+        h2 xp[16];
+        act32(a, xp);
+#pragma unroll
+        for (int b = 0; b < MAXB; ++b)
+          if (b < nb) acc[b][t] = fmaf(chunk_dot4(wq[b][m], xp), sc[b][m], acc[b][t]);
+      } else {
+        h2 xp[8];
+        act16(a, xp);
+#pragma unroll
+        for (int b = 0; b < MAXB; ++b)
+          if (b < nb) acc[b][t] = fmaf(chunk_dot8(wq[b][m], xp), sc[b][m], acc[b][t]);
+      }
+    }
+  }
+}
+
+}  // namespace moe
