@@ -1,0 +1,261 @@
+"""Throughput of the routed MoE layer (W4A16) on one MI355X.
+
+One step = one call of the whole layer (router, top-k, experts, shared
+expert, combine) on one batch of seeded synthetic input already resident in
+HBM.  The headline workload is single-token decode at real widths (T=1,
+H=2048, E=256, top-8, I=512, Is=512); the 512-token Zipf chunk is measured in
+the same run and reported beside it.
+
+Cold-cache discipline: the weights are replicated R times at distinct device
+addresses and step s uses copy s mod R, so a copy's touched bytes have been
+evicted from L2 and the 256 MB last-level cache before it is used again.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
+Prints one JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+MFMA_F16_PEAK_TFLOPS = 2500.0  # MI355X dense fp16 MFMA, TFLOP/s
+METRIC = "MoE-layer tokens/s at T=1 and T=512; achieved HBM GB/s and MFMA % of peak"
+PROFILE_TRAFFIC = os.path.join(ROOT, "profiles", "decode_kernel_t1_traffic.txt")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+# --------------------------------------------------------------- accounting
+
+def algorithmic_bytes(d, T, distinct_experts):
+    """Bytes a layer call must move at least once: router, shared expert, the
+    distinct routed experts' weights (codes + scales), x and out."""
+    H, E, I, Is, G = d.H, d.E, d.I, d.Is, d.G
+    router = (E + 1) * H + (E + 1) * (H // G) * 2
+    shared = 2 * Is * H + 2 * Is * (H // G) * 2 + H * Is + H * (Is // G) * 2
+    expert = 2 * I * H // 2 + 2 * I * (H // G) * 2 + H * I // 2 + H * (I // G) * 2
+    return router + shared + distinct_experts * expert + 2 * T * H * 2
+
+
+def algorithmic_flops(d, T):
+    return T * (2 * (d.E + 1) * d.H + d.k * 6 * d.I * d.H + 6 * d.Is * d.H)
+
+
+def source_digest():
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "w4a16_routed_experts_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(name.encode() + f.read())
+    return h.hexdigest()[:16]
+
+
+def read_traffic(expected_digest):
+    """HBM bytes per launch from the committed counter summary, if it still
+    describes the current kernels (same source digest)."""
+    if not os.path.exists(PROFILE_TRAFFIC):
+        return None
+    vals = {}
+    with open(PROFILE_TRAFFIC) as f:
+        for line in f:
+            if ":" in line and not line.startswith("#"):
+                k, v = line.split(":", 1)
+                vals[k.strip()] = v.strip()
+    if vals.get("source_digest") != expected_digest:
+        return None
+    try:
+        return float(vals["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+# --------------------------------------------------------------- GPU leg
+
+def build_if_missing():
+    import w4a16_routed_experts_amd as m
+    if not os.path.exists(m.library_path()):
+        from w4a16_routed_experts_amd import build
+        build.build()
+    m.lib()
+
+
+def make_copies(case, R, torch, m):
+    """R device copies of the layer's weights at distinct addresses."""
+    import numpy as np
+    base = {}
+    for f, a in case.weights.items():
+        view = {"|i1": np.int8, "|u1": np.uint8, "<u2": np.int16}[a.dtype.str]
+        base[f] = torch.from_numpy(a.view(view)).cuda()
+    copies = [m.DeviceWeights(tensors=base)]
+    for _ in range(R - 1):
+        copies.append(m.DeviceWeights(tensors={f: t.clone() for f, t in base.items()}))
+    torch.cuda.synchronize()
+    return copies
+
+
+def time_config(cfg, steps, warmup, R, torch, m, gen, per_launch_events):
+    import ctypes
+    import numpy as np
+    case = gen.make_config(cfg)
+    d, T = case.dims, case.T
+    dims = m.make_dims(d.H, d.E, d.k, d.I, d.Is, d.G)
+    copies = make_copies(case, R, torch, m)
+    x = torch.from_numpy(case.x.view(np.int16)).cuda()
+    out = torch.empty((T, d.H), dtype=torch.int16, device="cuda")
+    ids = torch.empty((T, d.k), dtype=torch.int32, device="cuda")
+    ws = m.workspace(dims, T)
+    stream = torch.cuda.current_stream()
+    L = m.lib()
+    fwd = L.moe_forward
+    # pre-marshalled arguments: the timed loop makes one ctypes call per step
+    args = [(ctypes.byref(dims), ctypes.byref(c.struct), x.data_ptr(), T, out.data_ptr(), ids.data_ptr(), None,
+             None, ws.data_ptr(), ws.numel(), stream.cuda_stream) for c in copies]
+    for s in range(warmup):
+        st = fwd(*args[s % R])
+        if st != 0:
+            raise RuntimeError(f"moe_forward: {m.moe_status_string(st)}")
+    torch.cuda.synchronize()
+    distinct = int(np.unique(ids.cpu().numpy()).size)
+
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    t0 = time.perf_counter()
+    for s in range(steps):
+        fwd(*args[s % R])
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = e0.elapsed_time(e1)
+    res = dict(cfg=cfg, name=case.name, T=T, dims=d, steps=steps, ms_total=ms, wall_s=wall,
+               us_per_step=ms * 1e3 / steps, distinct_experts=distinct)
+
+    if per_launch_events:
+        # the same steps with an event pair around every launch (one kernel per step)
+        n = min(steps, 2000)
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+        torch.cuda.synchronize()
+        for s in range(n):
+            ev[s][0].record(stream)
+            fwd(*args[s % R])
+            ev[s][1].record(stream)
+        torch.cuda.synchronize()
+        durs = np.array([a.elapsed_time(b) for a, b in ev]) * 1e3
+        res["us_per_launch"] = float(durs.mean())
+        res["us_per_launch_median"] = float(np.median(durs))
+    del copies
+    torch.cuda.empty_cache()
+    return res
+
+
+# --------------------------------------------------------------- CPU leg
+
+def cpu_baseline(gen, budget_s=12.0):
+    """The float64 oracle on the host cores, on the single-token workload."""
+    from oracle import ref
+    try:
+        from threadpoolctl import threadpool_info
+        blas_threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:
+        blas_threads = int(os.environ.get("OMP_NUM_THREADS", "1"))
+    case = gen.make_config(1)
+    n = 0
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < budget_s or n == 0:
+        ref.forward(case.x, case.weights, case.dims)
+        n += 1
+    dt = time.perf_counter() - t0
+    return {"value": round(n * case.T / dt, 3), "unit": "tokens/s", "cores": int(blas_threads), "kind": "oracle",
+            "sample": f"{n} calls of the float64 oracle forward on the T=1 decode input "
+                      f"({dt:.1f} s; host has {len(os.sched_getaffinity(0))} cores available)"}
+
+
+# --------------------------------------------------------------- main
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=2000)
+    ap.add_argument("--warmup", type=int, default=200)
+    ap.add_argument("--copies", type=int, default=32, help="weight copies rotated for cold-cache timing")
+    ap.add_argument("--chunk-steps", type=int, default=300, help="steps of the 512-token workload")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this layer is measured on one GPU; multi-GPU runs are not part of this build",
+                          "n_gpus": args.gpus}))
+        sys.exit(2)
+
+    import torch
+    import w4a16_routed_experts_amd as m
+    from workloads import gen
+    build_if_missing()
+
+    digest = source_digest()
+    log("decode T=1 ...")
+    r1 = time_config(1, args.steps, args.warmup, args.copies, torch, m, gen, per_launch_events=True)
+    log(f"  {r1['us_per_step']:.3f} us/step, {r1['us_per_launch']:.3f} us/launch")
+    log("chunk T=512 ...")
+    r4 = time_config(4, args.chunk_steps, max(10, args.warmup // 10), max(4, args.copies // 8), torch, m, gen,
+                     per_launch_events=False)
+    log(f"  {r4['us_per_step']:.3f} us/step")
+
+    d1 = r1["dims"]
+    b1 = algorithmic_bytes(d1, 1, r1["distinct_experts"])
+    f1 = algorithmic_flops(d1, 1)
+    achieved_gbs = b1 / (r1["us_per_launch"] * 1e-6) / 1e9
+    traffic = read_traffic(digest)
+    value = r1["T"] * r1["steps"] / (r1["ms_total"] * 1e-3)
+
+    d4 = r4["dims"]
+    b4 = algorithmic_bytes(d4, r4["T"], r4["distinct_experts"])
+    f4 = algorithmic_flops(d4, r4["T"])
+    t4 = r4["us_per_step"] * 1e-6
+    line = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(r1["ms_total"] / r1["steps"], 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16",
+        "data": "synthetic",
+        "config": {"workload": "single-token decode: T=1, hidden 2048, 256 experts, top-8, expert intermediate 512, "
+                               "shared intermediate 512, int4 g64 experts, int8 g64 router and shared expert",
+                   "weight_copies_rotated": args.copies, "distinct_experts": r1["distinct_experts"]},
+        "roofline": {"bound": "hbm", "achieved": round(achieved_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved_gbs / HBM_PEAK_GBS, 4), "traffic": traffic,
+                     "kernel": "decode_kernel<0> (the whole layer in one launch)",
+                     "algorithmic_bytes_per_launch": b1, "us_per_launch": round(r1["us_per_launch"], 3),
+                     "mfma_pct": round(100 * f1 / (r1["us_per_launch"] * 1e-6) / (MFMA_F16_PEAK_TFLOPS * 1e12), 4)},
+        "chunk_t512": {"workload": "512-token chunk, Zipf(1.1) expert popularity, same widths",
+                       "tokens_per_s": round(r4["T"] / t4, 1), "us_per_step": round(r4["us_per_step"], 3),
+                       "hbm_gbs": round(b4 / t4 / 1e9, 1), "hbm_frac": round(b4 / t4 / 1e9 / HBM_PEAK_GBS, 4),
+                       "mfma_pct": round(100 * f4 / t4 / (MFMA_F16_PEAK_TFLOPS * 1e12), 3),
+                       "algorithmic_bytes": b4, "flops": f4, "distinct_experts": r4["distinct_experts"],
+                       "roofline_frac": round(max(b4 / (HBM_PEAK_GBS * 1e9), f4 / (MFMA_F16_PEAK_TFLOPS * 1e12)) / t4,
+                                              4)},
+        "source_digest": digest,
+    }
+    if not args.no_cpu:
+        log("cpu baseline ...")
+        line["cpu_baseline"] = cpu_baseline(gen)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

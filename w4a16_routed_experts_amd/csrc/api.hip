@@ -78,8 +78,8 @@ struct Carve {
 struct DecodeWs {
   uint32_t* sync;
   float* logits;
-  _Float16* h_e;
-  _Float16* h_s;
+  float* h_e;
+  float* h_s;
   float* s_sh;
 };
 
@@ -87,8 +87,8 @@ DecodeWs carve_decode(const moe_dims* d, int T, Carve& c) {
   DecodeWs w;
   w.sync = c.take<uint32_t>(kSyncBytes);
   w.logits = c.take<float>((size_t)T * (d->num_experts + 1) * 4);
-  w.h_e = c.take<_Float16>((size_t)T * d->top_k * d->expert_inter * 2);
-  w.h_s = c.take<_Float16>((size_t)T * d->shared_inter * 2);
+  w.h_e = c.take<float>((size_t)T * d->top_k * d->expert_inter * 4);
+  w.h_s = c.take<float>((size_t)T * d->shared_inter * 4);
   w.s_sh = c.take<float>((size_t)T * d->hidden * 4);
   return w;
 }

@@ -17,6 +17,14 @@
 // Every workgroup recomputes the top-k from the logits itself (one wave per
 // token), so no extra hand-off is needed between routing and the experts.
 // The weights of a workgroup's first C item are loaded before it waits.
+//
+// Hand-off without cache maintenance: on gfx950 each XCD has its own L2, and
+// agent-scope acquire/release fences invalidate / write back a whole L2.  The
+// values passed between workgroups (logits, h, s) are therefore written and
+// read with device-coherent (agent-scope) relaxed atomic accesses, which do
+// not leave stale or dirty copies in an XCD's L2.  A producer waits until its
+// stores are acknowledged (vmcnt 0) before it bumps the counter; a consumer
+// polls the counter and then reads the values with the same coherent loads.
 #include "decode.hpp"
 #include "gemv.hpp"
 
@@ -24,11 +32,18 @@ namespace moe {
 
 // ------------------------------------------------------------------ helpers
 
+__device__ __forceinline__ void st_co(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float ld_co(const float* p) {
+  return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 __device__ __forceinline__ void wait_count(uint32_t* sync, int which, uint32_t target) {
   if (threadIdx.x == 0) {
     uint32_t* ctr = sync + which * kSyncStride;
     uint32_t spins = 0;
-    while (acquire_load(ctr) < target) {
+    while (__hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < target) {
       __builtin_amdgcn_s_sleep(1);
       if (++spins > (1u << 24)) {  // never expected; guarantees the launch drains
         __hip_atomic_store(sync + SYNC_ERR * kSyncStride, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -37,13 +52,60 @@ __device__ __forceinline__ void wait_count(uint32_t* sync, int which, uint32_t t
     }
   }
   __syncthreads();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
 }
 
+// every wave's coherent stores are acknowledged before the counter moves
 __device__ __forceinline__ void signal_item(uint32_t* sync, int which) {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
-  if (threadIdx.x == 0) signal_add(sync + which * kSyncStride, 1u);
+  if (threadIdx.x == 0)
+    __hip_atomic_fetch_add(sync + which * kSyncStride, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// n coherent floats (n even, src 8-byte aligned) -> LDS halves.  Loads are
+// issued in batches of 8 per thread before any is used, so a copy costs one
+// memory round trip per batch rather than one per element.
+__device__ __forceinline__ void copy_co_to_halves(_Float16* dst, const float* src, int n) {
+  const uint64_t* s2 = reinterpret_cast<const uint64_t*>(src);
+  const int n2 = n / 2;
+  constexpr int B = 8;
+  for (int base = 0; base < n2; base += B * 256) {
+    uint64_t v[B];
+#pragma unroll
+    for (int u = 0; u < B; ++u) {
+      const int i = base + u * 256 + (int)threadIdx.x;
+      v[u] = i < n2 ? __hip_atomic_load(const_cast<uint64_t*>(s2 + i), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                    : 0ull;
+    }
+#pragma unroll
+    for (int u = 0; u < B; ++u) {
+      const int i = base + u * 256 + (int)threadIdx.x;
+      if (i < n2) {
+        h2 hv;
+        hv[0] = (_Float16)__builtin_bit_cast(float, (uint32_t)v[u]);
+        hv[1] = (_Float16)__builtin_bit_cast(float, (uint32_t)(v[u] >> 32));
+        reinterpret_cast<h2*>(dst)[i] = hv;
+      }
+    }
+  }
+}
+
+// n coherent floats -> LDS floats, batched the same way
+__device__ __forceinline__ void copy_co_floats(float* dst, const float* src, int n) {
+  constexpr int B = 8;
+  for (int base = 0; base < n; base += B * 256) {
+    float v[B];
+#pragma unroll
+    for (int u = 0; u < B; ++u) {
+      const int i = base + u * 256 + (int)threadIdx.x;
+      v[u] = i < n ? ld_co(src + i) : 0.f;
+    }
+#pragma unroll
+    for (int u = 0; u < B; ++u) {
+      const int i = base + u * 256 + (int)threadIdx.x;
+      if (i < n) dst[i] = v[u];
+    }
+  }
 }
 
 // copy n halves (n multiple of 8) global -> LDS with 16-byte accesses
@@ -157,7 +219,7 @@ __device__ void router_item(const DecodeArgs& a, int item, const _Float16* xs) {
 #pragma unroll
   for (int t = 0; t < kDecMaxT; ++t) {
     const float v = group_sum(acc[0][t], g.lpr);
-    if (t < a.T && row < nrows && (lane % g.lpr) == 0) a.logits[(size_t)t * nrows + row] = v;
+    if (t < a.T && row < nrows && (lane % g.lpr) == 0) st_co(a.logits + (size_t)t * nrows + row, v);
   }
 }
 
@@ -193,7 +255,7 @@ __device__ void shup_item(const DecodeArgs& a, int item, const _Float16* xs) {
       const float gate = group_sum(acc[h][t], g.lpr);
       const float up = group_sum(acc[2 + h][t], g.lpr);
       if (t < a.T && jj[h] < a.Is && (lane % g.lpr) == 0)
-        a.h_s[(size_t)t * a.Is + jj[h]] = (_Float16)(silu_f(gate) * up);
+        st_co(a.h_s + (size_t)t * a.Is + jj[h], silu_f(gate) * up);
     }
 }
 
@@ -233,7 +295,7 @@ __device__ void up_item(const DecodeArgs& a, int item, const _Float16* xs, const
     const float gate = group_sum(acc[h][0], g.lpr);
     const float up = group_sum(acc[4 + h][0], g.lpr);
     if (jj[h] < a.I && (lane % g.lpr) == 0)
-      a.h_e[((size_t)t * a.k + i) * a.I + jj[h]] = (_Float16)(e >= 0 ? silu_f(gate) * up : 0.f);
+      st_co(a.h_e + ((size_t)t * a.k + i) * a.I + jj[h], e >= 0 ? silu_f(gate) * up : 0.f);
   }
 }
 
@@ -265,7 +327,7 @@ __device__ void sd_item(const DecodeArgs& a, int item, const _Float16* hs) {
 #pragma unroll
     for (int t = 0; t < kDecMaxT; ++t) {
       const float v = group_sum(acc[h][t], g.lpr);
-      if (t < a.T && nn[h] < a.H && (lane % g.lpr) == 0) a.s_sh[(size_t)t * a.H + nn[h]] = v;
+      if (t < a.T && nn[h] < a.H && (lane % g.lpr) == 0) st_co(a.s_sh + (size_t)t * a.H + nn[h], v);
     }
 }
 
@@ -281,6 +343,7 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
   __shared__ float s_w[kDecMaxT][kMaxTopK];
   __shared__ float s_sig[kDecMaxT];
   __shared__ float s_red[4][64];
+  __shared__ float s_logits_raw[kDecMaxT * (kMaxExperts + 1)];
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int nb = gridDim.x, b = blockIdx.x;
@@ -304,9 +367,11 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
   if (MODE == DEC_FORWARD) {
     wait_count(a.sync, SYNC_ROUTER, a.n_router);
     const int nrows = a.E + 1;
+    copy_co_floats(s_logits_raw, a.logits, T * nrows);  // [T][E+1]
+    __syncthreads();
     for (int t = wave; t < T; t += 4) {
-      wave_topk(a.logits + (size_t)t * nrows, a.E, a.k, s_ids[t], s_w[t]);
-      if (lane == 0) s_sig[t] = sigmoid_f(a.logits[(size_t)t * nrows + a.E]);
+      wave_topk(s_logits_raw + t * nrows, a.E, a.k, s_ids[t], s_w[t]);
+      if (lane == 0) s_sig[t] = sigmoid_f(s_logits_raw[t * nrows + a.E]);
     }
     __syncthreads();
     if (b == 0) {
@@ -318,7 +383,7 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
       for (int t = tid; t < T; t += blockDim.x)
         if (a.sigma_out) a.sigma_out[t] = s_sig[t];
       if (a.logits_out)
-        for (int p = tid; p < T * nrows; p += blockDim.x) a.logits_out[p] = a.logits[p];
+        for (int p = tid; p < T * nrows; p += blockDim.x) a.logits_out[p] = s_logits_raw[p];
     }
   } else {
     for (int p = tid; p < T * a.k; p += blockDim.x) {
@@ -341,7 +406,7 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
       } else {
         if (!hs_ready) {
           wait_count(a.sync, SYNC_SHUP, a.n_shup);
-          copy_halves(hs_lds, a.h_s, T * a.Is);
+          copy_co_to_halves(hs_lds, a.h_s, T * a.Is);
           __syncthreads();
           hs_ready = true;
         }
@@ -378,7 +443,7 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
       if (!h_ready) {
         wait_count(a.sync, SYNC_UP, a.n_up);
         if (MODE == DEC_FORWARD) wait_count(a.sync, SYNC_SD, a.n_sd);
-        copy_halves(act, a.h_e, T * a.k * a.I);
+        copy_co_to_halves(act, a.h_e, T * a.k * a.I);
         __syncthreads();
         h_ready = true;
       }
@@ -398,7 +463,7 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
       if (tid < g.rpb) {
         float v = s_red[0][tid] + s_red[1][tid] + s_red[2][tid] + s_red[3][tid];
         const int nn = n0 + tid;
-        if (MODE == DEC_FORWARD) v += s_sig[t] * a.s_sh[(size_t)t * a.H + nn];
+        if (MODE == DEC_FORWARD) v += s_sig[t] * ld_co(a.s_sh + (size_t)t * a.H + nn);
         const _Float16 hv = (_Float16)v;
         a.out[(size_t)t * a.H + nn] = __builtin_bit_cast(uint16_t, hv);
       }
@@ -409,7 +474,7 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
   // ---------------- drain: the last workgroup out clears the counters
   __syncthreads();
   if (tid == 0) {
-    const uint32_t old = __hip_atomic_fetch_add(a.sync + SYNC_EXIT * kSyncStride, 1u, __ATOMIC_ACQ_REL,
+    const uint32_t old = __hip_atomic_fetch_add(a.sync + SYNC_EXIT * kSyncStride, 1u, __ATOMIC_RELAXED,
                                                 __HIP_MEMORY_SCOPE_AGENT);
     if (old == (uint32_t)nb - 1) {
       for (int w = 0; w < SYNC_EXIT + 1; ++w)

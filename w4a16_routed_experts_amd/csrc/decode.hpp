@@ -23,8 +23,8 @@ struct DecodeArgs {
   const int32_t* ids_in; const float* w_in;                             // routing given by the caller
   uint32_t* sync;
   float* logits;   // [T][E+1]
-  _Float16* h_e;   // [T][k][I]
-  _Float16* h_s;   // [T][Is]
+  float* h_e;      // [T][k][I]
+  float* h_s;      // [T][Is]
   float* s_sh;     // [T][H]
   int n_router, n_shup, n_up, n_sd, n_down;
   int up_jblocks;  // j-blocks per (token, slot)
