@@ -78,18 +78,24 @@ struct Carve {
 struct DecodeWs {
   uint32_t* sync;
   float* logits;
-  float* h_e;
   float* h_s;
+  float* h_e;
   float* s_sh;
 };
 
+DecodePlan plan_of(const moe_dims* d, int T, bool routed_only) {
+  return decode_plan(d->hidden, d->num_experts, d->top_k, d->expert_inter, d->shared_inter, T, routed_only);
+}
+
 DecodeWs carve_decode(const moe_dims* d, int T, Carve& c) {
+  // sized for the complete block; the routed half alone uses a subset
+  const DecodePlan p = plan_of(d, T, false);
   DecodeWs w;
   w.sync = c.take<uint32_t>(kSyncBytes);
-  w.logits = c.take<float>((size_t)T * (d->num_experts + 1) * 4);
-  w.h_e = c.take<float>((size_t)T * d->top_k * d->expert_inter * 4);
-  w.h_s = c.take<float>((size_t)T * d->shared_inter * 4);
-  w.s_sh = c.take<float>((size_t)T * d->hidden * 4);
+  w.logits = c.take<float>(decode_region_floats(p, T, 0) * 4);
+  w.h_s = c.take<float>(decode_region_floats(p, T, 1) * 4);
+  w.h_e = c.take<float>(decode_region_floats(p, T, 2) * 4);
+  w.s_sh = c.take<float>(decode_region_floats(p, T, 3) * 4);
   return w;
 }
 
@@ -131,7 +137,7 @@ struct DeviceInfo {
   bool checked = false;
   bool ok = false;
   int cus = 0;
-  int occ[2][17] = {};  // blocks per CU by mode and LDS (4 KiB steps up to 64 KiB)
+  int occ[2][2][17] = {};  // blocks per CU by mode, width specialisation and LDS (4 KiB steps)
 };
 
 std::mutex g_dev_mu;
@@ -149,7 +155,8 @@ int device_info(DeviceInfo** out) {
       di.ok = true;
       di.cus = prop.multiProcessorCount;
       for (int m = 0; m < 2; ++m)
-        for (int s = 0; s <= 16; ++s) di.occ[m][s] = decode_blocks_per_cu(m, (size_t)s * 4096);
+        for (int r = 0; r < 2; ++r)
+          for (int s = 0; s <= 16; ++s) di.occ[m][r][s] = decode_blocks_per_cu(m, r == 1, (size_t)s * 4096);
     }
   }
   if (!di.ok) return MOE_ERR_DEVICE;
@@ -177,24 +184,17 @@ int run_decode(const moe_dims* d, const moe_weights* w, const uint16_t* x, int T
   fill_weights(w, &a.router_q, &a.router_s, &a.w13_q, &a.w13_s, &a.w2_q, &a.w2_s, &a.sh13_q, &a.sh13_s, &a.sh2_q,
                &a.sh2_s);
   a.x = x; a.out = out;
-  a.ids_out = ids_out; a.w_out = w_out; a.sigma_out = sig_out; a.logits_out = nullptr;
+  a.ids_out = ids_out; a.w_out = w_out; a.sigma_out = sig_out;
   a.ids_in = ids_in; a.w_in = w_in;
   Carve c{static_cast<char*>(ws)};
   DecodeWs dw = carve_decode(d, T, c);
-  a.sync = dw.sync; a.logits = dw.logits; a.h_e = dw.h_e; a.h_s = dw.h_s; a.s_sh = dw.s_sh;
-  // item counts; these mirror the per-item row arithmetic of the kernel
-  auto rpb = [](int K, int bits) { const int cpr = K * bits / 128; return 64 / std::min(cpr, 64); };
-  const int r8h = rpb(a.H, 8), r4h = rpb(a.H, 4), r8s = rpb(a.Is, 8), r4i = rpb(a.I, 4);
-  a.n_router = mode == DEC_FORWARD ? (a.E + 1 + 4 * r8h - 1) / (4 * r8h) : 0;
-  a.n_shup = mode == DEC_FORWARD ? (a.Is + 8 * r8h - 1) / (8 * r8h) : 0;
-  a.up_jblocks = (a.I + 16 * r4h - 1) / (16 * r4h);
-  a.n_up = T * a.k * a.up_jblocks;
-  a.n_sd = mode == DEC_FORWARD ? (a.H + 16 * r8s - 1) / (16 * r8s) : 0;
-  a.n_down = T * (a.H / r4i);
+  a.sync = dw.sync; a.logits = dw.logits; a.h_s = dw.h_s; a.h_e = dw.h_e; a.s_sh = dw.s_sh;
+  a.p = plan_of(d, T, mode == DEC_EXPERTS);
   const size_t lds = decode_lds_bytes(d, T);
-  const int per_cu = di->occ[mode][(lds + 4095) / 4096];
+  const bool real = decode_real_widths(a.H, a.I, a.Is);
+  const int per_cu = di->occ[mode][real ? 1 : 0][(lds + 4095) / 4096];
   if (per_cu < 1) return MOE_ERR_LAUNCH;
-  const int want = std::max(std::max(a.n_router + a.n_shup, a.n_up + a.n_sd), a.n_down);
+  const int want = std::max(std::max(a.p.n_router + a.p.n_shup, a.p.n_up + a.p.n_sd), a.p.n_down);
   const int grid = std::max(1, std::min(want, per_cu * di->cus));
   return launch_decode(a, mode, grid, lds, s);
 }

@@ -7,24 +7,27 @@
 // TensorFold PR, "Design").
 //
 // Work is split into items executed by a grid of co-resident workgroups.  Items
-// hand results to each other through agent-scope counters instead of kernel
-// boundaries (one launch costs about as much as the whole layer's HBM time at
-// one token):
+// hand results to each other through counters instead of kernel boundaries
+// (one launch costs about as much as the whole layer's HBM time at one token):
 //   A  router rows (logits) | shared-expert gate/up rows (h_s)
 //   B  expert gate/up rows of the k selected experts (h_e)   <- router
 //      shared-expert down rows (s)                           <- shared gate/up
 //   C  expert down rows + weighted combine + sigma * s       <- B
-// Every workgroup recomputes the top-k from the logits itself (one wave per
-// token), so no extra hand-off is needed between routing and the experts.
-// The weights of a workgroup's first C item are loaded before it waits.
+// Every workgroup recomputes the top-k from the logits (all 256 threads, see
+// block_topk), so no hand-off is needed between routing and the experts.  The
+// weights of a workgroup's first C item are loaded before it waits.
 //
-// Hand-off without cache maintenance: on gfx950 each XCD has its own L2, and
-// agent-scope acquire/release fences invalidate / write back a whole L2.  The
-// values passed between workgroups (logits, h, s) are therefore written and
-// read with device-coherent (agent-scope) relaxed atomic accesses, which do
-// not leave stale or dirty copies in an XCD's L2.  A producer waits until its
-// stores are acknowledged (vmcnt 0) before it bumps the counter; a consumer
-// polls the counter and then reads the values with the same coherent loads.
+// Hand-off without cache maintenance.  On gfx950 each XCD has its own L2, and
+// agent-scope fences write back or invalidate a whole L2.  Instead:
+//   * a producer writes its values with device-coherent stores into a region
+//     of the workspace that only it writes (128-byte aligned, so no cache line
+//     is shared between producers), waits until they are acknowledged
+//     (vmcnt 0) and then bumps a counter with a device-scope atomic;
+//   * a consumer polls the counter with device-coherent loads and then reads
+//     the values with ordinary loads: no L2 can hold a stale copy, because the
+//     L2s start each launch invalidated and nothing reads these lines before
+//     their counter is complete.  The ordinary loads let each XCD's L2 serve
+//     the many workgroups that read the same values.
 #include "decode.hpp"
 #include "gemv.hpp"
 
@@ -35,15 +38,24 @@ namespace moe {
 __device__ __forceinline__ void st_co(float* p, float v) {
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-__device__ __forceinline__ float ld_co(const float* p) {
-  return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+
+// Completion signalling.  Producers count finished items with a device-scope
+// atomic on the counter; the producer whose increment completes it raises a
+// done flag in each XCD's flag page.  Consumers poll only their own XCD's flag
+// (device-coherent loads), so no memory line is polled by more than one XCD's
+// workgroups and the counters themselves are never polled.
+__device__ __forceinline__ int xcc_id() {
+  return (int)(__builtin_amdgcn_s_getreg(20 | (15 << 11)) & (kXcds - 1));  // HW_REG_XCC_ID[3:0]
+}
+__device__ __forceinline__ uint32_t* flag_of(uint32_t* sync, int xcd, int which) {
+  return sync + (1 + xcd) * kFlagPage + which * kSyncStride;
 }
 
-__device__ __forceinline__ void wait_count(uint32_t* sync, int which, uint32_t target) {
+__device__ __forceinline__ void wait_done(uint32_t* sync, int which) {
   if (threadIdx.x == 0) {
-    uint32_t* ctr = sync + which * kSyncStride;
+    uint32_t* f = flag_of(sync, xcc_id(), which);
     uint32_t spins = 0;
-    while (__hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < target) {
+    while (__hip_atomic_load(f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 0u) {
       __builtin_amdgcn_s_sleep(1);
       if (++spins > (1u << 24)) {  // never expected; guarantees the launch drains
         __hip_atomic_store(sync + SYNC_ERR * kSyncStride, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -54,57 +66,17 @@ __device__ __forceinline__ void wait_count(uint32_t* sync, int which, uint32_t t
   __syncthreads();
 }
 
-// every wave's coherent stores are acknowledged before the counter moves
-__device__ __forceinline__ void signal_item(uint32_t* sync, int which) {
+// Every wave's coherent stores are acknowledged before the counter moves; the
+// last of `target` items raises the done flags.
+__device__ __forceinline__ void signal_item(uint32_t* sync, int which, uint32_t target) {
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
-  if (threadIdx.x == 0)
-    __hip_atomic_fetch_add(sync + which * kSyncStride, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
-// n coherent floats (n even, src 8-byte aligned) -> LDS halves.  Loads are
-// issued in batches of 8 per thread before any is used, so a copy costs one
-// memory round trip per batch rather than one per element.
-__device__ __forceinline__ void copy_co_to_halves(_Float16* dst, const float* src, int n) {
-  const uint64_t* s2 = reinterpret_cast<const uint64_t*>(src);
-  const int n2 = n / 2;
-  constexpr int B = 8;
-  for (int base = 0; base < n2; base += B * 256) {
-    uint64_t v[B];
-#pragma unroll
-    for (int u = 0; u < B; ++u) {
-      const int i = base + u * 256 + (int)threadIdx.x;
-      v[u] = i < n2 ? __hip_atomic_load(const_cast<uint64_t*>(s2 + i), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
-                    : 0ull;
-    }
-#pragma unroll
-    for (int u = 0; u < B; ++u) {
-      const int i = base + u * 256 + (int)threadIdx.x;
-      if (i < n2) {
-        h2 hv;
-        hv[0] = (_Float16)__builtin_bit_cast(float, (uint32_t)v[u]);
-        hv[1] = (_Float16)__builtin_bit_cast(float, (uint32_t)(v[u] >> 32));
-        reinterpret_cast<h2*>(dst)[i] = hv;
-      }
-    }
-  }
-}
-
-// n coherent floats -> LDS floats, batched the same way
-__device__ __forceinline__ void copy_co_floats(float* dst, const float* src, int n) {
-  constexpr int B = 8;
-  for (int base = 0; base < n; base += B * 256) {
-    float v[B];
-#pragma unroll
-    for (int u = 0; u < B; ++u) {
-      const int i = base + u * 256 + (int)threadIdx.x;
-      v[u] = i < n ? ld_co(src + i) : 0.f;
-    }
-#pragma unroll
-    for (int u = 0; u < B; ++u) {
-      const int i = base + u * 256 + (int)threadIdx.x;
-      if (i < n) dst[i] = v[u];
-    }
+  if (threadIdx.x == 0) {
+    const uint32_t old =
+        __hip_atomic_fetch_add(sync + which * kSyncStride, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (old == target - 1)
+      for (int x = 0; x < kXcds; ++x)
+        __hip_atomic_store(flag_of(sync, x, which), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 }
 
@@ -113,6 +85,56 @@ __device__ __forceinline__ void copy_halves(_Float16* dst, const void* src, int 
   const uint4* s = reinterpret_cast<const uint4*>(src);
   uint4* d = reinterpret_cast<uint4*>(dst);
   for (int i = threadIdx.x; i < n / 8; i += blockDim.x) d[i] = s[i];
+}
+
+// dst[q] = src[index(q)] for q < n, 8 independent loads in flight per thread
+// (a plain loop would wait for each load before issuing the next)
+template <typename Dst, typename Index>
+__device__ __forceinline__ void gather_batched(Dst* dst, const float* src, int n, Index index) {
+  constexpr int B = 8;
+  for (int base = 0; base < n; base += B * 256) {
+    float v[B];
+#pragma unroll
+    for (int u = 0; u < B; ++u) {
+      const int q = base + u * 256 + (int)threadIdx.x;
+      v[u] = q < n ? src[index(q)] : 0.f;
+    }
+#pragma unroll
+    for (int u = 0; u < B; ++u) {
+      const int q = base + u * 256 + (int)threadIdx.x;
+      if (q < n) dst[q] = (Dst)v[u];
+    }
+  }
+}
+
+// Sums within aligned groups of `width` lanes (power of two <= 64); every lane
+// of a group receives the group's sum.  Rows of 16 lanes reduce with DPP.
+template <int CTRL>
+__device__ __forceinline__ float dppf(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float row16_sum(float v) {
+  v += dppf<0xB1>(v);   // quad_perm(1,0,3,2)
+  v += dppf<0x4E>(v);   // quad_perm(2,3,0,1)
+  v += dppf<0x124>(v);  // row_ror 4
+  v += dppf<0x128>(v);  // row_ror 8
+  return v;
+}
+__device__ __forceinline__ float readlane_f(float v, int l) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), l));
+}
+__device__ __forceinline__ float lane_group_sum(float v, int width) {
+  if (width == 64) {
+    v = row16_sum(v);
+    return (readlane_f(v, 0) + readlane_f(v, 16)) + (readlane_f(v, 32) + readlane_f(v, 48));
+  }
+  if (width == 32) {
+    v = row16_sum(v);
+    return v + __shfl_xor(v, 16, 64);
+  }
+  if (width == 16) return row16_sum(v);
+  for (int m = 1; m < width; m <<= 1) v += __shfl_xor(v, m, 64);
+  return v;
 }
 
 // per-lane 16-byte chunks of up to NB row-batches
@@ -201,229 +223,324 @@ struct Frag {
   }
 };
 
-// ------------------------------------------------------------------ items
+// ------------------------------------------------------------------ top-k
 
-// A: router rows (and the stacked shared-gate row) -> logits[t][row]
-__device__ void router_item(const DecodeArgs& a, int item, const _Float16* xs) {
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const RowGeom g = row_geom(a.H, 8);
-  const int nrows = a.E + 1;
-  const int row = (item * 4 + wave) * g.rpb + lane / g.lpr;
-  const size_t rb = (size_t)a.H;
-  const uint8_t* rows[1] = {row < nrows ? reinterpret_cast<const uint8_t*>(a.router_q) + row * rb : nullptr};
-  const uint16_t* srow[1] = {a.router_s + (size_t)(row < nrows ? row : 0) * (a.H / kGroup)};
-  Frag<8, 1, 4> f;
-  f.load(rows, srow, g);
-  float acc[1][kDecMaxT];
-  f.dot_shared<kDecMaxT>(g, xs, a.H, a.T, acc);
-#pragma unroll
-  for (int t = 0; t < kDecMaxT; ++t) {
-    const float v = group_sum(acc[0][t], g.lpr);
-    if (t < a.T && row < nrows && (lane % g.lpr) == 0) st_co(a.logits + (size_t)t * nrows + row, v);
+struct TopkScratch {
+  uint32_t gmax[8];
+  int count;
+  uint32_t ckey[kMaxExperts];
+  int cidx[kMaxExperts];
+  int sel_idx[kMaxTopK];
+  float sel_val[kMaxTopK];
+};
+
+// Top-k of one token's E router logits (LDS) by the whole workgroup.
+//
+// Selection is by logit (softmax is monotone), descending, ties to the lower
+// expert index; the kept probabilities are renormalised, which equals a
+// softmax over the k kept logits.  A lower bound tau of the k-th largest logit
+// is the smallest of k or more group maxima (groups of 32 experts); only the
+// experts at or above tau are ranked, each against the other candidates.
+__device__ void block_topk(const float* lg, int E, int k, int* ids_out, float* w_out, TopkScratch& sc) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const bool valid = tid < E;
+  const uint32_t key = valid ? order_key(lg[tid]) : 0u;
+  const bool grouped = E >= 32 * k;  // uniform
+  if (grouped) {
+    uint32_t m = key;
+    m = max(m, dpp_u32<0xB1>(m));
+    m = max(m, dpp_u32<0x4E>(m));
+    m = max(m, dpp_u32<0x124>(m));
+    m = max(m, dpp_u32<0x128>(m));
+    const uint32_t r0 = __builtin_amdgcn_readlane(m, 0), r1 = __builtin_amdgcn_readlane(m, 16);
+    const uint32_t r2 = __builtin_amdgcn_readlane(m, 32), r3 = __builtin_amdgcn_readlane(m, 48);
+    if (lane == 0) {
+      sc.gmax[2 * wave] = max(r0, r1);
+      sc.gmax[2 * wave + 1] = max(r2, r3);
+    }
+  }
+  if (tid == 0) sc.count = 0;
+  __syncthreads();
+  uint32_t tau = 0;
+  if (grouped) {
+    tau = 0xFFFFFFFFu;
+    const int ng = (E + 31) / 32;
+    for (int g = 0; g < ng; ++g) tau = min(tau, sc.gmax[g]);
+  }
+  if (valid && key >= tau) {
+    const int slot = atomicAdd(&sc.count, 1);
+    sc.ckey[slot] = key;
+    sc.cidx[slot] = tid;
+  }
+  __syncthreads();
+  const int C = sc.count;
+  if (tid < C) {
+    const uint32_t mk = sc.ckey[tid];
+    const int mi = sc.cidx[tid];
+    int r0 = 0, r1 = 0;
+    int c = 0;
+    for (; c + 1 < C; c += 2) {
+      const uint32_t k0 = sc.ckey[c], k1 = sc.ckey[c + 1];
+      const int i0 = sc.cidx[c], i1 = sc.cidx[c + 1];
+      r0 += (k0 > mk) || (k0 == mk && i0 < mi);
+      r1 += (k1 > mk) || (k1 == mk && i1 < mi);
+    }
+    if (c < C) r0 += (sc.ckey[c] > mk) || (sc.ckey[c] == mk && sc.cidx[c] < mi);
+    const int rank = r0 + r1;
+    if (rank < k) {
+      sc.sel_idx[rank] = mi;
+      sc.sel_val[rank] = lg[mi];
+    }
+  }
+  __syncthreads();
+  if (wave == 0) {
+    const float v0 = sc.sel_val[0];
+    const float e = lane < k ? expf(sc.sel_val[lane < k ? lane : 0] - v0) : 0.f;
+    const float s = row16_sum(e);  // k <= 8: lanes 0..k-1 sit in row 0
+    if (lane < k) {
+      ids_out[lane] = sc.sel_idx[lane];
+      w_out[lane] = e / s;
+    }
   }
 }
 
-// A: shared expert gate/up rows -> h_s[t][j] = silu(gate) * up
-__device__ void shup_item(const DecodeArgs& a, int item, const _Float16* xs) {
+// ------------------------------------------------------------------ items
+
+template <int MAXCPL>
+__device__ void router_item(const DecodeArgs& a, int H, int item, const _Float16* xs) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const RowGeom g = row_geom(a.H, 8);
-  const int jw = 2 * g.rpb;  // j per wave
-  const int j0 = (item * 4 + wave) * jw;
-  const size_t rb = (size_t)a.H;
+  const RowGeom g = row_geom(H, 8);
+  const int nrows = a.E + 1;
+  const int rl = wave * g.rpb + lane / g.lpr;  // row within the item
+  const int row = item * a.p.lg_rows + rl;
+  const uint8_t* rows[1] = {row < nrows ? reinterpret_cast<const uint8_t*>(a.router_q) + (size_t)row * H : nullptr};
+  const uint16_t* srow[1] = {a.router_s + (size_t)(row < nrows ? row : 0) * (H / kGroup)};
+  Frag<8, 1, MAXCPL> f;
+  f.load(rows, srow, g);
+  float acc[1][kDecMaxT];
+  f.template dot_shared<kDecMaxT>(g, xs, H, a.T, acc);
+#pragma unroll
+  for (int t = 0; t < kDecMaxT; ++t) {
+    if (t < a.T) {
+      const float v = lane_group_sum(acc[0][t], g.lpr);
+      if (row < nrows && (lane % g.lpr) == 0) st_co(a.logits + ((size_t)item * a.T + t) * a.p.lg_stride + rl, v);
+    }
+  }
+}
+
+template <int MAXCPL>
+__device__ void shup_item(const DecodeArgs& a, int H, int Is, int item, const _Float16* xs) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const RowGeom g = row_geom(H, 8);
   const uint8_t* base = reinterpret_cast<const uint8_t*>(a.sh13_q);
   const uint8_t* rows[4];
   const uint16_t* srow[4];
-  int jj[2];
+  int jl[2];
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
-    const int j = j0 + h * g.rpb + lane / g.lpr;
-    jj[h] = j;
-    const bool ok = j < a.Is;
-    rows[h] = ok ? base + (size_t)j * rb : nullptr;
-    rows[2 + h] = ok ? base + (size_t)(a.Is + j) * rb : nullptr;
-    srow[h] = a.sh13_s + (size_t)(ok ? j : 0) * (a.H / kGroup);
-    srow[2 + h] = a.sh13_s + (size_t)(ok ? a.Is + j : 0) * (a.H / kGroup);
+    jl[h] = (wave * 2 + h) * g.rpb + lane / g.lpr;
+    const int j = item * a.p.hs_cols + jl[h];
+    const bool ok = j < Is;
+    rows[h] = ok ? base + (size_t)j * H : nullptr;
+    rows[2 + h] = ok ? base + (size_t)(Is + j) * H : nullptr;
+    srow[h] = a.sh13_s + (size_t)(ok ? j : 0) * (H / kGroup);
+    srow[2 + h] = a.sh13_s + (size_t)(ok ? Is + j : 0) * (H / kGroup);
   }
-  Frag<8, 4, 4> f;
+  Frag<8, 4, MAXCPL> f;
   f.load(rows, srow, g);
   float acc[4][kDecMaxT];
-  f.dot_shared<kDecMaxT>(g, xs, a.H, a.T, acc);
+  f.template dot_shared<kDecMaxT>(g, xs, H, a.T, acc);
 #pragma unroll
   for (int h = 0; h < 2; ++h)
 #pragma unroll
     for (int t = 0; t < kDecMaxT; ++t) {
-      const float gate = group_sum(acc[h][t], g.lpr);
-      const float up = group_sum(acc[2 + h][t], g.lpr);
-      if (t < a.T && jj[h] < a.Is && (lane % g.lpr) == 0)
-        st_co(a.h_s + (size_t)t * a.Is + jj[h], silu_f(gate) * up);
+      if (t < a.T) {
+        const float gate = lane_group_sum(acc[h][t], g.lpr);
+        const float up = lane_group_sum(acc[2 + h][t], g.lpr);
+        if (item * a.p.hs_cols + jl[h] < Is && (lane % g.lpr) == 0)
+          st_co(a.h_s + ((size_t)item * a.T + t) * a.p.hs_stride + jl[h], silu_f(gate) * up);
+      }
     }
 }
 
-// B: one (token, slot, j-block): expert gate/up rows -> h_e[t][i][j]
-__device__ void up_item(const DecodeArgs& a, int item, const _Float16* xs, const int (*ids)[kMaxTopK]) {
+template <int MAXCPL>
+__device__ void up_item(const DecodeArgs& a, int H, int I, int item, const _Float16* xs, const int (*ids)[kMaxTopK]) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const RowGeom g = row_geom(a.H, 4);
-  const int jblk = item % a.up_jblocks;
-  const int ti = item / a.up_jblocks;
+  const RowGeom g = row_geom(H, 4);
+  const int jblk = item % a.p.up_jblocks;
+  const int ti = item / a.p.up_jblocks;
   const int t = ti / a.k, i = ti % a.k;
   const int e = ids[t][i];
-  const int jw = 4 * g.rpb;
-  const int j0 = (jblk * 4 + wave) * jw;
-  const size_t rb = (size_t)a.H / 2;
-  const size_t ng = a.H / kGroup;
-  const uint8_t* wbase = a.w13_q + (size_t)(e < 0 ? 0 : e) * 2 * a.I * rb;
-  const uint16_t* sbase = a.w13_s + (size_t)(e < 0 ? 0 : e) * 2 * a.I * ng;
+  const size_t rb = (size_t)H / 2;
+  const size_t ng = H / kGroup;
+  const uint8_t* wbase = a.w13_q + (size_t)(e < 0 ? 0 : e) * 2 * I * rb;
+  const uint16_t* sbase = a.w13_s + (size_t)(e < 0 ? 0 : e) * 2 * I * ng;
   const uint8_t* rows[8];
   const uint16_t* srow[8];
-  int jj[4];
+  int jl[4];
 #pragma unroll
   for (int h = 0; h < 4; ++h) {
-    const int j = j0 + h * g.rpb + lane / g.lpr;
-    jj[h] = j;
-    const bool ok = e >= 0 && j < a.I;
+    jl[h] = (wave * 4 + h) * g.rpb + lane / g.lpr;
+    const int j = jblk * a.p.he_cols + jl[h];
+    const bool ok = e >= 0 && j < I;
     rows[h] = ok ? wbase + (size_t)j * rb : nullptr;
-    rows[4 + h] = ok ? wbase + (size_t)(a.I + j) * rb : nullptr;
+    rows[4 + h] = ok ? wbase + (size_t)(I + j) * rb : nullptr;
     srow[h] = sbase + (size_t)(ok ? j : 0) * ng;
-    srow[4 + h] = sbase + (size_t)(ok ? a.I + j : 0) * ng;
+    srow[4 + h] = sbase + (size_t)(ok ? I + j : 0) * ng;
   }
-  Frag<4, 8, 2> f;
+  Frag<4, 8, MAXCPL> f;
   f.load(rows, srow, g);
   float acc[8][1];
-  f.dot_shared<1>(g, xs + (size_t)t * a.H, a.H, 1, acc);
+  f.template dot_shared<1>(g, xs + (size_t)t * H, H, 1, acc);
+  float* dst = a.h_e + (size_t)item * a.p.he_stride;
 #pragma unroll
   for (int h = 0; h < 4; ++h) {
-    const float gate = group_sum(acc[h][0], g.lpr);
-    const float up = group_sum(acc[4 + h][0], g.lpr);
-    if (jj[h] < a.I && (lane % g.lpr) == 0)
-      st_co(a.h_e + ((size_t)t * a.k + i) * a.I + jj[h], e >= 0 ? silu_f(gate) * up : 0.f);
+    const float gate = lane_group_sum(acc[h][0], g.lpr);
+    const float up = lane_group_sum(acc[4 + h][0], g.lpr);
+    if (jblk * a.p.he_cols + jl[h] < I && (lane % g.lpr) == 0) st_co(dst + jl[h], e >= 0 ? silu_f(gate) * up : 0.f);
   }
 }
 
-// B: shared expert down rows -> s_sh[t][n]
-__device__ void sd_item(const DecodeArgs& a, int item, const _Float16* hs) {
+template <int MAXCPL>
+__device__ void sd_item(const DecodeArgs& a, int H, int Is, int item, const _Float16* hs) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const RowGeom g = row_geom(a.Is, 8);
-  const int rw = 4 * g.rpb;
-  const int n0 = (item * 4 + wave) * rw;
-  const size_t rb = (size_t)a.Is;
-  const size_t ng = a.Is / kGroup;
+  const RowGeom g = row_geom(Is, 8);
   const uint8_t* base = reinterpret_cast<const uint8_t*>(a.sh2_q);
+  const size_t ng = Is / kGroup;
   const uint8_t* rows[4];
   const uint16_t* srow[4];
-  int nn[4];
+  int nl[4];
 #pragma unroll
   for (int h = 0; h < 4; ++h) {
-    const int n = n0 + h * g.rpb + lane / g.lpr;
-    nn[h] = n;
-    rows[h] = n < a.H ? base + (size_t)n * rb : nullptr;
-    srow[h] = a.sh2_s + (size_t)(n < a.H ? n : 0) * ng;
+    nl[h] = (wave * 4 + h) * g.rpb + lane / g.lpr;
+    const int n = item * a.p.ss_rows + nl[h];
+    rows[h] = n < H ? base + (size_t)n * Is : nullptr;
+    srow[h] = a.sh2_s + (size_t)(n < H ? n : 0) * ng;
   }
-  Frag<8, 4, 4> f;
+  Frag<8, 4, MAXCPL> f;
   f.load(rows, srow, g);
   float acc[4][kDecMaxT];
-  f.dot_shared<kDecMaxT>(g, hs, a.Is, a.T, acc);
+  f.template dot_shared<kDecMaxT>(g, hs, Is, a.T, acc);
 #pragma unroll
   for (int h = 0; h < 4; ++h)
 #pragma unroll
     for (int t = 0; t < kDecMaxT; ++t) {
-      const float v = group_sum(acc[h][t], g.lpr);
-      if (t < a.T && nn[h] < a.H && (lane % g.lpr) == 0) st_co(a.s_sh + (size_t)t * a.H + nn[h], v);
+      if (t < a.T) {
+        const float v = lane_group_sum(acc[h][t], g.lpr);
+        if (item * a.p.ss_rows + nl[h] < H && (lane % g.lpr) == 0)
+          st_co(a.s_sh + ((size_t)item * a.T + t) * a.p.ss_stride + nl[h], v);
+      }
     }
 }
 
 // ------------------------------------------------------------------ kernel
 
-template <int MODE>
+// HC, IC, ISC: compile-time H, I, Is (0: taken from the arguments)
+template <int MODE, int HC, int IC, int ISC>
 __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
   extern __shared__ uint4 smem_raw[];
+  const int H = HC ? HC : a.H;
+  const int I = IC ? IC : a.I;
+  const int Is = ISC ? ISC : a.Is;
+  constexpr int CPL8H = HC ? (HC / 1024 > 1 ? HC / 1024 : 1) : 4;
+  constexpr int CPL4H = HC ? (HC / 2048 > 1 ? HC / 2048 : 1) : 2;
+  constexpr int CPL8S = ISC ? (ISC / 1024 > 1 ? ISC / 1024 : 1) : 4;
+  constexpr int CPL4I = IC ? (IC / 2048 > 1 ? IC / 2048 : 1) : 2;
+  const DecodePlan& p = a.p;
+  const int T = a.T, E = a.E, k = a.k;
+
   _Float16* act = reinterpret_cast<_Float16*>(smem_raw);  // x [T][H], later h_e [T][k][I]
-  const int act_halves = max(a.T * a.H, a.T * a.k * a.I);
+  const int act_halves = max(T * H, T * k * I);
   _Float16* hs_lds = act + act_halves;                    // h_s [T][Is]
   __shared__ int s_ids[kDecMaxT][kMaxTopK];
   __shared__ float s_w[kDecMaxT][kMaxTopK];
   __shared__ float s_sig[kDecMaxT];
   __shared__ float s_red[4][64];
-  __shared__ float s_logits_raw[kDecMaxT * (kMaxExperts + 1)];
+  __shared__ float s_logits[kDecMaxT * (kMaxExperts + 1)];
+  __shared__ TopkScratch s_topk;
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int nb = gridDim.x, b = blockIdx.x;
-  const int T = a.T;
 
-  copy_halves(act, a.x, T * a.H);
+  copy_halves(act, a.x, T * H);
   __syncthreads();
 
   // ---------------- stage A
   if (MODE == DEC_FORWARD) {
-    const int nA = a.n_router + a.n_shup;
+    const int nA = p.n_router + p.n_shup;
     for (int item = b; item < nA; item += nb) {
-      const bool is_router = item < a.n_router;
-      if (is_router) router_item(a, item, act);
-      else shup_item(a, item - a.n_router, act);
-      signal_item(a.sync, is_router ? SYNC_ROUTER : SYNC_SHUP);
+      const bool is_router = item < p.n_router;
+      if (is_router) router_item<CPL8H>(a, H, item, act);
+      else shup_item<CPL8H>(a, H, Is, item - p.n_router, act);
+      signal_item(a.sync, is_router ? SYNC_ROUTER : SYNC_SHUP, is_router ? p.n_router : p.n_shup);
     }
   }
 
   // ---------------- routing into LDS
   if (MODE == DEC_FORWARD) {
-    wait_count(a.sync, SYNC_ROUTER, a.n_router);
-    const int nrows = a.E + 1;
-    copy_co_floats(s_logits_raw, a.logits, T * nrows);  // [T][E+1]
+    wait_done(a.sync, SYNC_ROUTER);
+    const int nrows = E + 1;
+    gather_batched(s_logits, a.logits, T * nrows, [&](int q) {
+      const int t = q / nrows, r = q % nrows;
+      return ((size_t)(r / p.lg_rows) * T + t) * p.lg_stride + r % p.lg_rows;
+    });
     __syncthreads();
-    for (int t = wave; t < T; t += 4) {
-      wave_topk(s_logits_raw + t * nrows, a.E, a.k, s_ids[t], s_w[t]);
-      if (lane == 0) s_sig[t] = sigmoid_f(s_logits_raw[t * nrows + a.E]);
+    for (int t = 0; t < T; ++t) {
+      block_topk(s_logits + t * nrows, E, k, s_ids[t], s_w[t], s_topk);
+      if (tid == 0) s_sig[t] = sigmoid_f(s_logits[t * nrows + E]);
+      __syncthreads();
     }
-    __syncthreads();
     if (b == 0) {
-      for (int p = tid; p < T * a.k; p += blockDim.x) {
-        const int t = p / a.k, i = p % a.k;
-        if (a.ids_out) a.ids_out[p] = s_ids[t][i];
-        if (a.w_out) a.w_out[p] = s_w[t][i];
+      for (int q = tid; q < T * k; q += blockDim.x) {
+        const int t = q / k, i = q % k;
+        if (a.ids_out) a.ids_out[q] = s_ids[t][i];
+        if (a.w_out) a.w_out[q] = s_w[t][i];
       }
       for (int t = tid; t < T; t += blockDim.x)
         if (a.sigma_out) a.sigma_out[t] = s_sig[t];
-      if (a.logits_out)
-        for (int p = tid; p < T * nrows; p += blockDim.x) a.logits_out[p] = s_logits_raw[p];
     }
   } else {
-    for (int p = tid; p < T * a.k; p += blockDim.x) {
-      const int t = p / a.k, i = p % a.k;
-      const int e = a.ids_in[p];
-      s_ids[t][i] = (e >= 0 && e < a.E) ? e : -1;  // invalid ids contribute nothing
-      s_w[t][i] = a.w_in[p];
+    for (int q = tid; q < T * k; q += blockDim.x) {
+      const int t = q / k, i = q % k;
+      const int e = a.ids_in[q];
+      s_ids[t][i] = (e >= 0 && e < E) ? e : -1;  // invalid ids contribute nothing
+      s_w[t][i] = a.w_in[q];
     }
     __syncthreads();
   }
 
   // ---------------- stage B
   {
-    const int nB = a.n_up + (MODE == DEC_FORWARD ? a.n_sd : 0);
+    const int nB = p.n_up + (MODE == DEC_FORWARD ? p.n_sd : 0);
     bool hs_ready = false;
     for (int item = b; item < nB; item += nb) {
-      if (item < a.n_up) {
-        up_item(a, item, act, s_ids);
-        signal_item(a.sync, SYNC_UP);
+      if (item < p.n_up) {
+        up_item<CPL4H>(a, H, I, item, act, s_ids);
+        signal_item(a.sync, SYNC_UP, p.n_up);
       } else {
         if (!hs_ready) {
-          wait_count(a.sync, SYNC_SHUP, a.n_shup);
-          copy_co_to_halves(hs_lds, a.h_s, T * a.Is);
+          wait_done(a.sync, SYNC_SHUP);
+          gather_batched(hs_lds, a.h_s, T * Is, [&](int q) {
+            const int t = q / Is, j = q % Is;
+            return ((size_t)(j / p.hs_cols) * T + t) * p.hs_stride + j % p.hs_cols;
+          });
           __syncthreads();
           hs_ready = true;
         }
-        sd_item(a, item - a.n_up, hs_lds);
-        signal_item(a.sync, SYNC_SD);
+        sd_item<CPL8S>(a, H, Is, item - p.n_up, hs_lds);
+        signal_item(a.sync, SYNC_SD, p.n_sd);
       }
     }
   }
 
   // ---------------- stage C: down rows of every slot, combine, shared term
   {
-    const RowGeom g = row_geom(a.I, 4);
-    const int nblk = a.H / g.rpb;
-    const size_t rb = (size_t)a.I / 2;
-    const size_t ng = a.I / kGroup;
+    const RowGeom g = row_geom(I, 4);
+    const int nblk = H / g.rpb;
+    const size_t rb = (size_t)I / 2;
+    const size_t ng = I / kGroup;
     bool h_ready = false;
-    for (int item = b; item < a.n_down; item += nb) {
+    for (int item = b; item < p.n_down; item += nb) {
       const int t = item / nblk;
       const int n0 = (item % nblk) * g.rpb;
       const int n = n0 + lane / g.lpr;
@@ -433,29 +550,32 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
 #pragma unroll
       for (int q = 0; q < 2; ++q) {
         const int i = wave + 4 * q;
-        const int e = i < a.k ? s_ids[t][i] : -1;
+        const int e = i < k ? s_ids[t][i] : -1;
         slot[q] = e >= 0 ? i : -1;
-        rows[q] = e >= 0 ? a.w2_q + ((size_t)e * a.H + n) * rb : nullptr;
-        srow[q] = a.w2_s + ((size_t)(e >= 0 ? e : 0) * a.H + n) * ng;
+        rows[q] = e >= 0 ? a.w2_q + ((size_t)e * H + n) * rb : nullptr;
+        srow[q] = a.w2_s + ((size_t)(e >= 0 ? e : 0) * H + n) * ng;
       }
-      Frag<4, 2, 2> f;
+      Frag<4, 2, CPL4I> f;
       f.load(rows, srow, g);
       if (!h_ready) {
-        wait_count(a.sync, SYNC_UP, a.n_up);
-        if (MODE == DEC_FORWARD) wait_count(a.sync, SYNC_SD, a.n_sd);
-        copy_co_to_halves(act, a.h_e, T * a.k * a.I);
+        wait_done(a.sync, SYNC_UP);
+        if (MODE == DEC_FORWARD) wait_done(a.sync, SYNC_SD);
+        gather_batched(act, a.h_e, T * k * I, [&](int q) {
+          const int ti = q / I, j = q % I;
+          return (size_t)(ti * p.up_jblocks + j / p.he_cols) * p.he_stride + j % p.he_cols;
+        });
         __syncthreads();
         h_ready = true;
       }
       const _Float16* hact[2];
 #pragma unroll
-      for (int q = 0; q < 2; ++q) hact[q] = slot[q] >= 0 ? act + ((size_t)t * a.k + slot[q]) * a.I : nullptr;
+      for (int q = 0; q < 2; ++q) hact[q] = slot[q] >= 0 ? act + ((size_t)t * k + slot[q]) * I : nullptr;
       float acc[2];
       f.dot_per_batch(g, hact, acc);
       float part = 0.f;
 #pragma unroll
       for (int q = 0; q < 2; ++q) {
-        const float y = group_sum(acc[q], g.lpr);
+        const float y = lane_group_sum(acc[q], g.lpr);
         if (slot[q] >= 0) part += s_w[t][slot[q]] * y;
       }
       if ((lane % g.lpr) == 0) s_red[wave][lane / g.lpr] = part;
@@ -463,9 +583,10 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
       if (tid < g.rpb) {
         float v = s_red[0][tid] + s_red[1][tid] + s_red[2][tid] + s_red[3][tid];
         const int nn = n0 + tid;
-        if (MODE == DEC_FORWARD) v += s_sig[t] * ld_co(a.s_sh + (size_t)t * a.H + nn);
+        if (MODE == DEC_FORWARD)
+          v += s_sig[t] * a.s_sh[((size_t)(nn / p.ss_rows) * T + t) * p.ss_stride + nn % p.ss_rows];
         const _Float16 hv = (_Float16)v;
-        a.out[(size_t)t * a.H + nn] = __builtin_bit_cast(uint16_t, hv);
+        a.out[(size_t)t * H + nn] = __builtin_bit_cast(uint16_t, hv);
       }
       __syncthreads();
     }
@@ -474,30 +595,43 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
   // ---------------- drain: the last workgroup out clears the counters
   __syncthreads();
   if (tid == 0) {
-    const uint32_t old = __hip_atomic_fetch_add(a.sync + SYNC_EXIT * kSyncStride, 1u, __ATOMIC_RELAXED,
-                                                __HIP_MEMORY_SCOPE_AGENT);
+    const uint32_t old =
+        __hip_atomic_fetch_add(a.sync + SYNC_EXIT * kSyncStride, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     if (old == (uint32_t)nb - 1) {
-      for (int w = 0; w < SYNC_EXIT + 1; ++w)
+      for (int w = 0; w < SYNC_EXIT + 1; ++w) {
         __hip_atomic_store(a.sync + w * kSyncStride, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        for (int x = 0; x < kXcds; ++x)
+          __hip_atomic_store(flag_of(a.sync, x, w), 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
     }
   }
 }
 
 // ------------------------------------------------------------------ host side
 
-int decode_blocks_per_cu(int mode, size_t lds_bytes) {
+bool decode_real_widths(int H, int I, int Is) { return H == 2048 && I == 512 && Is == 512; }
+
+template <int MODE>
+static int occupancy(bool real, size_t lds) {
   int n = 0;
-  hipError_t err = mode == DEC_FORWARD
-                       ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_kernel<DEC_FORWARD>, 256, lds_bytes)
-                       : hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_kernel<DEC_EXPERTS>, 256, lds_bytes);
+  hipError_t err = real ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_kernel<MODE, 2048, 512, 512>, 256, lds)
+                        : hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_kernel<MODE, 0, 0, 0>, 256, lds);
   return err == hipSuccess ? n : 0;
 }
 
+int decode_blocks_per_cu(int mode, bool real, size_t lds_bytes) {
+  return mode == DEC_FORWARD ? occupancy<DEC_FORWARD>(real, lds_bytes) : occupancy<DEC_EXPERTS>(real, lds_bytes);
+}
+
 int launch_decode(const DecodeArgs& a, int mode, int grid, size_t lds_bytes, hipStream_t s) {
-  if (mode == DEC_FORWARD)
-    hipLaunchKernelGGL(decode_kernel<DEC_FORWARD>, dim3(grid), dim3(256), lds_bytes, s, a);
-  else
-    hipLaunchKernelGGL(decode_kernel<DEC_EXPERTS>, dim3(grid), dim3(256), lds_bytes, s, a);
+  const bool real = decode_real_widths(a.H, a.I, a.Is);
+  if (mode == DEC_FORWARD) {
+    if (real) hipLaunchKernelGGL((decode_kernel<DEC_FORWARD, 2048, 512, 512>), dim3(grid), dim3(256), lds_bytes, s, a);
+    else hipLaunchKernelGGL((decode_kernel<DEC_FORWARD, 0, 0, 0>), dim3(grid), dim3(256), lds_bytes, s, a);
+  } else {
+    if (real) hipLaunchKernelGGL((decode_kernel<DEC_EXPERTS, 2048, 512, 512>), dim3(grid), dim3(256), lds_bytes, s, a);
+    else hipLaunchKernelGGL((decode_kernel<DEC_EXPERTS, 0, 0, 0>), dim3(grid), dim3(256), lds_bytes, s, a);
+  }
   return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_LAUNCH;
 }
 
