@@ -18,7 +18,6 @@ using namespace moe;
 constexpr int kMaxT = 65536;
 constexpr int kMaxWidth = 4096;
 constexpr size_t kDecodeMaxLds = 64 * 1024;
-constexpr int kTileRows = 32;
 
 size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
@@ -57,9 +56,10 @@ bool use_decode(const moe_dims* d, int T) {
   return decode_admissible(d, T);  // AUTO and DECODE both take it when it fits
 }
 
+// each expert with c > 0 rows takes ceil(c / kTileRows) tiles
 int max_route_tiles(const moe_dims* d, int T) {
   const int P = T * d->top_k;
-  return std::min(d->num_experts, P) + P / kTileRows;
+  return std::min(d->num_experts, P) + P / kTileRows + 1;
 }
 
 // --------------------------------------------------------------- workspace
@@ -113,8 +113,8 @@ void carve_chunk(const moe_dims* d, int T, Carve& c, ChunkArgs& a) {
   a.n_tiles = c.take<int32_t>(4);
   a.h = c.take<_Float16>(P * d->expert_inter * 2);
   a.hs = c.take<_Float16>((size_t)T * d->shared_inter * 2);
-  a.y = c.take<float>(P * d->hidden * 4);
-  a.ys = c.take<float>((size_t)T * d->hidden * 4);
+  a.y = c.take<_Float16>(P * d->hidden * 2);
+  a.ys = c.take<_Float16>((size_t)T * d->hidden * 2);
 }
 
 size_t workspace_bytes(const moe_dims* d, int T) {

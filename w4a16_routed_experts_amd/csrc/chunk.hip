@@ -1,176 +1,128 @@
 // Multi-token path of the routed MoE block: grouped GEMMs on MFMA.
 //
-// The same block as the decode path (the Chimera notebook, section 5; the
+// The same block as the few-token path (the Chimera notebook, section 5; the
 // router ordering of section 5.2; int8 group-64 router rows stacked with the
 // shared gate, the TensorFold PR "Design"), organised for many tokens:
-//   1. router GEMM          logits[T][E+1]               (int8 rows, MFMA)
+//   1. router GEMM          logits[T][E+1]   (int8 rows, MFMA, per-group scales)
 //   2. top-k per token      ids, renormalised weights, sigma
 //   3. bucketing            (token, slot) pairs sorted by expert, then pair
-//                           index; 32-row tiles per expert; shared-expert tiles
-//   4. gate/up GEMM         h[row][I] = silu(x W_gate^T) * (x W_up^T)  (fp16)
-//   5. down GEMM            y[row][H] = w * (h W_down^T)                (fp32)
+//                           index; 64- or 32-row tiles per expert; shared tiles
+//   4. gate/up GEMM         h[row][I] = silu(x W_gate^T) * (x W_up^T)   (fp16)
+//   5. down GEMM            y[row][H] = w * (h W_down^T)                 (fp16)
 //   6. combine              out[t] = sum_i y[pos(t,i)] + sigma_t * s[t]
-// Each expert's weights are streamed once per 32-row tile; a tile's rows are
-// the tokens routed to that expert.  Scales are applied per 64-wide K group
-// to fp32 partial sums, so the MFMA products of binary16 codes and binary16
-// activations are exact.
+// Each tile streams its expert's weights once; a tile's rows are the tokens
+// routed to that expert.
 #include "chunk.hpp"
 
 namespace moe {
 
 // ---------------------------------------------------------------------------
-// MFMA tile core: acc[f] += A[32][K] . W_f[32][K]^T for NF fragments of 32
-// weight rows.  MFMA 32x32x16 f16: lane l works on weight row (l % 32) of a
-// fragment and K offsets 32*(l/32) .. +32 of each 64-wide group, so the 16
-// codes of every MFMA step share one scale.
+// MFMA 32x32x16 f16 operand layout used throughout: lane l works on row
+// (l % 32) of a 32-row operand and on K offsets 32*(l/32) + 8*s .. +8 of each
+// 64-wide group in MFMA step s (0..3).  A and B use the same K assignment, so
+// the products pair up; the 16 K values of one step lie in one group.
+// Accumulator element i of lane l is row 8*(i/4) + 4*(l/32) + (i%4), column
+// l % 32.
 // ---------------------------------------------------------------------------
 
-static constexpr int kBM = 32;                 // tile rows (tokens)
-static constexpr int kKB = 256;                // K per LDS stage
-static constexpr int kLdsStride = kKB + 8;     // halves per LDS row (padding)
+__device__ __forceinline__ int acc_row(int i) { return 8 * (i >> 2) + 4 * ((threadIdx.x & 63) >> 5) + (i & 3); }
 
-// Stage A[32][kb .. kb+kKB) into LDS, each 8-element run permuted to the
-// (0,4,1,5,2,6,3,7) order of the weight conversion.
-__device__ __forceinline__ void stage_a(_Float16* lds, const _Float16* const* rows, int kb, int K) {
-  const int nchunk = kKB / 8;  // 16-byte chunks per row
-  for (int idx = threadIdx.x; idx < kBM * nchunk; idx += blockDim.x) {
-    const int m = idx / nchunk, c = idx % nchunk;
-    const int k = kb + 8 * c;
-    uint4 v = make_uint4(0, 0, 0, 0);
-    if (rows[m] != nullptr && k < K) v = *reinterpret_cast<const uint4*>(rows[m] + k);
-    const uint32_t x[4] = {v.x, v.y, v.z, v.w};
-    uint32_t o[4];
-    perm8_words(x, o);
-    *reinterpret_cast<uint4*>(lds + m * kLdsStride + 8 * c) = make_uint4(o[0], o[1], o[2], o[3]);
-  }
-}
-
-// Weight codes of this lane for one 64-group: K offsets kg + 32*(lane/32) .. +32
-template <int BITS>
-struct BChunk {
-  uint4 q[BITS == 4 ? 1 : 2];
-};
-
-template <int BITS>
-__device__ __forceinline__ BChunk<BITS> load_b(const uint8_t* row, int kg) {
-  const int g = (threadIdx.x & 63) >> 5;
-  BChunk<BITS> c;
-  if (row == nullptr) {
-#pragma unroll
-    for (int i = 0; i < (BITS == 4 ? 1 : 2); ++i) c.q[i] = make_uint4(0, 0, 0, 0);
-    return c;
-  }
-  if (BITS == 4) {
-    c.q[0] = *reinterpret_cast<const uint4*>(row + (kg + 32 * g) / 2);
-  } else {
-    const uint4* p = reinterpret_cast<const uint4*>(row + kg + 32 * g);
-    c.q[0] = p[0];
-    c.q[1] = p[1];
-  }
-  return c;
-}
-
-// operand of MFMA step s (0..3) from a loaded chunk
-template <int BITS>
-__device__ __forceinline__ h8 b_step(const BChunk<BITS>& c, int s) {
-  h2 w[4];
-  if (BITS == 4) {
-    const uint32_t ws[4] = {c.q[0].x, c.q[0].y, c.q[0].z, c.q[0].w};
-    int4x8_to_h2x4(ws[s], w);
-  } else {
-    const uint32_t ws[8] = {c.q[0].x, c.q[0].y, c.q[0].z, c.q[0].w, c.q[1].x, c.q[1].y, c.q[1].z, c.q[1].w};
-    int8x8_to_h2x4(ws[2 * s], ws[2 * s + 1], w);
-  }
+__device__ __forceinline__ h8 pack8(const h2 w[4]) {
   h8 r;
   r[0] = w[0][0]; r[1] = w[0][1]; r[2] = w[1][0]; r[3] = w[1][1];
   r[4] = w[2][0]; r[5] = w[2][1]; r[6] = w[3][0]; r[7] = w[3][1];
   return r;
 }
 
-// acc[f] += A . W_f^T over K (a multiple of 64).  brow[f]: this lane's weight
-// row (nullptr = zero row); bscale[f]: its scales.
-template <int BITS, int NF>
-__device__ __forceinline__ void tile_gemm(_Float16* lds, const _Float16* const* arows, int K,
-                                          const uint8_t* const brow[NF], const uint16_t* const bscale[NF],
-                                          f16v acc[NF]) {
-  const int lane = threadIdx.x & 63;
-  const int m = lane & 31, g = lane >> 5;
-  for (int kb = 0; kb < K; kb += kKB) {
-    __syncthreads();
-    stage_a(lds, arows, kb, K);
-    __syncthreads();
-    const int ngr = min(kKB, K - kb) / kGroup;
-    for (int gi = 0; gi < ngr; ++gi) {
-      const int kg = kb + gi * kGroup;
-      BChunk<BITS> bc[NF];
-      float sc[NF];
-#pragma unroll
-      for (int f = 0; f < NF; ++f) {
-        bc[f] = load_b<BITS>(brow[f], kg);
-        sc[f] = brow[f] ? half_bits_to_float(bscale[f][kg / kGroup]) : 0.f;
-      }
-      const _Float16* ap = lds + m * kLdsStride + gi * kGroup + 32 * g;
-      h8 av[4];
-#pragma unroll
-      for (int s = 0; s < 4; ++s) av[s] = *reinterpret_cast<const h8*>(ap + 8 * s);
-#pragma unroll
-      for (int f = 0; f < NF; ++f) {
-        f16v p = {};
-#pragma unroll
-        for (int s = 0; s < 4; ++s) p = __builtin_amdgcn_mfma_f32_32x32x16_f16(av[s], b_step<BITS>(bc[f], s), p, 0, 0, 0);
-#pragma unroll
-        for (int i = 0; i < 16; ++i) acc[f][i] = fmaf(p[i], sc[f], acc[f][i]);
-      }
-    }
-  }
+// 8 activations (one 16-byte chunk, natural order) -> MFMA operand in the
+// (0,4,1,5,2,6,3,7) order of the weight conversion
+__device__ __forceinline__ h8 act_operand(uint4 v) {
+  const uint32_t x[4] = {v.x, v.y, v.z, v.w};
+  uint32_t o[4];
+  perm8_words(x, o);
+  return __builtin_bit_cast(h8, make_uint4(o[0], o[1], o[2], o[3]));
 }
 
-// row of the 32x32 accumulator held in element i of this lane
-__device__ __forceinline__ int acc_row(int i) { return 8 * (i >> 2) + 4 * ((threadIdx.x & 63) >> 5) + (i & 3); }
-
 // ---------------------------------------------------------------------------
-// 1. router GEMM: logits[t][r], r < E+1
+// 1. router GEMM: 32 tokens x 32 rows per workgroup; the four waves take
+//    interleaved 64-groups of K and are summed through LDS.  The scales are
+//    applied per group to fp32 partial sums, so routing sees logits accurate to
+//    fp32 rounding.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void router_gemm_kernel(ChunkArgs a) {
-  __shared__ __attribute__((aligned(16))) _Float16 lds[kBM * kLdsStride];
-  __shared__ const _Float16* arows[kBM];
+  __shared__ float red[4][16][64];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int t0 = blockIdx.x * kBM;
-  const int nrows = a.E + 1;
-  if (threadIdx.x < kBM) {
-    const int t = t0 + threadIdx.x;
-    arows[threadIdx.x] = t < a.T ? reinterpret_cast<const _Float16*>(a.x) + (size_t)t * a.H : nullptr;
+  const int m = lane & 31, g = lane >> 5;
+  const int t = blockIdx.x * 32 + m;  // A row (token)
+  const int r = blockIdx.y * 32 + m;  // B row (router row)
+  const int nrows = a.E + 1, H = a.H, ngr = H / kGroup;
+  const _Float16* xrow = t < a.T ? reinterpret_cast<const _Float16*>(a.x) + (size_t)t * H : nullptr;
+  const int8_t* rrow = r < nrows ? a.router_q + (size_t)r * H : nullptr;
+  f16v acc = {};
+  constexpr int BATCH = 4;
+  for (int g0 = wave; g0 < ngr; g0 += 4 * BATCH) {
+    uint4 xa[BATCH][4], wb[BATCH][2];
+    float sc[BATCH];
+#pragma unroll
+    for (int u = 0; u < BATCH; ++u) {
+      const int gi = g0 + 4 * u;
+      const bool ok = gi < ngr;
+      const int k0 = gi * kGroup + 32 * g;
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        xa[u][q] = (ok && xrow) ? reinterpret_cast<const uint4*>(xrow + k0)[q] : make_uint4(0, 0, 0, 0);
+#pragma unroll
+      for (int q = 0; q < 2; ++q)
+        wb[u][q] = (ok && rrow) ? reinterpret_cast<const uint4*>(rrow + k0)[q] : make_uint4(0, 0, 0, 0);
+      sc[u] = (ok && rrow) ? half_bits_to_float(a.router_s[(size_t)r * ngr + gi]) : 0.f;
+    }
+#pragma unroll
+    for (int u = 0; u < BATCH; ++u) {
+      f16v p = {};
+      const uint32_t ws[8] = {wb[u][0].x, wb[u][0].y, wb[u][0].z, wb[u][0].w,
+                              wb[u][1].x, wb[u][1].y, wb[u][1].z, wb[u][1].w};
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        h2 w[4];
+        int8x8_to_h2x4(ws[2 * s], ws[2 * s + 1], w);
+        p = __builtin_amdgcn_mfma_f32_32x32x16_f16(act_operand(xa[u][s]), pack8(w), p, 0, 0, 0);
+      }
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc[i] = fmaf(p[i], sc[u], acc[i]);
+    }
   }
-  const int r = blockIdx.y * 128 + wave * 32 + (lane & 31);
-  const uint8_t* brow[1] = {r < nrows ? reinterpret_cast<const uint8_t*>(a.router_q) + (size_t)r * a.H : nullptr};
-  const uint16_t* bsc[1] = {a.router_s + (size_t)(r < nrows ? r : 0) * (a.H / kGroup)};
-  f16v acc[1] = {};
-  tile_gemm<8, 1>(lds, arows, a.H, brow, bsc, acc);
-  if (r < nrows) {
+#pragma unroll
+  for (int i = 0; i < 16; ++i) red[wave][i][lane] = acc[i];
+  __syncthreads();
+  if (wave == 0 && r < nrows) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-      const int t = t0 + acc_row(i);
-      if (t < a.T) a.logits[(size_t)t * nrows + r] = acc[0][i];
+      const int tt = blockIdx.x * 32 + acc_row(i);
+      const float v = (red[0][i][lane] + red[1][i][lane]) + (red[2][i][lane] + red[3][i][lane]);
+      if (tt < a.T) a.logits[(size_t)tt * nrows + r] = v;
     }
   }
 }
 
 // ---------------------------------------------------------------------------
-// 2. top-k per token (one wave per token)
+// 2. top-k: one workgroup per token
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void topk_kernel(ChunkArgs a) {
-  __shared__ int s_ids[4][kMaxTopK];
-  __shared__ float s_w[4][kMaxTopK];
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int t = blockIdx.x * 4 + wave;
-  if (t >= a.T) return;
+  __shared__ float lg[kMaxExperts + 1];
+  __shared__ TopkScratch sc;
+  __shared__ int ids[kMaxTopK];
+  __shared__ float w[kMaxTopK];
+  const int t = blockIdx.x;
   const int nrows = a.E + 1;
-  wave_topk(a.logits + (size_t)t * nrows, a.E, a.k, s_ids[wave], s_w[wave]);
-  if (lane < a.k) {
-    a.ids[(size_t)t * a.k + lane] = s_ids[wave][lane];
-    a.wts[(size_t)t * a.k + lane] = s_w[wave][lane];
+  for (int e = threadIdx.x; e < nrows; e += blockDim.x) lg[e] = a.logits[(size_t)t * nrows + e];
+  __syncthreads();
+  block_topk(lg, a.E, a.k, ids, w, sc);
+  __syncthreads();
+  if ((int)threadIdx.x < a.k) {
+    a.ids[(size_t)t * a.k + threadIdx.x] = ids[threadIdx.x];
+    a.wts[(size_t)t * a.k + threadIdx.x] = w[threadIdx.x];
   }
-  if (lane == 0) a.sigma[t] = sigmoid_f(a.logits[(size_t)t * nrows + a.E]);
+  if (threadIdx.x == 0) a.sigma[t] = sigmoid_f(lg[a.E]);
 }
 
 // ---------------------------------------------------------------------------
@@ -178,7 +130,9 @@ __global__ __launch_bounds__(256) void topk_kernel(ChunkArgs a) {
 //
 // Pairs p = t*k + i are ordered by (expert, p): a stable counting sort.  Each
 // wave owns a contiguous run of pairs; ranks inside a 64-pair batch come from
-// ballots over the 8 bits of the expert id.
+// ballots over the 8 bits of the expert id.  Each expert's rows are cut into
+// 64-row tiles and one last tile of 1..64 rows (the 32-row kind when it has
+// at most 32).
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ uint64_t peers_of(int e) {
   uint64_t peers = ~0ull;
@@ -189,6 +143,10 @@ __device__ __forceinline__ uint64_t peers_of(int e) {
   }
   return peers;
 }
+
+__device__ __forceinline__ int tiles_for(int c) { return (c + kTileRows - 1) / kTileRows; }
+
+__device__ __forceinline__ int4 make_tile(int e, int r0, int rows) { return make_int4(e, r0, rows, rows > 32 ? 2 : 1); }
 
 __global__ __launch_bounds__(1024) void bucket_kernel(ChunkArgs a) {
   __shared__ int hist[16][kMaxExperts + 1];  // per-wave counts, then per-wave bases
@@ -213,17 +171,16 @@ __global__ __launch_bounds__(1024) void bucket_kernel(ChunkArgs a) {
     if (ok && (pe & lt) == 0) hist[wave][e] += __popcll(pe);  // one leader per expert
   }
   __syncthreads();
-  // exclusive scan over experts of the totals; per-wave bases
   if (threadIdx.x < kMaxExperts + 1) {
     const int e = threadIdx.x;
     int tot = 0;
     if (e < E)
       for (int w = 0; w < 16; ++w) { const int c = hist[w][e]; hist[w][e] = tot; tot += c; }
     s_off[e] = e < E ? tot : 0;  // counts for now
-    s_tiles[e] = e < E ? (tot + kBM - 1) / kBM : 0;
+    s_tiles[e] = e < E ? tiles_for(tot) : 0;
   }
   __syncthreads();
-  if (wave == 0) {  // scans of counts and tile counts (E <= 256: 4 per lane)
+  if (wave == 0) {  // exclusive scans of counts and tile counts (E <= 256: 4 per lane)
     int c[4], tl[4];
     int sc = 0, st = 0;
 #pragma unroll
@@ -248,20 +205,18 @@ __global__ __launch_bounds__(1024) void bucket_kernel(ChunkArgs a) {
       et += tl[j];
     }
     if (lane == 63) {
-      s_total = ic;  // valid pairs
-      a.offsets[E] = ic;
+      s_total = ic;
       *a.n_tiles = it;
     }
   }
   __syncthreads();
-  for (int e = threadIdx.x; e < E; e += blockDim.x) a.offsets[e] = s_off[e];
   {
     const int total = s_total;
     for (int e = threadIdx.x; e < E; e += blockDim.x) {
       const int start = s_off[e];
       const int end = (e + 1 < E) ? s_off[e + 1] : total;
       int ti = s_tiles[e];
-      for (int r = start; r < end; r += kBM, ++ti) a.tiles[ti] = make_int4(e, r, min(kBM, end - r), 0);
+      for (int r = start; r < end; r += kTileRows, ++ti) a.tiles[ti] = make_tile(e, r, min(kTileRows, end - r));
     }
   }
   // stable scatter: position of pair p in expert-major order
@@ -282,75 +237,216 @@ __global__ __launch_bounds__(1024) void bucket_kernel(ChunkArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// 4. gate/up GEMM with SwiGLU epilogue.  blockIdx.x: tile (routed tiles, then
-// shared-expert tiles); blockIdx.y: block of 128 intermediate columns.
+// Grouped-GEMM tile core: acc[mt][f] += A[32*MT][K] . W_f[32][K]^T.
+//
+// A (activation rows) goes through LDS in stages of kKS = 128 (two 64-groups),
+// double-buffered: the next stage's rows are loaded into registers while the
+// current one is multiplied.  Each wave streams its own weight rows straight
+// into registers one stage ahead.  The binary16 scale of each 64-group is
+// folded into the weight conversion (code * scale rounded to binary16).
 // ---------------------------------------------------------------------------
-template <int BITS>
-__device__ __forceinline__ void up_tile(const ChunkArgs& a, _Float16* lds, const _Float16* const* arows,
-                                        const uint8_t* wq, const uint16_t* ws, int inter, int jb,
-                                        _Float16* hout, const int* hrow, int cnt) {
+static constexpr int kKS = 128;
+static constexpr int kAStride = kKS + 8;  // halves per LDS row (padding against bank conflicts)
+
+template <int MT>
+struct AStage {
+  static constexpr int CH = kKS / 8;            // 16-byte chunks per row per stage
+  static constexpr int N = 32 * MT * CH / 256;  // chunks per thread
+  uint4 v[N];
+  __device__ __forceinline__ void load(const _Float16* const* rows, int kb, int K) {
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+      const int idx = (int)threadIdx.x + 256 * i;
+      const int m = idx / CH, c = idx % CH;
+      const int k = kb + 8 * c;
+      v[i] = (rows[m] != nullptr && k < K) ? *reinterpret_cast<const uint4*>(rows[m] + k) : make_uint4(0, 0, 0, 0);
+    }
+  }
+  __device__ __forceinline__ void store(_Float16* lds) const {
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+      const int idx = (int)threadIdx.x + 256 * i;
+      const int m = idx / CH, c = idx % CH;
+      *reinterpret_cast<h8*>(lds + m * kAStride + 8 * c) = act_operand(v[i]);
+    }
+  }
+};
+
+template <int BITS, int NF>
+struct BStage {
+  static constexpr int Q = BITS == 4 ? 1 : 2;  // 16-byte loads per lane per group
+  uint4 q[2][NF][Q];
+  uint32_t s[2][NF];  // (scale, scale) as a binary16 pair
+  __device__ __forceinline__ void load(const uint8_t* const brow[NF], const uint16_t* const bsc[NF], int kb, int K) {
+    const int g = (threadIdx.x & 63) >> 5;
+#pragma unroll
+    for (int gi = 0; gi < 2; ++gi) {
+      const int kg = kb + kGroup * gi;
+#pragma unroll
+      for (int f = 0; f < NF; ++f) {
+        const bool ok = brow[f] != nullptr && kg < K;
+        const uint8_t* p = ok ? brow[f] + (size_t)(kg + 32 * g) * BITS / 8 : nullptr;
+#pragma unroll
+        for (int j = 0; j < Q; ++j) q[gi][f][j] = ok ? reinterpret_cast<const uint4*>(p)[j] : make_uint4(0, 0, 0, 0);
+        const uint32_t sb = ok ? bsc[f][kg / kGroup] : 0u;
+        s[gi][f] = sb | (sb << 16);
+      }
+    }
+  }
+  // MFMA operand for step st of group gi, fragment f, scale applied
+  __device__ __forceinline__ h8 operand(int gi, int f, int st) const {
+    h2 w[4];
+    if (BITS == 4) {
+      const uint32_t ws[4] = {q[gi][f][0].x, q[gi][f][0].y, q[gi][f][0].z, q[gi][f][0].w};
+      int4x8_to_h2x4(ws[st], w);
+    } else {
+      const uint32_t ws[8] = {q[gi][f][0].x, q[gi][f][0].y, q[gi][f][0].z, q[gi][f][0].w,
+                              q[gi][f][1].x, q[gi][f][1].y, q[gi][f][1].z, q[gi][f][1].w};
+      int8x8_to_h2x4(ws[2 * st], ws[2 * st + 1], w);
+    }
+    const h2 sc = as_h2(s[gi][f]);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) w[i] *= sc;
+    return pack8(w);
+  }
+};
+
+template <int BITS, int NF, int MT>
+__device__ __forceinline__ void tile_gemm(_Float16* lds, const _Float16* const* arows, int K,
+                                          const uint8_t* const brow[NF], const uint16_t* const bsc[NF],
+                                          f16v acc[MT][NF]) {
+  const int lane = threadIdx.x & 63;
+  const int m = lane & 31, g = lane >> 5;
+  constexpr int BUF = 32 * MT * kAStride;
+  const int nst = (K + kKS - 1) / kKS;
+  AStage<MT> as;
+  BStage<BITS, NF> bcur, bnxt;
+  as.load(arows, 0, K);
+  bcur.load(brow, bsc, 0, K);
+  as.store(lds);
+  __syncthreads();
+  for (int st = 0; st < nst; ++st) {
+    const int kb = st * kKS;
+    const bool more = st + 1 < nst;
+    if (more) {
+      as.load(arows, kb + kKS, K);
+      bnxt.load(brow, bsc, kb + kKS, K);
+    }
+    const _Float16* L = lds + (st & 1) * BUF;
+#pragma unroll
+    for (int gi = 0; gi < 2; ++gi) {
+      if (kb + kGroup * gi < K) {
+        h8 av[MT][4];
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+          for (int s = 0; s < 4; ++s)
+            av[mt][s] = *reinterpret_cast<const h8*>(L + (32 * mt + m) * kAStride + kGroup * gi + 32 * g + 8 * s);
+#pragma unroll
+        for (int f = 0; f < NF; ++f)
+#pragma unroll
+          for (int s = 0; s < 4; ++s) {
+            const h8 bv = bcur.operand(gi, f, s);
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt)
+              acc[mt][f] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av[mt][s], bv, acc[mt][f], 0, 0, 0);
+          }
+      }
+    }
+    if (more) {
+      as.store(lds + ((st + 1) & 1) * BUF);
+      bcur = bnxt;
+    }
+    __syncthreads();
+  }
+}
+
+// LDS of one GEMM workgroup: two A buffers of 64 rows
+static constexpr int kGemmLds = 2 * 64 * kAStride;
+
+struct TileRows {
+  const _Float16* a[64];  // A row pointers (null: zero row)
+  int out_row[64];        // destination row
+  float scale[64];        // epilogue scale (routing weight or sigma)
+};
+
+// ---------------------------------------------------------------------------
+// 4. gate/up GEMM with SwiGLU epilogue.  blockIdx.x: tile (routed tiles, then
+//    shared-expert tiles); blockIdx.y: block of 128 intermediate columns.
+// ---------------------------------------------------------------------------
+template <int BITS, int MT>
+__device__ __forceinline__ void up_tile(const ChunkArgs& a, _Float16* lds, const TileRows& tr, const uint8_t* wq,
+                                        const uint16_t* wsc, int inter, int jb, _Float16* hout, int rows) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int j = jb * 128 + wave * 32 + (lane & 31);
   const size_t rb = (size_t)a.H * BITS / 8;
   const size_t ng = a.H / kGroup;
   const bool ok = j < inter;
   const uint8_t* brow[2] = {ok ? wq + (size_t)j * rb : nullptr, ok ? wq + (size_t)(inter + j) * rb : nullptr};
-  const uint16_t* bsc[2] = {ws + (size_t)(ok ? j : 0) * ng, ws + (size_t)(ok ? inter + j : 0) * ng};
-  f16v acc[2] = {};
-  tile_gemm<BITS, 2>(lds, arows, a.H, brow, bsc, acc);
+  const uint16_t* bsc[2] = {wsc + (size_t)(ok ? j : 0) * ng, wsc + (size_t)(ok ? inter + j : 0) * ng};
+  f16v acc[MT][2];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) acc[mt][0] = acc[mt][1] = f16v{};
+  tile_gemm<BITS, 2, MT>(lds, tr.a, a.H, brow, bsc, acc);
   if (!ok) return;
 #pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    const int m = acc_row(i);
-    if (m < cnt) hout[(size_t)hrow[m] * inter + j] = (_Float16)(silu_f(acc[0][i]) * acc[1][i]);
-  }
+  for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int r = 32 * mt + acc_row(i);
+      if (r < rows) hout[(size_t)tr.out_row[r] * inter + j] = (_Float16)(silu_f(acc[mt][0][i]) * acc[mt][1][i]);
+    }
 }
 
 __global__ __launch_bounds__(256) void up_gemm_kernel(ChunkArgs a) {
-  __shared__ __attribute__((aligned(16))) _Float16 lds[kBM * kLdsStride];
-  __shared__ const _Float16* arows[kBM];
-  __shared__ int hrow[kBM];
+  __shared__ __attribute__((aligned(16))) _Float16 lds[kGemmLds];
+  __shared__ TileRows tr;
   const int n_routed = a.route_tiles ? *a.n_tiles : 0;
-  const int n_shared = a.shared_tiles;
   const int tile = blockIdx.x;
-  if (tile >= n_routed + n_shared) return;
+  if (tile >= n_routed + a.shared_tiles) return;
   const _Float16* xh = reinterpret_cast<const _Float16*>(a.x);
+  int e = -1, r0, rows, mt;
   if (tile < n_routed) {
     const int4 td = a.tiles[tile];
-    const int e = td.x, r0 = td.y, cnt = td.z;
+    e = td.x; r0 = td.y; rows = td.z; mt = td.w;
     if ((int)blockIdx.y * 128 >= a.I) return;
-    if (threadIdx.x < kBM) {
-      const int m = threadIdx.x;
-      const int p = m < cnt ? a.sorted_pair[r0 + m] : -1;
-      arows[m] = p >= 0 ? xh + (size_t)(p / a.k) * a.H : nullptr;
-      hrow[m] = r0 + m;
-    }
-    __syncthreads();
-    up_tile<4>(a, lds, arows, a.w13_q + (size_t)e * 2 * a.I * (a.H / 2), a.w13_s + (size_t)e * 2 * a.I * (a.H / kGroup),
-               a.I, blockIdx.y, a.h, hrow, cnt);
   } else {
-    const int t0 = (tile - n_routed) * kBM;
-    const int cnt = min(kBM, a.T - t0);
+    r0 = (tile - n_routed) * kTileRows;
+    rows = min(kTileRows, a.T - r0);
+    mt = rows > 32 ? 2 : 1;
     if ((int)blockIdx.y * 128 >= a.Is) return;
-    if (threadIdx.x < kBM) {
-      const int m = threadIdx.x;
-      arows[m] = m < cnt ? xh + (size_t)(t0 + m) * a.H : nullptr;
-      hrow[m] = t0 + m;
+  }
+  if (threadIdx.x < 64) {
+    const int r = threadIdx.x;
+    if (e >= 0) {
+      const int p = r < rows ? a.sorted_pair[r0 + r] : -1;
+      tr.a[r] = p >= 0 ? xh + (size_t)(p / a.k) * a.H : nullptr;
+    } else {
+      tr.a[r] = r < rows ? xh + (size_t)(r0 + r) * a.H : nullptr;
     }
-    __syncthreads();
-    up_tile<8>(a, lds, arows, reinterpret_cast<const uint8_t*>(a.sh13_q), a.sh13_s, a.Is, blockIdx.y, a.hs, hrow,
-               cnt);
+    tr.out_row[r] = r0 + r;
+  }
+  __syncthreads();
+  if (e >= 0) {
+    const uint8_t* wq = a.w13_q + (size_t)e * 2 * a.I * (a.H / 2);
+    const uint16_t* wsc = a.w13_s + (size_t)e * 2 * a.I * (a.H / kGroup);
+    if (mt == 2) up_tile<4, 2>(a, lds, tr, wq, wsc, a.I, blockIdx.y, a.h, rows);
+    else up_tile<4, 1>(a, lds, tr, wq, wsc, a.I, blockIdx.y, a.h, rows);
+  } else {
+    const uint8_t* wq = reinterpret_cast<const uint8_t*>(a.sh13_q);
+    if (mt == 2) up_tile<8, 2>(a, lds, tr, wq, a.sh13_s, a.Is, blockIdx.y, a.hs, rows);
+    else up_tile<8, 1>(a, lds, tr, wq, a.sh13_s, a.Is, blockIdx.y, a.hs, rows);
   }
 }
 
 // ---------------------------------------------------------------------------
 // 5. down GEMM: y[row][n] = w_row * (h_row . W_down[n]); shared tiles write
-// ys[t][n] = sigma_t * (h_s[t] . S_down[n]).  blockIdx.y: block of 256 outputs.
+//    ys[t][n] = sigma_t * (h_s[t] . S_down[n]).  blockIdx.y: block of 256
+//    outputs.
 // ---------------------------------------------------------------------------
-template <int BITS>
-__device__ __forceinline__ void down_tile(const ChunkArgs& a, _Float16* lds, const _Float16* const* arows,
-                                          const uint8_t* wq, const uint16_t* ws, int K, int nb, float* yout,
-                                          const int* yrow, const float* yscale, int cnt) {
+template <int BITS, int MT>
+__device__ __forceinline__ void down_tile(const ChunkArgs& a, _Float16* lds, const TileRows& tr, const uint8_t* wq,
+                                          const uint16_t* wsc, int K, int nb, _Float16* yout, int rows) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const size_t rb = (size_t)K * BITS / 8;
   const size_t ng = K / kGroup;
@@ -362,85 +458,102 @@ __device__ __forceinline__ void down_tile(const ChunkArgs& a, _Float16* lds, con
     n[f] = nb * 256 + wave * 64 + f * 32 + (lane & 31);
     const bool ok = n[f] < a.H;
     brow[f] = ok ? wq + (size_t)n[f] * rb : nullptr;
-    bsc[f] = ws + (size_t)(ok ? n[f] : 0) * ng;
+    bsc[f] = wsc + (size_t)(ok ? n[f] : 0) * ng;
   }
-  f16v acc[2] = {};
-  tile_gemm<BITS, 2>(lds, arows, K, brow, bsc, acc);
+  f16v acc[MT][2];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) acc[mt][0] = acc[mt][1] = f16v{};
+  tile_gemm<BITS, 2, MT>(lds, tr.a, K, brow, bsc, acc);
 #pragma unroll
   for (int f = 0; f < 2; ++f) {
     if (n[f] >= a.H) continue;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int m = acc_row(i);
-      if (m < cnt) yout[(size_t)yrow[m] * a.H + n[f]] = yscale[m] * acc[f][i];
-    }
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int r = 32 * mt + acc_row(i);
+        if (r < rows) yout[(size_t)tr.out_row[r] * a.H + n[f]] = (_Float16)(tr.scale[r] * acc[mt][f][i]);
+      }
   }
 }
 
 __global__ __launch_bounds__(256) void down_gemm_kernel(ChunkArgs a) {
-  __shared__ __attribute__((aligned(16))) _Float16 lds[kBM * kLdsStride];
-  __shared__ const _Float16* arows[kBM];
-  __shared__ int yrow[kBM];
-  __shared__ float yscale[kBM];
+  __shared__ __attribute__((aligned(16))) _Float16 lds[kGemmLds];
+  __shared__ TileRows tr;
   const int n_routed = a.route_tiles ? *a.n_tiles : 0;
-  const int n_shared = a.shared_tiles;
   const int tile = blockIdx.x;
-  if (tile >= n_routed + n_shared) return;
+  if (tile >= n_routed + a.shared_tiles) return;
   if ((int)blockIdx.y * 256 >= a.H) return;
+  int e = -1, r0, rows, mt;
   if (tile < n_routed) {
     const int4 td = a.tiles[tile];
-    const int e = td.x, r0 = td.y, cnt = td.z;
-    if (threadIdx.x < kBM) {
-      const int m = threadIdx.x;
-      const int p = m < cnt ? a.sorted_pair[r0 + m] : -1;
-      arows[m] = p >= 0 ? a.h + (size_t)(r0 + m) * a.I : nullptr;
-      yrow[m] = r0 + m;
-      yscale[m] = p >= 0 ? a.wts[p] : 0.f;
-    }
-    __syncthreads();
-    down_tile<4>(a, lds, arows, a.w2_q + (size_t)e * a.H * (a.I / 2), a.w2_s + (size_t)e * a.H * (a.I / kGroup), a.I,
-                 blockIdx.y, a.y, yrow, yscale, cnt);
+    e = td.x; r0 = td.y; rows = td.z; mt = td.w;
   } else {
-    const int t0 = (tile - n_routed) * kBM;
-    const int cnt = min(kBM, a.T - t0);
-    if (threadIdx.x < kBM) {
-      const int m = threadIdx.x;
-      arows[m] = m < cnt ? a.hs + (size_t)(t0 + m) * a.Is : nullptr;
-      yrow[m] = t0 + m;
-      yscale[m] = m < cnt ? a.sigma[t0 + m] : 0.f;
+    r0 = (tile - n_routed) * kTileRows;
+    rows = min(kTileRows, a.T - r0);
+    mt = rows > 32 ? 2 : 1;
+  }
+  if (threadIdx.x < 64) {
+    const int r = threadIdx.x;
+    if (e >= 0) {
+      const int p = r < rows ? a.sorted_pair[r0 + r] : -1;
+      tr.a[r] = p >= 0 ? a.h + (size_t)(r0 + r) * a.I : nullptr;
+      tr.scale[r] = p >= 0 ? a.wts[p] : 0.f;
+    } else {
+      tr.a[r] = r < rows ? a.hs + (size_t)(r0 + r) * a.Is : nullptr;
+      tr.scale[r] = r < rows ? a.sigma[r0 + r] : 0.f;
     }
-    __syncthreads();
-    down_tile<8>(a, lds, arows, reinterpret_cast<const uint8_t*>(a.sh2_q), a.sh2_s, a.Is, blockIdx.y, a.ys, yrow,
-                 yscale, cnt);
+    tr.out_row[r] = r0 + r;
+  }
+  __syncthreads();
+  if (e >= 0) {
+    const uint8_t* wq = a.w2_q + (size_t)e * a.H * (a.I / 2);
+    const uint16_t* wsc = a.w2_s + (size_t)e * a.H * (a.I / kGroup);
+    if (mt == 2) down_tile<4, 2>(a, lds, tr, wq, wsc, a.I, blockIdx.y, a.y, rows);
+    else down_tile<4, 1>(a, lds, tr, wq, wsc, a.I, blockIdx.y, a.y, rows);
+  } else {
+    const uint8_t* wq = reinterpret_cast<const uint8_t*>(a.sh2_q);
+    if (mt == 2) down_tile<8, 2>(a, lds, tr, wq, a.sh2_s, a.Is, blockIdx.y, a.ys, rows);
+    else down_tile<8, 1>(a, lds, tr, wq, a.sh2_s, a.Is, blockIdx.y, a.ys, rows);
   }
 }
 
 // ---------------------------------------------------------------------------
-// 6. combine: out[t][n] = sum_i y[pos(t,i)][n] (+ ys[t][n]); 4 outputs/thread
+// 6. combine: out[t][n] = sum_i y[pos(t,i)][n] (+ ys[t][n]); 8 outputs/thread
 // ---------------------------------------------------------------------------
+__device__ __forceinline__ void add8(float acc[8], uint4 v) {
+  const h8 h = __builtin_bit_cast(h8, v);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) acc[i] += (float)h[i];
+}
+
 __global__ __launch_bounds__(256) void combine_kernel(ChunkArgs a) {
   const int t = blockIdx.y;
-  const int n = (blockIdx.x * blockDim.x + threadIdx.x) * 4;
+  const int n = (blockIdx.x * blockDim.x + threadIdx.x) * 8;
   if (n >= a.H) return;
-  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-  if (a.ys) acc = *reinterpret_cast<const float4*>(a.ys + (size_t)t * a.H + n);
-  for (int i = 0; i < a.k; ++i) {
-    const int pos = a.pos_of_pair[(size_t)t * a.k + i];
-    if (pos < 0) continue;
-    const float4 v = *reinterpret_cast<const float4*>(a.y + (size_t)pos * a.H + n);
-    acc.x += v.x; acc.y += v.y; acc.z += v.z; acc.w += v.w;
-  }
-  const _Float16 o[4] = {(_Float16)acc.x, (_Float16)acc.y, (_Float16)acc.z, (_Float16)acc.w};
-  *reinterpret_cast<uint2*>(a.out + (size_t)t * a.H + n) = *reinterpret_cast<const uint2*>(o);
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  uint4 v[kMaxTopK];
+  int pos[kMaxTopK];
+#pragma unroll
+  for (int i = 0; i < kMaxTopK; ++i) pos[i] = i < a.k ? a.pos_of_pair[(size_t)t * a.k + i] : -1;
+#pragma unroll
+  for (int i = 0; i < kMaxTopK; ++i)
+    v[i] = pos[i] >= 0 ? *reinterpret_cast<const uint4*>(a.y + (size_t)pos[i] * a.H + n) : make_uint4(0, 0, 0, 0);
+  if (a.ys) add8(acc, *reinterpret_cast<const uint4*>(a.ys + (size_t)t * a.H + n));
+#pragma unroll
+  for (int i = 0; i < kMaxTopK; ++i) add8(acc, v[i]);
+  h8 o;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) o[i] = (_Float16)acc[i];
+  *reinterpret_cast<h8*>(a.out + (size_t)t * a.H + n) = o;
 }
 
 // ---------------------------------------------------------------------------
 // launchers
 // ---------------------------------------------------------------------------
 int launch_route_chunk(const ChunkArgs& a, hipStream_t s) {
-  dim3 g1((a.T + kBM - 1) / kBM, (a.E + 1 + 127) / 128);
-  hipLaunchKernelGGL(router_gemm_kernel, g1, dim3(256), 0, s, a);
-  hipLaunchKernelGGL(topk_kernel, dim3((a.T + 3) / 4), dim3(256), 0, s, a);
+  hipLaunchKernelGGL(router_gemm_kernel, dim3((a.T + 31) / 32, (a.E + 1 + 31) / 32), dim3(256), 0, s, a);
+  hipLaunchKernelGGL(topk_kernel, dim3(a.T), dim3(256), 0, s, a);
   return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_LAUNCH;
 }
 
@@ -450,7 +563,7 @@ int launch_experts_chunk(const ChunkArgs& a, hipStream_t s) {
   const int nbi = (max(a.I, a.shared_tiles ? a.Is : 0) + 127) / 128;
   hipLaunchKernelGGL(up_gemm_kernel, dim3(max_tiles, nbi), dim3(256), 0, s, a);
   hipLaunchKernelGGL(down_gemm_kernel, dim3(max_tiles, (a.H + 255) / 256), dim3(256), 0, s, a);
-  hipLaunchKernelGGL(combine_kernel, dim3((a.H / 4 + 255) / 256, a.T), dim3(256), 0, s, a);
+  hipLaunchKernelGGL(combine_kernel, dim3((a.H / 8 + 255) / 256, a.T), dim3(256), 0, s, a);
   return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_LAUNCH;
 }
 

@@ -4,6 +4,8 @@
 
 namespace moe {
 
+static constexpr int kTileRows = 64;  // rows of a grouped-GEMM tile (32-row kind for short tails)
+
 struct ChunkArgs {
   int H, E, k, I, Is, T;
   const int8_t* router_q; const uint16_t* router_s;
@@ -20,14 +22,14 @@ struct ChunkArgs {
   int32_t* offsets;    // [E+1]
   int32_t* sorted_pair;  // [T*k]  pair index at each expert-major position
   int32_t* pos_of_pair;  // [T*k]  expert-major position of each pair (-1: dropped)
-  int4* tiles;         // [max_route_tiles] (expert, first row, rows, 0)
+  int4* tiles;         // [max_route_tiles] (expert, first row, rows, 32-row subtiles)
   int32_t* n_tiles;    // routed tiles written by the bucketing kernel
   _Float16* h;         // [T*k][I]  expert-major rows
   _Float16* hs;        // [T][Is]
-  float* y;            // [T*k][H]  weighted expert outputs, expert-major rows
-  float* ys;           // [T][H]    sigma * shared output, or null (routed half only)
+  _Float16* y;         // [T*k][H]  weighted expert outputs, expert-major rows
+  _Float16* ys;        // [T][H]    sigma * shared output, or null (routed half only)
   int route_tiles;     // 1: routed tiles present
-  int shared_tiles;    // number of 32-token shared-expert tiles (0: routed half only)
+  int shared_tiles;    // number of 64-token shared-expert tiles (0: routed half only)
   int max_route_tiles; // bound on routed tiles for the grid
 };
 

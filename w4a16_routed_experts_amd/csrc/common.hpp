@@ -118,59 +118,117 @@ __device__ __forceinline__ float key_to_float(uint32_t k) {
   return __builtin_bit_cast(float, u);
 }
 
-// ---------------------------------------------------------------------------
-// Top-k of one token's router logits by one wave.
-//
-// Selection is by logit (softmax is monotone), descending, ties to the lower
-// expert index; the kept probabilities are renormalised, which equals a
-// softmax over the k kept logits.  Results are uniform across the wave.
-// ---------------------------------------------------------------------------
-__device__ __forceinline__ void wave_topk(const float* logits, int E, int k, int* ids, float* w) {
-  const int lane = threadIdx.x & 63;
-  uint32_t key[4];
-  for (int j = 0; j < 4; ++j) {
-    const int e = lane + 64 * j;
-    key[j] = (e < E) ? order_key(logits[e]) : 0u;
+// Sums within aligned groups of `width` lanes (power of two <= 64); every lane
+// of a group receives the group's sum.  Rows of 16 lanes reduce with DPP.
+template <int CTRL>
+__device__ __forceinline__ float dppf(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float row16_sum(float v) {
+  v += dppf<0xB1>(v);   // quad_perm(1,0,3,2)
+  v += dppf<0x4E>(v);   // quad_perm(2,3,0,1)
+  v += dppf<0x124>(v);  // row_ror 4
+  v += dppf<0x128>(v);  // row_ror 8
+  return v;
+}
+__device__ __forceinline__ float readlane_f(float v, int l) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), l));
+}
+__device__ __forceinline__ float lane_group_sum(float v, int width) {
+  if (width == 64) {
+    v = row16_sum(v);
+    return (readlane_f(v, 0) + readlane_f(v, 16)) + (readlane_f(v, 32) + readlane_f(v, 48));
   }
-  uint32_t removed = 0;  // bit j: element lane + 64 j already taken
-  float val[kMaxTopK];
-  for (int r = 0; r < k; ++r) {
-    uint32_t best = 0;
-    int bj = -1;
-    for (int j = 0; j < 4; ++j) {
-      const int e = lane + 64 * j;
-      if (e < E && !((removed >> j) & 1u) && (bj < 0 || key[j] > best)) { best = key[j]; bj = j; }
-    }
-    const uint32_t m = wave_max_u32(bj >= 0 ? best : 0u);
-    const uint64_t hit = __ballot(bj >= 0 && best == m);
-    int win;
-    if (__popcll(hit) == 1) {
-      const int wl = __ffsll((unsigned long long)hit) - 1;
-      const int wj = __shfl(bj, wl, 64);
-      win = wl + 64 * wj;
-    } else {
-      const uint32_t mine = (bj >= 0 && best == m) ? (uint32_t)(lane + 64 * bj) : 0xFFFFFFFFu;
-      win = (int)wave_min_u32(mine);
-    }
-    if (lane == (win & 63)) removed |= 1u << (win >> 6);
-    ids[r] = win;
-    val[r] = key_to_float(m);
+  if (width == 32) {
+    v = row16_sum(v);
+    return v + __shfl_xor(v, 16, 64);
   }
-  float s = 0.f;
-  for (int r = 0; r < k; ++r) { w[r] = expf(val[r] - val[0]); s += w[r]; }
-  const float inv = 1.0f / s;
-  for (int r = 0; r < k; ++r) w[r] *= inv;
+  if (width == 16) return row16_sum(v);
+  for (int m = 1; m < width; m <<= 1) v += __shfl_xor(v, m, 64);
+  return v;
 }
 
 // ---------------------------------------------------------------------------
-// Counters shared by the workgroups of one persistent launch.  Producers make
-// their stores visible at agent scope before counting; consumers acquire.
+// top-k
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ void signal_add(uint32_t* ctr, uint32_t v) {
-  __hip_atomic_fetch_add(ctr, v, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ uint32_t acquire_load(uint32_t* ctr) {
-  return __hip_atomic_load(ctr, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT);
+
+struct TopkScratch {
+  uint32_t gmax[8];
+  int count;
+  uint32_t ckey[kMaxExperts];
+  int cidx[kMaxExperts];
+  int sel_idx[kMaxTopK];
+  float sel_val[kMaxTopK];
+};
+
+// Top-k of one token's E router logits (LDS) by the whole workgroup.
+//
+// Selection is by logit (softmax is monotone), descending, ties to the lower
+// expert index; the kept probabilities are renormalised, which equals a
+// softmax over the k kept logits.  A lower bound tau of the k-th largest logit
+// is the smallest of k or more group maxima (groups of 32 experts); only the
+// experts at or above tau are ranked, each against the other candidates.
+__device__ inline void block_topk(const float* lg, int E, int k, int* ids_out, float* w_out, TopkScratch& sc) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const bool valid = tid < E;
+  const uint32_t key = valid ? order_key(lg[tid]) : 0u;
+  const bool grouped = E >= 32 * k;  // uniform
+  if (grouped) {
+    uint32_t m = key;
+    m = max(m, dpp_u32<0xB1>(m));
+    m = max(m, dpp_u32<0x4E>(m));
+    m = max(m, dpp_u32<0x124>(m));
+    m = max(m, dpp_u32<0x128>(m));
+    const uint32_t r0 = __builtin_amdgcn_readlane(m, 0), r1 = __builtin_amdgcn_readlane(m, 16);
+    const uint32_t r2 = __builtin_amdgcn_readlane(m, 32), r3 = __builtin_amdgcn_readlane(m, 48);
+    if (lane == 0) {
+      sc.gmax[2 * wave] = max(r0, r1);
+      sc.gmax[2 * wave + 1] = max(r2, r3);
+    }
+  }
+  if (tid == 0) sc.count = 0;
+  __syncthreads();
+  uint32_t tau = 0;
+  if (grouped) {
+    tau = 0xFFFFFFFFu;
+    const int ng = (E + 31) / 32;
+    for (int g = 0; g < ng; ++g) tau = min(tau, sc.gmax[g]);
+  }
+  if (valid && key >= tau) {
+    const int slot = atomicAdd(&sc.count, 1);
+    sc.ckey[slot] = key;
+    sc.cidx[slot] = tid;
+  }
+  __syncthreads();
+  const int C = sc.count;
+  if (tid < C) {
+    const uint32_t mk = sc.ckey[tid];
+    const int mi = sc.cidx[tid];
+    int r0 = 0, r1 = 0;
+    int c = 0;
+    for (; c + 1 < C; c += 2) {
+      const uint32_t k0 = sc.ckey[c], k1 = sc.ckey[c + 1];
+      const int i0 = sc.cidx[c], i1 = sc.cidx[c + 1];
+      r0 += (k0 > mk) || (k0 == mk && i0 < mi);
+      r1 += (k1 > mk) || (k1 == mk && i1 < mi);
+    }
+    if (c < C) r0 += (sc.ckey[c] > mk) || (sc.ckey[c] == mk && sc.cidx[c] < mi);
+    const int rank = r0 + r1;
+    if (rank < k) {
+      sc.sel_idx[rank] = mi;
+      sc.sel_val[rank] = lg[mi];
+    }
+  }
+  __syncthreads();
+  if (wave == 0) {
+    const float v0 = sc.sel_val[0];
+    const float e = lane < k ? expf(sc.sel_val[lane < k ? lane : 0] - v0) : 0.f;
+    const float s = row16_sum(e);  // k <= 8: lanes 0..k-1 sit in row 0
+    if (lane < k) {
+      ids_out[lane] = sc.sel_idx[lane];
+      w_out[lane] = e / s;
+    }
+  }
 }
 
 }  // namespace moe
