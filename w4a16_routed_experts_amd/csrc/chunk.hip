@@ -244,22 +244,47 @@ __global__ __launch_bounds__(1024) void bucket_kernel(ChunkArgs a) {
 // current one is multiplied.  Each wave streams its own weight rows straight
 // into registers one stage ahead.  The binary16 scale of each 64-group is
 // folded into the weight conversion (code * scale rounded to binary16).
+//
+// All global reads are buffer loads through range-checked resources: a masked
+// row or column gets an offset outside the resource and reads zeros, so no
+// load sits under a branch or feeds a select (either would make the compiler
+// wait for the load where it is issued instead of where it is used).
 // ---------------------------------------------------------------------------
 static constexpr int kKS = 128;
-static constexpr int kAStride = kKS + 8;  // halves per LDS row (padding against bank conflicts)
+static constexpr int kAStride = kKS + 8;       // halves per LDS row (padding against bank conflicts)
+static constexpr uint32_t kOob = 0x80000000u;  // an offset outside every resource: reads return zero
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// raw (stride 0) resource; the config word selects 32-bit data format (gfx9).
+// Base and size must be workgroup-uniform: they are moved to scalar registers
+// here, so the compiler never wraps a load in a per-lane resource loop.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  const uint64_t b = reinterpret_cast<uint64_t>(base);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)b), hi = __builtin_amdgcn_readfirstlane((uint32_t)(b >> 32));
+  void* ub = reinterpret_cast<void*>(((uint64_t)hi << 32) | lo);
+  return __builtin_amdgcn_make_buffer_rsrc(ub, (short)0, (int)__builtin_amdgcn_readfirstlane(bytes), 0x00020000);
+}
+
+// the same for a buffer-load result
+__device__ __forceinline__ h8 act_operand(u32x4 v) {
+  const uint32_t x[4] = {v.x, v.y, v.z, v.w};
+  uint32_t o[4];
+  perm8_words(x, o);
+  return __builtin_bit_cast(h8, make_uint4(o[0], o[1], o[2], o[3]));
+}
 
 template <int MT>
 struct AStage {
   static constexpr int CH = kKS / 8;            // 16-byte chunks per row per stage
   static constexpr int N = 32 * MT * CH / 256;  // chunks per thread
-  uint4 v[N];
-  __device__ __forceinline__ void load(const _Float16* const* rows, int kb, int K) {
+  u32x4 v[N];
+  // kbyte: byte offset of the stage in a row (kOob past the last stage)
+  __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t res, const uint32_t off[N], uint32_t kbyte) {
 #pragma unroll
     for (int i = 0; i < N; ++i) {
-      const int idx = (int)threadIdx.x + 256 * i;
-      const int m = idx / CH, c = idx % CH;
-      const int k = kb + 8 * c;
-      v[i] = (rows[m] != nullptr && k < K) ? *reinterpret_cast<const uint4*>(rows[m] + k) : make_uint4(0, 0, 0, 0);
+      const int c = ((int)threadIdx.x + 256 * i) % CH;
+      v[i] = __builtin_amdgcn_raw_buffer_load_b128(res, off[i] + kbyte + 16u * c, 0, 0);
     }
   }
   __device__ __forceinline__ void store(_Float16* lds) const {
@@ -275,89 +300,115 @@ struct AStage {
 template <int BITS, int NF>
 struct BStage {
   static constexpr int Q = BITS == 4 ? 1 : 2;  // 16-byte loads per lane per group
-  uint4 q[2][NF][Q];
-  uint32_t s[2][NF];  // (scale, scale) as a binary16 pair
-  __device__ __forceinline__ void load(const uint8_t* const brow[NF], const uint16_t* const bsc[NF], int kb, int K) {
-    const int g = (threadIdx.x & 63) >> 5;
+  u32x4 q[2][NF][Q];
+  uint16_t s[2][NF];  // raw binary16 scales of the stage's two groups
+  // qoff: byte offset of the lane's K slice in its weight row; soff: byte
+  // offset of the row's scales (kOob for a masked row).  kb: first K of the
+  // stage; live = false turns every load into an out-of-range one.
+  __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t rq, __amdgpu_buffer_rsrc_t rs, const uint32_t qoff[NF],
+                                       const uint32_t soff[NF], int kb, bool live) {
+    const uint32_t qk = live ? (uint32_t)kb * BITS / 8 : kOob;
+    const uint32_t sk = live ? 2u * (kb / kGroup) : kOob;
 #pragma unroll
-    for (int gi = 0; gi < 2; ++gi) {
-      const int kg = kb + kGroup * gi;
+    for (int gi = 0; gi < 2; ++gi)
 #pragma unroll
       for (int f = 0; f < NF; ++f) {
-        const bool ok = brow[f] != nullptr && kg < K;
-        const uint8_t* p = ok ? brow[f] + (size_t)(kg + 32 * g) * BITS / 8 : nullptr;
 #pragma unroll
-        for (int j = 0; j < Q; ++j) q[gi][f][j] = ok ? reinterpret_cast<const uint4*>(p)[j] : make_uint4(0, 0, 0, 0);
-        const uint32_t sb = ok ? bsc[f][kg / kGroup] : 0u;
-        s[gi][f] = sb | (sb << 16);
+        for (int j = 0; j < Q; ++j)
+          q[gi][f][j] = __builtin_amdgcn_raw_buffer_load_b128(rq, qoff[f] + qk + (uint32_t)(kGroup * gi * BITS / 8 + 16 * j), 0, 0);
+        s[gi][f] = __builtin_amdgcn_raw_buffer_load_b16(rs, soff[f] + sk + 2u * gi, 0, 0);
       }
-    }
   }
   // MFMA operand for step st of group gi, fragment f, scale applied
   __device__ __forceinline__ h8 operand(int gi, int f, int st) const {
     h2 w[4];
     if (BITS == 4) {
-      const uint32_t ws[4] = {q[gi][f][0].x, q[gi][f][0].y, q[gi][f][0].z, q[gi][f][0].w};
-      int4x8_to_h2x4(ws[st], w);
+      int4x8_to_h2x4(q[gi][f][0][st], w);
     } else {
-      const uint32_t ws[8] = {q[gi][f][0].x, q[gi][f][0].y, q[gi][f][0].z, q[gi][f][0].w,
-                              q[gi][f][1].x, q[gi][f][1].y, q[gi][f][1].z, q[gi][f][1].w};
-      int8x8_to_h2x4(ws[2 * st], ws[2 * st + 1], w);
+      int8x8_to_h2x4(q[gi][f][st >> 1][2 * (st & 1)], q[gi][f][st >> 1][2 * (st & 1) + 1], w);
     }
-    const h2 sc = as_h2(s[gi][f]);
+    const uint32_t sb = s[gi][f];
+    const h2 sc = as_h2(sb | (sb << 16));
 #pragma unroll
     for (int i = 0; i < 4; ++i) w[i] *= sc;
     return pack8(w);
   }
 };
 
+// Operands of one tile: A rows through `ra` at byte offsets aoff (one per
+// 16-byte chunk this thread stages), weight fragments through rq/rs.
 template <int BITS, int NF, int MT>
-__device__ __forceinline__ void tile_gemm(_Float16* lds, const _Float16* const* arows, int K,
-                                          const uint8_t* const brow[NF], const uint16_t* const bsc[NF],
-                                          f16v acc[MT][NF]) {
+struct GemmOperands {
+  __amdgpu_buffer_rsrc_t ra, rq, rs;
+  uint32_t aoff[AStage<MT>::N];
+  uint32_t qoff[NF], soff[NF];
+};
+
+template <int BITS, int NF, int MT>
+__device__ __forceinline__ void stage_mfma(const _Float16* L, const BStage<BITS, NF>& b, int kb, int K,
+                                           f16v acc[MT][NF]) {
   const int lane = threadIdx.x & 63;
   const int m = lane & 31, g = lane >> 5;
+#pragma unroll
+  for (int gi = 0; gi < 2; ++gi) {
+    if (kb + kGroup * gi < K) {
+      h8 av[MT][4];
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int s = 0; s < 4; ++s)
+          av[mt][s] = *reinterpret_cast<const h8*>(L + (32 * mt + m) * kAStride + kGroup * gi + 32 * g + 8 * s);
+#pragma unroll
+      for (int f = 0; f < NF; ++f)
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+          const h8 bv = b.operand(gi, f, s);
+#pragma unroll
+          for (int mt = 0; mt < MT; ++mt)
+            acc[mt][f] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av[mt][s], bv, acc[mt][f], 0, 0, 0);
+        }
+    }
+  }
+}
+
+template <int BITS, int NF, int MT>
+__device__ __forceinline__ void tile_gemm(_Float16* lds, const GemmOperands<BITS, NF, MT>& op, int K,
+                                          f16v acc[MT][NF]) {
   constexpr int BUF = 32 * MT * kAStride;
   const int nst = (K + kKS - 1) / kKS;
   AStage<MT> as;
-  BStage<BITS, NF> bcur, bnxt;
-  as.load(arows, 0, K);
-  bcur.load(brow, bsc, 0, K);
+  BStage<BITS, NF> b0, b1;
+  as.load(op.ra, op.aoff, 0);
+  b0.load(op.rq, op.rs, op.qoff, op.soff, 0, true);
   as.store(lds);
   __syncthreads();
-  for (int st = 0; st < nst; ++st) {
-    const int kb = st * kKS;
-    const bool more = st + 1 < nst;
-    if (more) {
-      as.load(arows, kb + kKS, K);
-      bnxt.load(brow, bsc, kb + kKS, K);
+  // Two stages per iteration, so the register stages swap roles without
+  // copies.  The next stage's loads are issued unconditionally (out of range
+  // past the last stage): loads issued on one path only would make the
+  // compiler drain the load queue where the paths join.
+  for (int st = 0; st < nst; st += 2) {
+    {
+      const int kb = st * kKS;
+      const bool more = st + 1 < nst;
+      as.load(op.ra, op.aoff, more ? 2u * (kb + kKS) : kOob);
+      b1.load(op.rq, op.rs, op.qoff, op.soff, kb + kKS, more);
+      // keep the next stage's loads ahead of this stage's arithmetic
+      __builtin_amdgcn_sched_barrier(0);
+      stage_mfma<BITS, NF, MT>(lds, b0, kb, K, acc);
+      as.store(lds + BUF);
+      __syncthreads();
+      if (!more) break;
     }
-    const _Float16* L = lds + (st & 1) * BUF;
-#pragma unroll
-    for (int gi = 0; gi < 2; ++gi) {
-      if (kb + kGroup * gi < K) {
-        h8 av[MT][4];
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-          for (int s = 0; s < 4; ++s)
-            av[mt][s] = *reinterpret_cast<const h8*>(L + (32 * mt + m) * kAStride + kGroup * gi + 32 * g + 8 * s);
-#pragma unroll
-        for (int f = 0; f < NF; ++f)
-#pragma unroll
-          for (int s = 0; s < 4; ++s) {
-            const h8 bv = bcur.operand(gi, f, s);
-#pragma unroll
-            for (int mt = 0; mt < MT; ++mt)
-              acc[mt][f] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av[mt][s], bv, acc[mt][f], 0, 0, 0);
-          }
-      }
+    {
+      const int kb = (st + 1) * kKS;
+      const bool more = st + 2 < nst;
+      as.load(op.ra, op.aoff, more ? 2u * (kb + kKS) : kOob);
+      b0.load(op.rq, op.rs, op.qoff, op.soff, kb + kKS, more);
+      __builtin_amdgcn_sched_barrier(0);
+      stage_mfma<BITS, NF, MT>(lds + BUF, b1, kb, K, acc);
+      as.store(lds);
+      __syncthreads();
     }
-    if (more) {
-      as.store(lds + ((st + 1) & 1) * BUF);
-      bcur = bnxt;
-    }
-    __syncthreads();
   }
 }
 
@@ -365,29 +416,57 @@ __device__ __forceinline__ void tile_gemm(_Float16* lds, const _Float16* const* 
 static constexpr int kGemmLds = 2 * 64 * kAStride;
 
 struct TileRows {
-  const _Float16* a[64];  // A row pointers (null: zero row)
-  int out_row[64];        // destination row
-  float scale[64];        // epilogue scale (routing weight or sigma)
+  uint32_t aoff[64];  // byte offset of each A row in its resource (kOob: zero row)
+  int out_row[64];    // destination row
+  float scale[64];    // epilogue scale (routing weight or sigma)
 };
 
+template <int BITS, int NF, int MT>
+__device__ __forceinline__ void set_a_offsets(GemmOperands<BITS, NF, MT>& op, const TileRows& tr) {
+#pragma unroll
+  for (int i = 0; i < AStage<MT>::N; ++i) op.aoff[i] = tr.aoff[((int)threadIdx.x + 256 * i) / AStage<MT>::CH];
+}
+
 // ---------------------------------------------------------------------------
-// 4. gate/up GEMM with SwiGLU epilogue.  blockIdx.x: tile (routed tiles, then
-//    shared-expert tiles); blockIdx.y: block of 128 intermediate columns.
+// XCD-aware work order.  The dispatcher hands block b to XCD b % 8 in order of
+// b; item w = (b % 8) * ceil(n/8) + b / 8 gives each XCD a contiguous run of
+// the item list, so the tiles that share one expert's weight slice (adjacent
+// items) run together on one L2.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ int xcd_item(int n_items) {
+  const int b = blockIdx.x;
+  const int per = (n_items + 7) / 8;
+  const int w = (b & 7) * per + (b >> 3);
+  return ((b >> 3) < per && w < n_items) ? w : -1;
+}
+
+// ---------------------------------------------------------------------------
+// 4. gate/up GEMM with SwiGLU epilogue.  Items: (column block of 128, tile),
+//    column-block major; routed tiles first, then shared-expert tiles.
 // ---------------------------------------------------------------------------
 template <int BITS, int MT>
-__device__ __forceinline__ void up_tile(const ChunkArgs& a, _Float16* lds, const TileRows& tr, const uint8_t* wq,
-                                        const uint16_t* wsc, int inter, int jb, _Float16* hout, int rows) {
+__device__ __forceinline__ void up_tile(const ChunkArgs& a, _Float16* lds, const TileRows& tr,
+                                        __amdgpu_buffer_rsrc_t ra, const uint8_t* wq, const uint16_t* wsc, int inter,
+                                        int jb, _Float16* hout, int rows) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int j = jb * 128 + wave * 32 + (lane & 31);
-  const size_t rb = (size_t)a.H * BITS / 8;
-  const size_t ng = a.H / kGroup;
+  const uint32_t rb = (uint32_t)a.H * BITS / 8;
+  const uint32_t ng = a.H / kGroup;
   const bool ok = j < inter;
-  const uint8_t* brow[2] = {ok ? wq + (size_t)j * rb : nullptr, ok ? wq + (size_t)(inter + j) * rb : nullptr};
-  const uint16_t* bsc[2] = {wsc + (size_t)(ok ? j : 0) * ng, wsc + (size_t)(ok ? inter + j : 0) * ng};
+  GemmOperands<BITS, 2, MT> op;
+  op.ra = ra;
+  op.rq = make_rsrc(wq, 2u * inter * rb);
+  op.rs = make_rsrc(wsc, 2u * inter * ng * 2u);
+  const uint32_t kl = 32u * (lane >> 5) * BITS / 8;  // the lane's K slice inside a group
+  op.qoff[0] = ok ? (uint32_t)j * rb + kl : kOob;
+  op.qoff[1] = ok ? (uint32_t)(inter + j) * rb + kl : kOob;
+  op.soff[0] = ok ? (uint32_t)j * ng * 2u : kOob;
+  op.soff[1] = ok ? (uint32_t)(inter + j) * ng * 2u : kOob;
+  set_a_offsets(op, tr);
   f16v acc[MT][2];
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) acc[mt][0] = acc[mt][1] = f16v{};
-  tile_gemm<BITS, 2, MT>(lds, tr.a, a.H, brow, bsc, acc);
+  tile_gemm<BITS, 2, MT>(lds, op, a.H, acc);
   if (!ok) return;
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt)
@@ -398,72 +477,82 @@ __device__ __forceinline__ void up_tile(const ChunkArgs& a, _Float16* lds, const
     }
 }
 
-__global__ __launch_bounds__(256) void up_gemm_kernel(ChunkArgs a) {
+__global__ __launch_bounds__(256, 2) void up_gemm_kernel(ChunkArgs a) {
   __shared__ __attribute__((aligned(16))) _Float16 lds[kGemmLds];
   __shared__ TileRows tr;
   const int n_routed = a.route_tiles ? *a.n_tiles : 0;
-  const int tile = blockIdx.x;
-  if (tile >= n_routed + a.shared_tiles) return;
-  const _Float16* xh = reinterpret_cast<const _Float16*>(a.x);
-  int e = -1, r0, rows, mt;
-  if (tile < n_routed) {
-    const int4 td = a.tiles[tile];
+  const int nbi = (a.I + 127) / 128, nbs = (a.Is + 127) / 128;
+  const int n_items = n_routed * nbi + a.shared_tiles * nbs;
+  int w = xcd_item(n_items);
+  if (w < 0) return;
+  int e = -1, r0, rows, mt, jb;
+  if (w < n_routed * nbi) {
+    jb = w / n_routed;
+    const int4 td = a.tiles[w - jb * n_routed];
     e = td.x; r0 = td.y; rows = td.z; mt = td.w;
-    if ((int)blockIdx.y * 128 >= a.I) return;
   } else {
-    r0 = (tile - n_routed) * kTileRows;
+    w -= n_routed * nbi;
+    jb = w / a.shared_tiles;
+    r0 = (w - jb * a.shared_tiles) * kTileRows;
     rows = min(kTileRows, a.T - r0);
     mt = rows > 32 ? 2 : 1;
-    if ((int)blockIdx.y * 128 >= a.Is) return;
   }
   if (threadIdx.x < 64) {
     const int r = threadIdx.x;
+    int tok = -1;
     if (e >= 0) {
       const int p = r < rows ? a.sorted_pair[r0 + r] : -1;
-      tr.a[r] = p >= 0 ? xh + (size_t)(p / a.k) * a.H : nullptr;
-    } else {
-      tr.a[r] = r < rows ? xh + (size_t)(r0 + r) * a.H : nullptr;
+      tok = p >= 0 ? p / a.k : -1;
+    } else if (r < rows) {
+      tok = r0 + r;
     }
+    tr.aoff[r] = tok >= 0 ? (uint32_t)tok * a.H * 2u : kOob;
     tr.out_row[r] = r0 + r;
   }
   __syncthreads();
+  const __amdgpu_buffer_rsrc_t ra = make_rsrc(a.x, (uint32_t)a.T * a.H * 2u);
   if (e >= 0) {
     const uint8_t* wq = a.w13_q + (size_t)e * 2 * a.I * (a.H / 2);
     const uint16_t* wsc = a.w13_s + (size_t)e * 2 * a.I * (a.H / kGroup);
-    if (mt == 2) up_tile<4, 2>(a, lds, tr, wq, wsc, a.I, blockIdx.y, a.h, rows);
-    else up_tile<4, 1>(a, lds, tr, wq, wsc, a.I, blockIdx.y, a.h, rows);
+    if (mt == 2) up_tile<4, 2>(a, lds, tr, ra, wq, wsc, a.I, jb, a.h, rows);
+    else up_tile<4, 1>(a, lds, tr, ra, wq, wsc, a.I, jb, a.h, rows);
   } else {
     const uint8_t* wq = reinterpret_cast<const uint8_t*>(a.sh13_q);
-    if (mt == 2) up_tile<8, 2>(a, lds, tr, wq, a.sh13_s, a.Is, blockIdx.y, a.hs, rows);
-    else up_tile<8, 1>(a, lds, tr, wq, a.sh13_s, a.Is, blockIdx.y, a.hs, rows);
+    if (mt == 2) up_tile<8, 2>(a, lds, tr, ra, wq, a.sh13_s, a.Is, jb, a.hs, rows);
+    else up_tile<8, 1>(a, lds, tr, ra, wq, a.sh13_s, a.Is, jb, a.hs, rows);
   }
 }
 
 // ---------------------------------------------------------------------------
 // 5. down GEMM: y[row][n] = w_row * (h_row . W_down[n]); shared tiles write
-//    ys[t][n] = sigma_t * (h_s[t] . S_down[n]).  blockIdx.y: block of 256
-//    outputs.
+//    ys[t][n] = sigma_t * (h_s[t] . S_down[n]).  Items: (block of 256
+//    outputs, tile), output-block major.
 // ---------------------------------------------------------------------------
 template <int BITS, int MT>
-__device__ __forceinline__ void down_tile(const ChunkArgs& a, _Float16* lds, const TileRows& tr, const uint8_t* wq,
-                                          const uint16_t* wsc, int K, int nb, _Float16* yout, int rows) {
+__device__ __forceinline__ void down_tile(const ChunkArgs& a, _Float16* lds, const TileRows& tr,
+                                          __amdgpu_buffer_rsrc_t ra, const uint8_t* wq, const uint16_t* wsc, int K,
+                                          int nb, _Float16* yout, int rows) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const size_t rb = (size_t)K * BITS / 8;
-  const size_t ng = K / kGroup;
+  const uint32_t rb = (uint32_t)K * BITS / 8;
+  const uint32_t ng = K / kGroup;
+  GemmOperands<BITS, 2, MT> op;
+  op.ra = ra;
+  op.rq = make_rsrc(wq, (uint32_t)a.H * rb);
+  op.rs = make_rsrc(wsc, (uint32_t)a.H * ng * 2u);
+  const uint32_t kl = 32u * (lane >> 5) * BITS / 8;
   int n[2];
-  const uint8_t* brow[2];
-  const uint16_t* bsc[2];
 #pragma unroll
   for (int f = 0; f < 2; ++f) {
     n[f] = nb * 256 + wave * 64 + f * 32 + (lane & 31);
     const bool ok = n[f] < a.H;
-    brow[f] = ok ? wq + (size_t)n[f] * rb : nullptr;
-    bsc[f] = wsc + (size_t)(ok ? n[f] : 0) * ng;
+    op.qoff[f] = ok ? (uint32_t)n[f] * rb + kl : kOob;
+    op.soff[f] = ok ? (uint32_t)n[f] * ng * 2u : kOob;
   }
+  set_a_offsets(op, tr);
   f16v acc[MT][2];
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) acc[mt][0] = acc[mt][1] = f16v{};
-  tile_gemm<BITS, 2, MT>(lds, tr.a, K, brow, bsc, acc);
+  tile_gemm<BITS, 2, MT>(lds, op, K, acc);
 #pragma unroll
   for (int f = 0; f < 2; ++f) {
     if (n[f] >= a.H) continue;
@@ -477,13 +566,15 @@ __device__ __forceinline__ void down_tile(const ChunkArgs& a, _Float16* lds, con
   }
 }
 
-__global__ __launch_bounds__(256) void down_gemm_kernel(ChunkArgs a) {
+__global__ __launch_bounds__(256, 2) void down_gemm_kernel(ChunkArgs a) {
   __shared__ __attribute__((aligned(16))) _Float16 lds[kGemmLds];
   __shared__ TileRows tr;
   const int n_routed = a.route_tiles ? *a.n_tiles : 0;
-  const int tile = blockIdx.x;
-  if (tile >= n_routed + a.shared_tiles) return;
-  if ((int)blockIdx.y * 256 >= a.H) return;
+  const int nbh = (a.H + 255) / 256;
+  const int n_tiles = n_routed + a.shared_tiles;
+  int w = xcd_item(n_tiles * nbh);
+  if (w < 0) return;
+  const int nb = w / n_tiles, tile = w - nb * n_tiles;
   int e = -1, r0, rows, mt;
   if (tile < n_routed) {
     const int4 td = a.tiles[tile];
@@ -493,28 +584,34 @@ __global__ __launch_bounds__(256) void down_gemm_kernel(ChunkArgs a) {
     rows = min(kTileRows, a.T - r0);
     mt = rows > 32 ? 2 : 1;
   }
+  const int K = e >= 0 ? a.I : a.Is;
   if (threadIdx.x < 64) {
     const int r = threadIdx.x;
+    bool ok;
     if (e >= 0) {
       const int p = r < rows ? a.sorted_pair[r0 + r] : -1;
-      tr.a[r] = p >= 0 ? a.h + (size_t)(r0 + r) * a.I : nullptr;
-      tr.scale[r] = p >= 0 ? a.wts[p] : 0.f;
+      ok = p >= 0;
+      tr.scale[r] = ok ? a.wts[p] : 0.f;
     } else {
-      tr.a[r] = r < rows ? a.hs + (size_t)(r0 + r) * a.Is : nullptr;
-      tr.scale[r] = r < rows ? a.sigma[r0 + r] : 0.f;
+      ok = r < rows;
+      tr.scale[r] = ok ? a.sigma[r0 + r] : 0.f;
     }
+    tr.aoff[r] = ok ? (uint32_t)r * K * 2u : kOob;
     tr.out_row[r] = r0 + r;
   }
   __syncthreads();
+  // A: the tile's own rows of h (or h_s), which start at row r0
+  const _Float16* abase = (e >= 0 ? a.h : a.hs) + (size_t)r0 * K;
+  const __amdgpu_buffer_rsrc_t ra = make_rsrc(abase, (uint32_t)rows * K * 2u);
   if (e >= 0) {
     const uint8_t* wq = a.w2_q + (size_t)e * a.H * (a.I / 2);
     const uint16_t* wsc = a.w2_s + (size_t)e * a.H * (a.I / kGroup);
-    if (mt == 2) down_tile<4, 2>(a, lds, tr, wq, wsc, a.I, blockIdx.y, a.y, rows);
-    else down_tile<4, 1>(a, lds, tr, wq, wsc, a.I, blockIdx.y, a.y, rows);
+    if (mt == 2) down_tile<4, 2>(a, lds, tr, ra, wq, wsc, a.I, nb, a.y, rows);
+    else down_tile<4, 1>(a, lds, tr, ra, wq, wsc, a.I, nb, a.y, rows);
   } else {
     const uint8_t* wq = reinterpret_cast<const uint8_t*>(a.sh2_q);
-    if (mt == 2) down_tile<8, 2>(a, lds, tr, wq, a.sh2_s, a.Is, blockIdx.y, a.ys, rows);
-    else down_tile<8, 1>(a, lds, tr, wq, a.sh2_s, a.Is, blockIdx.y, a.ys, rows);
+    if (mt == 2) down_tile<8, 2>(a, lds, tr, ra, wq, a.sh2_s, a.Is, nb, a.ys, rows);
+    else down_tile<8, 1>(a, lds, tr, ra, wq, a.sh2_s, a.Is, nb, a.ys, rows);
   }
 }
 
@@ -559,10 +656,12 @@ int launch_route_chunk(const ChunkArgs& a, hipStream_t s) {
 
 int launch_experts_chunk(const ChunkArgs& a, hipStream_t s) {
   hipLaunchKernelGGL(bucket_kernel, dim3(1), dim3(1024), 0, s, a);
-  const int max_tiles = a.max_route_tiles + a.shared_tiles;
-  const int nbi = (max(a.I, a.shared_tiles ? a.Is : 0) + 127) / 128;
-  hipLaunchKernelGGL(up_gemm_kernel, dim3(max_tiles, nbi), dim3(256), 0, s, a);
-  hipLaunchKernelGGL(down_gemm_kernel, dim3(max_tiles, (a.H + 255) / 256), dim3(256), 0, s, a);
+  // 1-D grids over the item lists (rounded up to whole XCD rounds); blocks
+  // beyond the items the bucketing produced exit at once
+  const int up_items = a.max_route_tiles * ((a.I + 127) / 128) + a.shared_tiles * ((a.Is + 127) / 128);
+  const int down_items = (a.max_route_tiles + a.shared_tiles) * ((a.H + 255) / 256);
+  hipLaunchKernelGGL(up_gemm_kernel, dim3((up_items + 7) & ~7), dim3(256), 0, s, a);
+  hipLaunchKernelGGL(down_gemm_kernel, dim3((down_items + 7) & ~7), dim3(256), 0, s, a);
   hipLaunchKernelGGL(combine_kernel, dim3((a.H / 8 + 255) / 256, a.T), dim3(256), 0, s, a);
   return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_LAUNCH;
 }

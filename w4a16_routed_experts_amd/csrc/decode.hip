@@ -113,21 +113,23 @@ struct Frag {
   uint4 q[NB][MAXCPL];
   float s[NB][MAXCPL];
 
-  // rows[b]: this lane's row pointer in batch b (nullptr = masked); srow: its scales
+  // rows[b]: this lane's row pointer in batch b (nullptr = masked); srow: its
+  // scales (always a valid row).  Loads are unconditional: a masked lane reads
+  // `safe` (a valid row) and zeroes the value, because a load under a branch
+  // would be waited for inside the branch.
   __device__ __forceinline__ void load(const uint8_t* const rows[NB], const uint16_t* const srow[NB],
-                                       const RowGeom& g) {
+                                       const RowGeom& g, const uint8_t* safe) {
     const int lane = threadIdx.x & 63;
 #pragma unroll
     for (int b = 0; b < NB; ++b)
 #pragma unroll
       for (int m = 0; m < MAXCPL; ++m) {
-        q[b][m] = make_uint4(0, 0, 0, 0);
-        s[b][m] = 0.f;
-        if (rows[b] != nullptr && m < g.cpl) {
-          const int c = (lane % g.lpr) + g.lpr * m;
-          q[b][m] = *reinterpret_cast<const uint4*>(rows[b] + 16 * (size_t)c);
-          s[b][m] = half_bits_to_float(srow[b][chunk_group<BITS>(c)]);
-        }
+        const bool ok = rows[b] != nullptr && m < g.cpl;
+        const int c = (lane % g.lpr) + g.lpr * (m < g.cpl ? m : 0);
+        const uint4 t = *reinterpret_cast<const uint4*>((ok ? rows[b] : safe) + 16 * (size_t)c);
+        const float sc = half_bits_to_float(srow[b][chunk_group<BITS>(c)]);
+        q[b][m] = ok ? t : make_uint4(0, 0, 0, 0);
+        s[b][m] = ok ? sc : 0.f;
       }
   }
 
@@ -205,7 +207,7 @@ __device__ void router_item(const DecodeArgs& a, int H, int item, const _Float16
   const uint8_t* rows[1] = {row < nrows ? reinterpret_cast<const uint8_t*>(a.router_q) + (size_t)row * H : nullptr};
   const uint16_t* srow[1] = {a.router_s + (size_t)(row < nrows ? row : 0) * (H / kGroup)};
   Frag<8, 1, MAXCPL> f;
-  f.load(rows, srow, g);
+  f.load(rows, srow, g, reinterpret_cast<const uint8_t*>(a.router_q));
   float acc[1][kDecMaxT];
   f.template dot_shared<kDecMaxT>(g, xs, H, a.T, acc);
 #pragma unroll
@@ -236,7 +238,7 @@ __device__ void shup_item(const DecodeArgs& a, int H, int Is, int item, const _F
     srow[2 + h] = a.sh13_s + (size_t)(ok ? Is + j : 0) * (H / kGroup);
   }
   Frag<8, 4, MAXCPL> f;
-  f.load(rows, srow, g);
+  f.load(rows, srow, g, base);
   float acc[4][kDecMaxT];
   f.template dot_shared<kDecMaxT>(g, xs, H, a.T, acc);
 #pragma unroll
@@ -278,7 +280,7 @@ __device__ void up_item(const DecodeArgs& a, int H, int I, int item, const _Floa
     srow[4 + h] = sbase + (size_t)(ok ? I + j : 0) * ng;
   }
   Frag<4, 8, MAXCPL> f;
-  f.load(rows, srow, g);
+  f.load(rows, srow, g, wbase);
   float acc[8][1];
   f.template dot_shared<1>(g, xs + (size_t)t * H, H, 1, acc);
   float* dst = a.h_e + (size_t)item * a.p.he_stride;
@@ -307,7 +309,7 @@ __device__ void sd_item(const DecodeArgs& a, int H, int Is, int item, const _Flo
     srow[h] = a.sh2_s + (size_t)(n < H ? n : 0) * ng;
   }
   Frag<8, 4, MAXCPL> f;
-  f.load(rows, srow, g);
+  f.load(rows, srow, g, base);
   float acc[4][kDecMaxT];
   f.template dot_shared<kDecMaxT>(g, hs, Is, a.T, acc);
 #pragma unroll
@@ -445,7 +447,8 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
         srow[q] = a.w2_s + ((size_t)(e >= 0 ? e : 0) * H + n) * ng;
       }
       Frag<4, 2, CPL4I> f;
-      f.load(rows, srow, g);
+      f.load(rows, srow, g, a.w2_q);
+      __builtin_amdgcn_sched_barrier(0);  // issue these loads before waiting
       if (!h_ready) {
         wait_done(a.sync, SYNC_UP);
         if (MODE == DEC_FORWARD) wait_done(a.sync, SYNC_SD);
