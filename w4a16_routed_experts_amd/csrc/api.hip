@@ -321,7 +321,7 @@ MOE_API int moe_forward(const moe_dims* dims, const moe_weights* w, const uint16
   if (weights) a.wts = weights;
   if (shared_gate) a.sigma = shared_gate;
   a.route_tiles = 1;
-  a.shared_tiles = (T + kTileRows - 1) / kTileRows;
+  a.shared_tiles = (T + kSharedRows - 1) / kSharedRows;
   int r = launch_route_chunk(a, stream);
   if (r != MOE_OK) return r;
   return launch_experts_chunk(a, stream);

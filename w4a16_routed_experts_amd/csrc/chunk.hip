@@ -131,8 +131,8 @@ __global__ __launch_bounds__(256) void topk_kernel(ChunkArgs a) {
 // Pairs p = t*k + i are ordered by (expert, p): a stable counting sort.  Each
 // wave owns a contiguous run of pairs; ranks inside a 64-pair batch come from
 // ballots over the 8 bits of the expert id.  Each expert's rows are cut into
-// 64-row tiles and one last tile of 1..64 rows (the 32-row kind when it has
-// at most 32).
+// kTileRows-row tiles and one last tile of 1..kTileRows rows, which uses only
+// as many 32-row MFMA blocks as it needs.
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ uint64_t peers_of(int e) {
   uint64_t peers = ~0ull;
@@ -146,7 +146,7 @@ __device__ __forceinline__ uint64_t peers_of(int e) {
 
 __device__ __forceinline__ int tiles_for(int c) { return (c + kTileRows - 1) / kTileRows; }
 
-__device__ __forceinline__ int4 make_tile(int e, int r0, int rows) { return make_int4(e, r0, rows, rows > 32 ? 2 : 1); }
+__device__ __forceinline__ int4 make_tile(int e, int r0, int rows) { return make_int4(e, r0, rows, (rows + 31) / 32); }
 
 __global__ __launch_bounds__(1024) void bucket_kernel(ChunkArgs a) {
   __shared__ int hist[16][kMaxExperts + 1];  // per-wave counts, then per-wave bases
@@ -352,21 +352,20 @@ __device__ __forceinline__ void stage_mfma(const _Float16* L, const BStage<BITS,
 #pragma unroll
   for (int gi = 0; gi < 2; ++gi) {
     if (kb + kGroup * gi < K) {
-      h8 av[MT][4];
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt)
+      for (int s = 0; s < 4; ++s) {
+        h8 av[MT];
 #pragma unroll
-        for (int s = 0; s < 4; ++s)
-          av[mt][s] = *reinterpret_cast<const h8*>(L + (32 * mt + m) * kAStride + kGroup * gi + 32 * g + 8 * s);
+        for (int mt = 0; mt < MT; ++mt)
+          av[mt] = *reinterpret_cast<const h8*>(L + (32 * mt + m) * kAStride + kGroup * gi + 32 * g + 8 * s);
 #pragma unroll
-      for (int f = 0; f < NF; ++f)
-#pragma unroll
-        for (int s = 0; s < 4; ++s) {
+        for (int f = 0; f < NF; ++f) {
           const h8 bv = b.operand(gi, f, s);
 #pragma unroll
           for (int mt = 0; mt < MT; ++mt)
-            acc[mt][f] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av[mt][s], bv, acc[mt][f], 0, 0, 0);
+            acc[mt][f] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av[mt], bv, acc[mt][f], 0, 0, 0);
         }
+      }
     }
   }
 }
@@ -412,13 +411,13 @@ __device__ __forceinline__ void tile_gemm(_Float16* lds, const GemmOperands<BITS
   }
 }
 
-// LDS of one GEMM workgroup: two A buffers of 64 rows
-static constexpr int kGemmLds = 2 * 64 * kAStride;
+// LDS of one GEMM workgroup: two A buffers of kTileRows rows
+static constexpr int kGemmLds = 2 * kTileRows * kAStride;
 
 struct TileRows {
-  uint32_t aoff[64];  // byte offset of each A row in its resource (kOob: zero row)
-  int out_row[64];    // destination row
-  float scale[64];    // epilogue scale (routing weight or sigma)
+  uint32_t aoff[kTileRows];  // byte offset of each A row in its resource (kOob: zero row)
+  int out_row[kTileRows];    // destination row
+  float scale[kTileRows];    // epilogue scale (routing weight or sigma)
 };
 
 template <int BITS, int NF, int MT>
@@ -493,11 +492,11 @@ __global__ __launch_bounds__(256, 2) void up_gemm_kernel(ChunkArgs a) {
   } else {
     w -= n_routed * nbi;
     jb = w / a.shared_tiles;
-    r0 = (w - jb * a.shared_tiles) * kTileRows;
-    rows = min(kTileRows, a.T - r0);
-    mt = rows > 32 ? 2 : 1;
+    r0 = (w - jb * a.shared_tiles) * kSharedRows;
+    rows = min(kSharedRows, a.T - r0);
+    mt = (rows + 31) / 32;
   }
-  if (threadIdx.x < 64) {
+  if (threadIdx.x < kTileRows) {
     const int r = threadIdx.x;
     int tok = -1;
     if (e >= 0) {
@@ -514,8 +513,12 @@ __global__ __launch_bounds__(256, 2) void up_gemm_kernel(ChunkArgs a) {
   if (e >= 0) {
     const uint8_t* wq = a.w13_q + (size_t)e * 2 * a.I * (a.H / 2);
     const uint16_t* wsc = a.w13_s + (size_t)e * 2 * a.I * (a.H / kGroup);
-    if (mt == 2) up_tile<4, 2>(a, lds, tr, ra, wq, wsc, a.I, jb, a.h, rows);
-    else up_tile<4, 1>(a, lds, tr, ra, wq, wsc, a.I, jb, a.h, rows);
+    switch (mt) {
+      case 4: up_tile<4, 4>(a, lds, tr, ra, wq, wsc, a.I, jb, a.h, rows); break;
+      case 3: up_tile<4, 3>(a, lds, tr, ra, wq, wsc, a.I, jb, a.h, rows); break;
+      case 2: up_tile<4, 2>(a, lds, tr, ra, wq, wsc, a.I, jb, a.h, rows); break;
+      default: up_tile<4, 1>(a, lds, tr, ra, wq, wsc, a.I, jb, a.h, rows); break;
+    }
   } else {
     const uint8_t* wq = reinterpret_cast<const uint8_t*>(a.sh13_q);
     if (mt == 2) up_tile<8, 2>(a, lds, tr, ra, wq, a.sh13_s, a.Is, jb, a.hs, rows);
@@ -580,12 +583,12 @@ __global__ __launch_bounds__(256, 2) void down_gemm_kernel(ChunkArgs a) {
     const int4 td = a.tiles[tile];
     e = td.x; r0 = td.y; rows = td.z; mt = td.w;
   } else {
-    r0 = (tile - n_routed) * kTileRows;
-    rows = min(kTileRows, a.T - r0);
-    mt = rows > 32 ? 2 : 1;
+    r0 = (tile - n_routed) * kSharedRows;
+    rows = min(kSharedRows, a.T - r0);
+    mt = (rows + 31) / 32;
   }
   const int K = e >= 0 ? a.I : a.Is;
-  if (threadIdx.x < 64) {
+  if (threadIdx.x < kTileRows) {
     const int r = threadIdx.x;
     bool ok;
     if (e >= 0) {
@@ -606,8 +609,12 @@ __global__ __launch_bounds__(256, 2) void down_gemm_kernel(ChunkArgs a) {
   if (e >= 0) {
     const uint8_t* wq = a.w2_q + (size_t)e * a.H * (a.I / 2);
     const uint16_t* wsc = a.w2_s + (size_t)e * a.H * (a.I / kGroup);
-    if (mt == 2) down_tile<4, 2>(a, lds, tr, ra, wq, wsc, a.I, nb, a.y, rows);
-    else down_tile<4, 1>(a, lds, tr, ra, wq, wsc, a.I, nb, a.y, rows);
+    switch (mt) {
+      case 4: down_tile<4, 4>(a, lds, tr, ra, wq, wsc, a.I, nb, a.y, rows); break;
+      case 3: down_tile<4, 3>(a, lds, tr, ra, wq, wsc, a.I, nb, a.y, rows); break;
+      case 2: down_tile<4, 2>(a, lds, tr, ra, wq, wsc, a.I, nb, a.y, rows); break;
+      default: down_tile<4, 1>(a, lds, tr, ra, wq, wsc, a.I, nb, a.y, rows); break;
+    }
   } else {
     const uint8_t* wq = reinterpret_cast<const uint8_t*>(a.sh2_q);
     if (mt == 2) down_tile<8, 2>(a, lds, tr, ra, wq, a.sh2_s, a.Is, nb, a.ys, rows);

@@ -4,7 +4,8 @@
 
 namespace moe {
 
-static constexpr int kTileRows = 64;  // rows of a grouped-GEMM tile (32-row kind for short tails)
+static constexpr int kTileRows = 128;  // rows of a routed grouped-GEMM tile (4 MFMA row blocks of 32)
+static constexpr int kSharedRows = 64;  // rows of a shared-expert tile (int8 weights need more registers)
 
 struct ChunkArgs {
   int H, E, k, I, Is, T;
@@ -22,14 +23,14 @@ struct ChunkArgs {
   int32_t* offsets;    // [E+1]
   int32_t* sorted_pair;  // [T*k]  pair index at each expert-major position
   int32_t* pos_of_pair;  // [T*k]  expert-major position of each pair (-1: dropped)
-  int4* tiles;         // [max_route_tiles] (expert, first row, rows, 32-row subtiles)
+  int4* tiles;         // [max_route_tiles] (expert, first row, rows, 32-row blocks)
   int32_t* n_tiles;    // routed tiles written by the bucketing kernel
   _Float16* h;         // [T*k][I]  expert-major rows
   _Float16* hs;        // [T][Is]
   _Float16* y;         // [T*k][H]  weighted expert outputs, expert-major rows
   _Float16* ys;        // [T][H]    sigma * shared output, or null (routed half only)
   int route_tiles;     // 1: routed tiles present
-  int shared_tiles;    // number of 64-token shared-expert tiles (0: routed half only)
+  int shared_tiles;    // number of kSharedRows-token shared-expert tiles (0: routed half only)
   int max_route_tiles; // bound on routed tiles for the grid
 };
 

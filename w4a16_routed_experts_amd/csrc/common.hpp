@@ -34,27 +34,34 @@ __device__ __forceinline__ uint32_t as_u32(h2 v) { return __builtin_bit_cast(uin
 // the bias, which is exact.
 // ---------------------------------------------------------------------------
 
+// mask ? (x ^ b) : b, bit by bit (a single v_bitop3 on gfx950).  With b
+// holding the sign bit of each field under the mask and the binary16 constant
+// outside it, this turns two's complement fields into biased codes and ORs
+// them into the constant in one instruction.
+__device__ __forceinline__ uint32_t flip_into(uint32_t x, uint32_t mask, uint32_t b) {
+  return (mask & (x ^ b)) | (~mask & b);
+}
+
 // one word = 8 int4 codes (k0 in bits 0-3 ... k7 in bits 28-31)
 __device__ __forceinline__ void int4x8_to_h2x4(uint32_t w, h2 out[4]) {
-  const uint32_t u = w ^ 0x88888888u;  // two's complement -> code + 8 in [0, 15]
-  const uint32_t v = u >> 8;
+  const uint32_t v = w >> 8;
   const h2 lo_bias = as_h2(0x64086408u);  // 1032 = 1024 + 8
   const h2 hi_bias = as_h2(0x54805480u);  // 72 = 64 + 8
-  out[0] = as_h2((u & 0x000F000Fu) | 0x64006400u) - lo_bias;  // (k0, k4)
-  out[1] = as_h2((u & 0x00F000F0u) | 0x54005400u) - hi_bias;  // (k1, k5)
-  out[2] = as_h2((v & 0x000F000Fu) | 0x64006400u) - lo_bias;  // (k2, k6)
-  out[3] = as_h2((v & 0x00F000F0u) | 0x54005400u) - hi_bias;  // (k3, k7)
+  out[0] = as_h2(flip_into(w, 0x000F000Fu, 0x64086408u)) - lo_bias;  // (k0, k4)
+  out[1] = as_h2(flip_into(w, 0x00F000F0u, 0x54805480u)) - hi_bias;  // (k1, k5)
+  out[2] = as_h2(flip_into(v, 0x000F000Fu, 0x64086408u)) - lo_bias;  // (k2, k6)
+  out[3] = as_h2(flip_into(v, 0x00F000F0u, 0x54805480u)) - hi_bias;  // (k3, k7)
 }
 
 // two words = 8 int8 codes (w0: k0..k3, w1: k4..k7), same output order
 __device__ __forceinline__ void int8x8_to_h2x4(uint32_t w0, uint32_t w1, h2 out[4]) {
-  const uint32_t a = __builtin_amdgcn_perm(w1, w0, 0x05040100u) ^ 0x80808080u;  // k0 k1 k4 k5 (+128)
-  const uint32_t b = __builtin_amdgcn_perm(w1, w0, 0x07060302u) ^ 0x80808080u;  // k2 k3 k6 k7 (+128)
+  const uint32_t a = __builtin_amdgcn_perm(w1, w0, 0x05040100u);  // k0 k1 k4 k5
+  const uint32_t b = __builtin_amdgcn_perm(w1, w0, 0x07060302u);  // k2 k3 k6 k7
   const h2 bias = as_h2(0x64806480u);  // 1152 = 1024 + 128
-  out[0] = as_h2((a & 0x00FF00FFu) | 0x64006400u) - bias;         // (k0, k4)
-  out[1] = as_h2(((a >> 8) & 0x00FF00FFu) | 0x64006400u) - bias;  // (k1, k5)
-  out[2] = as_h2((b & 0x00FF00FFu) | 0x64006400u) - bias;         // (k2, k6)
-  out[3] = as_h2(((b >> 8) & 0x00FF00FFu) | 0x64006400u) - bias;  // (k3, k7)
+  out[0] = as_h2(flip_into(a, 0x00FF00FFu, 0x64806480u)) - bias;       // (k0, k4)
+  out[1] = as_h2(flip_into(a >> 8, 0x00FF00FFu, 0x64806480u)) - bias;  // (k1, k5)
+  out[2] = as_h2(flip_into(b, 0x00FF00FFu, 0x64806480u)) - bias;       // (k2, k6)
+  out[3] = as_h2(flip_into(b >> 8, 0x00FF00FFu, 0x64806480u)) - bias;  // (k3, k7)
 }
 
 // Eight activations in natural order (4 words: [x1:x0] [x3:x2] [x5:x4] [x7:x6])
