@@ -43,7 +43,7 @@
  *   - Shape admission: G = 64; 1 <= k <= E <= 256 and k <= 8; each of H, I and
  *     Is is 64 * 2^m or a multiple of 2048, and at most 4096; 0 <= T <= 65536.
  *   - The workspace (`ws`, `ws_bytes` >= moe_workspace_bytes(dims, T)) is
- *     scratch owned by the caller.  Its first 36 KiB hold counters and flags
+ *     scratch owned by the caller.  Its first 40 KiB hold counters and flags
  *     that must be zero before the first call that uses the workspace
  *     (allocate it zero-filled); every completed call leaves them zero.  Calls
  *     that share a workspace must be ordered (same stream, or synchronised).

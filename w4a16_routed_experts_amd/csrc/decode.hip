@@ -39,16 +39,21 @@ __device__ __forceinline__ void st_co(float* p, float v) {
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// Completion signalling.  Producers count finished items with a device-scope
-// atomic on the counter; the producer whose increment completes it raises a
-// done flag in each XCD's flag page.  Consumers poll only their own XCD's flag
-// (device-coherent loads), so no memory line is polled by more than one XCD's
-// workgroups and the counters themselves are never polled.
+// Completion signalling.  Items of a stage count on kSubCounters
+// sub-counters (item mod 8, each on its own 128-byte line) with device-scope
+// atomics; the item that completes a sub-counter bumps the stage's top
+// counter, and the one that completes that raises a done flag in each XCD's
+// flag page.  Consumers poll only their own XCD's flag (device-coherent
+// loads): no line is polled by more than one XCD's workgroups, the counters
+// are never polled, and no counter takes more than about n/8 increments.
 __device__ __forceinline__ int xcc_id() {
   return (int)(__builtin_amdgcn_s_getreg(20 | (15 << 11)) & (kXcds - 1));  // HW_REG_XCC_ID[3:0]
 }
+__device__ __forceinline__ uint32_t* counter_of(uint32_t* sync, int which, int sub) {
+  return sync + (which * (kSubCounters + 1) + sub) * kSyncStride;
+}
 __device__ __forceinline__ uint32_t* flag_of(uint32_t* sync, int xcd, int which) {
-  return sync + (1 + xcd) * kFlagPage + which * kSyncStride;
+  return sync + (kCounterPages + xcd) * kFlagPage + which * kSyncStride;
 }
 
 __device__ __forceinline__ void wait_done(uint32_t* sync, int which) {
@@ -58,7 +63,7 @@ __device__ __forceinline__ void wait_done(uint32_t* sync, int which) {
     while (__hip_atomic_load(f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 0u) {
       __builtin_amdgcn_s_sleep(1);
       if (++spins > (1u << 24)) {  // never expected; guarantees the launch drains
-        __hip_atomic_store(sync + SYNC_ERR * kSyncStride, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(counter_of(sync, SYNC_ERR, 0), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         break;
       }
     }
@@ -66,18 +71,40 @@ __device__ __forceinline__ void wait_done(uint32_t* sync, int which) {
   __syncthreads();
 }
 
-// Every wave's coherent stores are acknowledged before the counter moves; the
-// last of `target` items raises the done flags.
-__device__ __forceinline__ void signal_item(uint32_t* sync, int which, uint32_t target) {
+// Item `item` of `n` is finished: every wave's coherent stores are
+// acknowledged before any counter moves.
+__device__ __forceinline__ void signal_item(uint32_t* sync, int which, int item, int n) {
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
   if (threadIdx.x == 0) {
+    const int sub = item % kSubCounters;
+    const uint32_t sub_target = (uint32_t)((n - sub + kSubCounters - 1) / kSubCounters);
     const uint32_t old =
-        __hip_atomic_fetch_add(sync + which * kSyncStride, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    if (old == target - 1)
-      for (int x = 0; x < kXcds; ++x)
-        __hip_atomic_store(flag_of(sync, x, which), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_fetch_add(counter_of(sync, which, sub), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (old == sub_target - 1) {
+      const uint32_t top_target = (uint32_t)(n < kSubCounters ? n : kSubCounters);
+      const uint32_t top = __hip_atomic_fetch_add(counter_of(sync, which, kSubCounters), 1u, __ATOMIC_RELAXED,
+                                                  __HIP_MEMORY_SCOPE_AGENT);
+      if (top == top_target - 1)
+        for (int x = 0; x < kXcds; ++x)
+          __hip_atomic_store(flag_of(sync, x, which), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
   }
+}
+
+// The workgroups of one role: those on XCDs [x0, x1) (the dispatcher places
+// block b on XCD b mod 8, and the XCDs start a launch at different times, so
+// the first stages go to the XCDs that start first).  When the grid is not a
+// whole number of XCD rounds every workgroup takes part, the role's items
+// starting `shift` blocks in (so two roles do not start on the same blocks).
+struct Role {
+  int idx, count;  // this workgroup's index in the role (-1: not in it), role size
+};
+__device__ __forceinline__ Role role_of(int b, int nb, int x0, int x1, int shift) {
+  if (nb % kXcds != 0 || nb < 8 * kXcds) return Role{(b + nb - shift % nb) % nb, nb};
+  const int x = b % kXcds;
+  if (x < x0 || x >= x1) return Role{-1, (nb / kXcds) * (x1 - x0)};
+  return Role{(b / kXcds) * (x1 - x0) + (x - x0), (nb / kXcds) * (x1 - x0)};
 }
 
 // copy n halves (n multiple of 8) global -> LDS with 16-byte accesses
@@ -103,6 +130,36 @@ __device__ __forceinline__ void gather_batched(Dst* dst, const float* src, int n
     for (int u = 0; u < B; ++u) {
       const int q = base + u * 256 + (int)threadIdx.x;
       if (q < n) dst[q] = (Dst)v[u];
+    }
+  }
+}
+
+// h_e (n_up items of he_cols floats, he_stride apart) -> act[ti][I] in
+// binary16, 16-byte loads, up to 8 in flight per thread (one round trip at
+// real widths)
+__device__ __forceinline__ void gather_h(_Float16* act, const float* h_e, const DecodePlan& p, int I) {
+  constexpr int B = 8;
+  const int cpi = p.he_cols / 4;
+  const int n = p.n_up * cpi;
+  for (int base = 0; base < n; base += B * 256) {
+    float4 v[B];
+#pragma unroll
+    for (int u = 0; u < B; ++u) {
+      const int c = base + u * 256 + (int)threadIdx.x;
+      const int item = c / cpi;
+      v[u] = c < n ? *reinterpret_cast<const float4*>(h_e + (size_t)item * p.he_stride + 4 * (c % cpi))
+                   : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+#pragma unroll
+    for (int u = 0; u < B; ++u) {
+      const int c = base + u * 256 + (int)threadIdx.x;
+      const int item = c / cpi;
+      const int ti = item / p.up_jblocks;
+      const int j = (item % p.up_jblocks) * p.he_cols + 4 * (c % cpi);
+      if (c < n && j < I) {
+        _Float16* d = act + (size_t)ti * I + j;
+        d[0] = (_Float16)v[u].x; d[1] = (_Float16)v[u].y; d[2] = (_Float16)v[u].z; d[3] = (_Float16)v[u].w;
+      }
     }
   }
 }
@@ -356,15 +413,24 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
   copy_halves(act, a.x, T * H);
   __syncthreads();
 
+  // Roles: router rows on XCDs 0-1 (they start first), shared gate/up on
+  // XCD 2, stage B (expert gate/up, shared down) on XCDs 3-7; the down rows
+  // on every workgroup.
+  const Role r_router = role_of(b, nb, 0, 2, 0), r_shup = role_of(b, nb, 2, 3, p.n_router);
+  const Role r_b = role_of(b, nb, 3, kXcds, 0);
+
   // ---------------- stage A
   if (MODE == DEC_FORWARD) {
-    const int nA = p.n_router + p.n_shup;
-    for (int item = b; item < nA; item += nb) {
-      const bool is_router = item < p.n_router;
-      if (is_router) router_item<CPL8H>(a, H, item, act);
-      else shup_item<CPL8H>(a, H, Is, item - p.n_router, act);
-      signal_item(a.sync, is_router ? SYNC_ROUTER : SYNC_SHUP, is_router ? p.n_router : p.n_shup);
-    }
+    if (r_router.idx >= 0)
+      for (int item = r_router.idx; item < p.n_router; item += r_router.count) {
+        router_item<CPL8H>(a, H, item, act);
+        signal_item(a.sync, SYNC_ROUTER, item, p.n_router);
+      }
+    if (r_shup.idx >= 0)
+      for (int item = r_shup.idx; item < p.n_shup; item += r_shup.count) {
+        shup_item<CPL8H>(a, H, Is, item, act);
+        signal_item(a.sync, SYNC_SHUP, item, p.n_shup);
+      }
   }
 
   // ---------------- routing into LDS
@@ -404,10 +470,10 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
   {
     const int nB = p.n_up + (MODE == DEC_FORWARD ? p.n_sd : 0);
     bool hs_ready = false;
-    for (int item = b; item < nB; item += nb) {
+    for (int item = r_b.idx; r_b.idx >= 0 && item < nB; item += r_b.count) {
       if (item < p.n_up) {
         up_item<CPL4H>(a, H, I, item, act, s_ids);
-        signal_item(a.sync, SYNC_UP, p.n_up);
+        signal_item(a.sync, SYNC_UP, item, p.n_up);
       } else {
         if (!hs_ready) {
           wait_done(a.sync, SYNC_SHUP);
@@ -419,7 +485,7 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
           hs_ready = true;
         }
         sd_item<CPL8S>(a, H, Is, item - p.n_up, hs_lds);
-        signal_item(a.sync, SYNC_SD, p.n_sd);
+        signal_item(a.sync, SYNC_SD, item - p.n_up, p.n_sd);
       }
     }
   }
@@ -452,10 +518,7 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
       if (!h_ready) {
         wait_done(a.sync, SYNC_UP);
         if (MODE == DEC_FORWARD) wait_done(a.sync, SYNC_SD);
-        gather_batched(act, a.h_e, T * k * I, [&](int q) {
-          const int ti = q / I, j = q % I;
-          return (size_t)(ti * p.up_jblocks + j / p.he_cols) * p.he_stride + j % p.he_cols;
-        });
+        gather_h(act, a.h_e, p, I);
         __syncthreads();
         h_ready = true;
       }
@@ -487,11 +550,12 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
   // ---------------- drain: the last workgroup out clears the counters
   __syncthreads();
   if (tid == 0) {
-    const uint32_t old =
-        __hip_atomic_fetch_add(a.sync + SYNC_EXIT * kSyncStride, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const uint32_t old = __hip_atomic_fetch_add(counter_of(a.sync, SYNC_EXIT, 0), 1u, __ATOMIC_RELAXED,
+                                                __HIP_MEMORY_SCOPE_AGENT);
     if (old == (uint32_t)nb - 1) {
-      for (int w = 0; w < SYNC_EXIT + 1; ++w) {
-        __hip_atomic_store(a.sync + w * kSyncStride, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      for (int w = 0; w <= SYNC_EXIT; ++w) {
+        for (int c = 0; c <= kSubCounters; ++c)
+          __hip_atomic_store(counter_of(a.sync, w, c), 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         for (int x = 0; x < kXcds; ++x)
           __hip_atomic_store(flag_of(a.sync, x, w), 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       }

@@ -8,8 +8,10 @@ static constexpr int kDecMaxT = 4;        // tokens per call on this path
 static constexpr int kSyncStride = 32;    // counters 128 bytes apart (in 32-bit words)
 static constexpr int kXcds = 8;           // XCDs of an MI355X
 static constexpr int kFlagPage = 1024;    // per-XCD flag pages 4 KiB apart (in words)
-static constexpr int kSyncBytes = (1 + kXcds) * kFlagPage * 4;  // counters, then one flag page per XCD
-enum { SYNC_ROUTER = 0, SYNC_SHUP = 1, SYNC_UP = 2, SYNC_SD = 3, SYNC_EXIT = 4, SYNC_ERR = 5 };
+static constexpr int kCounterPages = 2;   // 64 counter slots
+static constexpr int kSubCounters = 8;    // items of a stage count on 8 sub-counters, then one top counter
+static constexpr int kSyncBytes = (kCounterPages + kXcds) * kFlagPage * 4;  // counters, then one flag page per XCD
+enum { SYNC_ROUTER = 0, SYNC_SHUP = 1, SYNC_UP = 2, SYNC_SD = 3, SYNC_EXIT = 4, SYNC_ERR = 5, SYNC_COUNT = 6 };
 enum { DEC_FORWARD = 0, DEC_EXPERTS = 1 };
 
 __host__ __device__ constexpr int round32(int x) { return (x + 31) / 32 * 32; }
