@@ -105,24 +105,27 @@ __global__ __launch_bounds__(256) void router_gemm_kernel(ChunkArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// 2. top-k: one workgroup per token
+// 2. top-k: one wave per token
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void topk_kernel(ChunkArgs a) {
-  __shared__ float lg[kMaxExperts + 1];
-  __shared__ TopkScratch sc;
-  __shared__ int ids[kMaxTopK];
-  __shared__ float w[kMaxTopK];
-  const int t = blockIdx.x;
+  __shared__ TopkScratch sc[4];
+  __shared__ int ids[4][kMaxTopK];
+  __shared__ float w[4][kMaxTopK];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int t = blockIdx.x * 4 + wave;
+  if (t >= a.T) return;  // whole waves: no workgroup barrier below
   const int nrows = a.E + 1;
-  for (int e = threadIdx.x; e < nrows; e += blockDim.x) lg[e] = a.logits[(size_t)t * nrows + e];
-  __syncthreads();
-  block_topk(lg, a.E, a.k, ids, w, sc);
-  __syncthreads();
-  if ((int)threadIdx.x < a.k) {
-    a.ids[(size_t)t * a.k + threadIdx.x] = ids[threadIdx.x];
-    a.wts[(size_t)t * a.k + threadIdx.x] = w[threadIdx.x];
+  const float* lg = a.logits + (size_t)t * nrows;
+  float v[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) v[j] = 4 * lane + j < a.E ? lg[4 * lane + j] : 0.f;
+  wave_topk(v, a.E, a.k, ids[wave], w[wave], sc[wave]);
+  __builtin_amdgcn_wave_barrier();
+  if (lane < a.k) {
+    a.ids[(size_t)t * a.k + lane] = ids[wave][lane];
+    a.wts[(size_t)t * a.k + lane] = w[wave][lane];
   }
-  if (threadIdx.x == 0) a.sigma[t] = sigmoid_f(lg[a.E]);
+  if (lane == 0) a.sigma[t] = sigmoid_f(lg[a.E]);
 }
 
 // ---------------------------------------------------------------------------
@@ -657,7 +660,7 @@ __global__ __launch_bounds__(256) void combine_kernel(ChunkArgs a) {
 // ---------------------------------------------------------------------------
 int launch_route_chunk(const ChunkArgs& a, hipStream_t s) {
   hipLaunchKernelGGL(router_gemm_kernel, dim3((a.T + 31) / 32, (a.E + 1 + 31) / 32), dim3(256), 0, s, a);
-  hipLaunchKernelGGL(topk_kernel, dim3(a.T), dim3(256), 0, s, a);
+  hipLaunchKernelGGL(topk_kernel, dim3((a.T + 3) / 4), dim3(256), 0, s, a);
   return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_LAUNCH;
 }
 

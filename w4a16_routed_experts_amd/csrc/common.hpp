@@ -160,81 +160,77 @@ __device__ __forceinline__ float lane_group_sum(float v, int width) {
 // ---------------------------------------------------------------------------
 
 struct TopkScratch {
-  uint32_t gmax[8];
-  int count;
-  uint32_t ckey[kMaxExperts];
-  int cidx[kMaxExperts];
+  uint64_t comp[kMaxExperts];  // candidates: (order key << 32) | (0xFFFF - expert)
   int sel_idx[kMaxTopK];
   float sel_val[kMaxTopK];
 };
 
-// Top-k of one token's E router logits (LDS) by the whole workgroup.
+// Top-k of one token's E router logits by ONE wave, with no workgroup
+// barrier.  Lane l holds the logits of experts 4l .. 4l+3 in v[] (entries at
+// or past E are ignored).
 //
 // Selection is by logit (softmax is monotone), descending, ties to the lower
 // expert index; the kept probabilities are renormalised, which equals a
-// softmax over the k kept logits.  A lower bound tau of the k-th largest logit
-// is the smallest of k or more group maxima (groups of 32 experts); only the
-// experts at or above tau are ranked, each against the other candidates.
-__device__ inline void block_topk(const float* lg, int E, int k, int* ids_out, float* w_out, TopkScratch& sc) {
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const bool valid = tid < E;
-  const uint32_t key = valid ? order_key(lg[tid]) : 0u;
-  const bool grouped = E >= 32 * k;  // uniform
-  if (grouped) {
-    uint32_t m = key;
-    m = max(m, dpp_u32<0xB1>(m));
-    m = max(m, dpp_u32<0x4E>(m));
-    m = max(m, dpp_u32<0x124>(m));
-    m = max(m, dpp_u32<0x128>(m));
-    const uint32_t r0 = __builtin_amdgcn_readlane(m, 0), r1 = __builtin_amdgcn_readlane(m, 16);
-    const uint32_t r2 = __builtin_amdgcn_readlane(m, 32), r3 = __builtin_amdgcn_readlane(m, 48);
-    if (lane == 0) {
-      sc.gmax[2 * wave] = max(r0, r1);
-      sc.gmax[2 * wave + 1] = max(r2, r3);
-    }
+// softmax over the k kept logits.  With at least k groups of 32 experts, the
+// smallest group maximum tau bounds the k-th largest logit from below, so
+// only the experts at or above tau are candidates.  Candidates are compacted
+// by ballot and ranked, each against every other, on a 64-bit key that orders
+// by (logit desc, expert asc) and is unique.  Lanes 0..k-1 write ids_out and
+// w_out (rank order).
+__device__ inline void wave_topk(const float v[4], int E, int k, int* ids_out, float* w_out, TopkScratch& sc) {
+  const int lane = threadIdx.x & 63;
+  uint32_t key[4];
+  bool ok[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    ok[j] = 4 * lane + j < E;
+    key[j] = ok[j] ? order_key(v[j]) : 0u;
   }
-  if (tid == 0) sc.count = 0;
-  __syncthreads();
   uint32_t tau = 0;
-  if (grouped) {
-    tau = 0xFFFFFFFFu;
-    const int ng = (E + 31) / 32;
-    for (int g = 0; g < ng; ++g) tau = min(tau, sc.gmax[g]);
+  if ((E + 31) / 32 >= k) {  // uniform
+    // maximum of each 32-expert group (8 lanes), spread over its lanes
+    uint32_t m = max(max(key[0], key[1]), max(key[2], key[3]));
+    m = max(m, dpp_u32<0xB1>(m));  // quad_perm(1,0,3,2)
+    m = max(m, dpp_u32<0x4E>(m));  // quad_perm(2,3,0,1)
+    m = max(m, (uint32_t)__shfl_xor((int)m, 4, 64));
+    // smallest maximum over the groups that hold experts
+    tau = wave_min_u32(4 * lane < E ? m : 0xFFFFFFFFu);
   }
-  if (valid && key >= tau) {
-    const int slot = atomicAdd(&sc.count, 1);
-    sc.ckey[slot] = key;
-    sc.cidx[slot] = tid;
+  int base = 0;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const bool cand = ok[j] && key[j] >= tau;
+    const uint64_t bal = __ballot(cand);
+    const int pos = base + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0u));
+    if (cand) sc.comp[pos] = ((uint64_t)key[j] << 32) | (uint64_t)(0xFFFFu - (uint32_t)(4 * lane + j));
+    base += __popcll(bal);
   }
-  __syncthreads();
-  const int C = sc.count;
-  if (tid < C) {
-    const uint32_t mk = sc.ckey[tid];
-    const int mi = sc.cidx[tid];
-    int r0 = 0, r1 = 0;
+  const int C = base;
+  __builtin_amdgcn_wave_barrier();
+  for (int c0 = lane; c0 < C; c0 += 64) {
+    const uint64_t my = sc.comp[c0];
+    int r0 = 0, r1 = 0, r2 = 0, r3 = 0;
     int c = 0;
-    for (; c + 1 < C; c += 2) {
-      const uint32_t k0 = sc.ckey[c], k1 = sc.ckey[c + 1];
-      const int i0 = sc.cidx[c], i1 = sc.cidx[c + 1];
-      r0 += (k0 > mk) || (k0 == mk && i0 < mi);
-      r1 += (k1 > mk) || (k1 == mk && i1 < mi);
+    for (; c + 3 < C; c += 4) {
+      r0 += sc.comp[c] > my;
+      r1 += sc.comp[c + 1] > my;
+      r2 += sc.comp[c + 2] > my;
+      r3 += sc.comp[c + 3] > my;
     }
-    if (c < C) r0 += (sc.ckey[c] > mk) || (sc.ckey[c] == mk && sc.cidx[c] < mi);
-    const int rank = r0 + r1;
+    for (; c < C; ++c) r0 += sc.comp[c] > my;
+    const int rank = (r0 + r1) + (r2 + r3);
     if (rank < k) {
-      sc.sel_idx[rank] = mi;
-      sc.sel_val[rank] = lg[mi];
+      sc.sel_idx[rank] = (int)(0xFFFFu - (uint32_t)(my & 0xFFFFu));
+      sc.sel_val[rank] = key_to_float((uint32_t)(my >> 32));
     }
   }
-  __syncthreads();
-  if (wave == 0) {
-    const float v0 = sc.sel_val[0];
-    const float e = lane < k ? expf(sc.sel_val[lane < k ? lane : 0] - v0) : 0.f;
-    const float s = row16_sum(e);  // k <= 8: lanes 0..k-1 sit in row 0
-    if (lane < k) {
-      ids_out[lane] = sc.sel_idx[lane];
-      w_out[lane] = e / s;
-    }
+  __builtin_amdgcn_wave_barrier();
+  const float v0 = sc.sel_val[0];
+  const float e = lane < k ? expf(sc.sel_val[lane < k ? lane : 0] - v0) : 0.f;
+  const float s = row16_sum(e);  // k <= 8: lanes 0..k-1 sit in row 0
+  if (lane < k) {
+    ids_out[lane] = sc.sel_idx[lane];
+    w_out[lane] = e / s;
   }
 }
 

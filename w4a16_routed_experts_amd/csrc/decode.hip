@@ -13,8 +13,8 @@
 //   B  expert gate/up rows of the k selected experts (h_e)   <- router
 //      shared-expert down rows (s)                           <- shared gate/up
 //   C  expert down rows + weighted combine + sigma * s       <- B
-// Every workgroup recomputes the top-k from the logits (all 256 threads, see
-// block_topk), so no hand-off is needed between routing and the experts.  The
+// Every workgroup recomputes the top-k from the logits (one wave per token,
+// see wave_topk), so no hand-off is needed between routing and the experts.  The
 // weights of a workgroup's first C item are loaded before it waits.
 //
 // Hand-off without cache maintenance.  On gfx950 each XCD has its own L2, and
@@ -404,8 +404,7 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
   __shared__ float s_w[kDecMaxT][kMaxTopK];
   __shared__ float s_sig[kDecMaxT];
   __shared__ float s_red[4][64];
-  __shared__ float s_logits[kDecMaxT * (kMaxExperts + 1)];
-  __shared__ TopkScratch s_topk;
+  __shared__ TopkScratch s_topk[kDecMaxT];
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int nb = gridDim.x, b = blockIdx.x;
@@ -436,17 +435,23 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
   // ---------------- routing into LDS
   if (MODE == DEC_FORWARD) {
     wait_done(a.sync, SYNC_ROUTER);
-    const int nrows = E + 1;
-    gather_batched(s_logits, a.logits, T * nrows, [&](int q) {
-      const int t = q / nrows, r = q % nrows;
-      return ((size_t)(r / p.lg_rows) * T + t) * p.lg_stride + r % p.lg_rows;
-    });
-    __syncthreads();
-    for (int t = 0; t < T; ++t) {
-      block_topk(s_logits + t * nrows, E, k, s_ids[t], s_w[t], s_topk);
-      if (tid == 0) s_sig[t] = sigmoid_f(s_logits[t * nrows + E]);
-      __syncthreads();
+    // wave t ranks token t, reading its logits straight from the router
+    // items' regions (lane l: experts 4l..4l+3, one 16-byte load)
+    if (wave < T) {
+      const int t = wave;
+      const int e0 = 4 * lane;
+      // both loads are issued before either value is used
+      const float gate = a.logits[((size_t)(E / p.lg_rows) * T + t) * p.lg_stride + E % p.lg_rows];
+      float v[4] = {0.f, 0.f, 0.f, 0.f};
+      if (e0 < p.n_router * p.lg_rows) {
+        const float4 q = *reinterpret_cast<const float4*>(
+            a.logits + ((size_t)(e0 / p.lg_rows) * T + t) * p.lg_stride + e0 % p.lg_rows);
+        v[0] = q.x; v[1] = q.y; v[2] = q.z; v[3] = q.w;
+      }
+      wave_topk(v, E, k, s_ids[t], s_w[t], s_topk[t]);
+      if (lane == 0) s_sig[t] = sigmoid_f(gate);
     }
+    __syncthreads();
     if (b == 0) {
       for (int q = tid; q < T * k; q += blockDim.x) {
         const int t = q / k, i = q % k;
@@ -548,17 +553,29 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
   }
 
   // ---------------- drain: the last workgroup out clears the counters
+  // (exits count on sub-counters too: 512 increments of one counter would
+  // serialise at the memory for microseconds)
+  __shared__ int s_last;
   __syncthreads();
   if (tid == 0) {
-    const uint32_t old = __hip_atomic_fetch_add(counter_of(a.sync, SYNC_EXIT, 0), 1u, __ATOMIC_RELAXED,
-                                                __HIP_MEMORY_SCOPE_AGENT);
-    if (old == (uint32_t)nb - 1) {
-      for (int w = 0; w <= SYNC_EXIT; ++w) {
-        for (int c = 0; c <= kSubCounters; ++c)
-          __hip_atomic_store(counter_of(a.sync, w, c), 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        for (int x = 0; x < kXcds; ++x)
-          __hip_atomic_store(flag_of(a.sync, x, w), 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      }
+    const int sub = b % kSubCounters;
+    const uint32_t sub_target = (uint32_t)((nb - sub + kSubCounters - 1) / kSubCounters);
+    bool last = false;
+    if (__hip_atomic_fetch_add(counter_of(a.sync, SYNC_EXIT, sub), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+        sub_target - 1) {
+      const uint32_t top_target = (uint32_t)(nb < kSubCounters ? nb : kSubCounters);
+      last = __hip_atomic_fetch_add(counter_of(a.sync, SYNC_EXIT, kSubCounters), 1u, __ATOMIC_RELAXED,
+                                    __HIP_MEMORY_SCOPE_AGENT) == top_target - 1;
+    }
+    s_last = last;
+  }
+  __syncthreads();
+  if (s_last) {  // one store per thread: counters, then flags
+    constexpr int NC = (SYNC_EXIT + 1) * (kSubCounters + 1), NF = (SYNC_EXIT + 1) * kXcds;
+    for (int q = tid; q < NC + NF; q += blockDim.x) {
+      uint32_t* w = q < NC ? counter_of(a.sync, q / (kSubCounters + 1), q % (kSubCounters + 1))
+                           : flag_of(a.sync, (q - NC) % kXcds, (q - NC) / kXcds);
+      __hip_atomic_store(w, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
   }
 }
