@@ -10,7 +10,7 @@
 // hand results to each other through counters instead of kernel boundaries
 // (one launch costs about as much as the whole layer's HBM time at one token):
 //   A  router rows (logits) | shared-expert gate/up rows (h_s)
-//   B  expert gate/up rows of the k selected experts (h_e)   <- router
+//   B  expert gate/up rows of the k selected experts (h_e, binary16)  <- router
 //      shared-expert down rows (s)                           <- shared gate/up
 //   C  expert down rows + weighted combine + sigma * s       <- B
 // Every workgroup recomputes the top-k from the logits (one wave per token,
@@ -38,14 +38,17 @@ namespace moe {
 __device__ __forceinline__ void st_co(float* p, float v) {
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
+__device__ __forceinline__ void st_co_h(uint16_t* p, float v) {
+  __hip_atomic_store(p, __builtin_bit_cast(uint16_t, (_Float16)v), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
 
 // Completion signalling.  Items of a stage count on kSubCounters
 // sub-counters (item mod 8, each on its own 128-byte line) with device-scope
-// atomics; the item that completes a sub-counter bumps the stage's top
-// counter, and the one that completes that raises a done flag in each XCD's
-// flag page.  Consumers poll only their own XCD's flag (device-coherent
-// loads): no line is polled by more than one XCD's workgroups, the counters
-// are never polled, and no counter takes more than about n/8 increments.
+// atomics; the item that completes a sub-counter sets the sub-counter's bit
+// in the stage's done word of each XCD's flag page.  Consumers poll only
+// their own XCD's word (device-coherent loads) until every bit is set: no
+// line is polled by more than one XCD's workgroups, the counters are never
+// polled, and no counter takes more than about n/8 increments.
 __device__ __forceinline__ int xcc_id() {
   return (int)(__builtin_amdgcn_s_getreg(20 | (15 << 11)) & (kXcds - 1));  // HW_REG_XCC_ID[3:0]
 }
@@ -55,12 +58,15 @@ __device__ __forceinline__ uint32_t* counter_of(uint32_t* sync, int which, int s
 __device__ __forceinline__ uint32_t* flag_of(uint32_t* sync, int xcd, int which) {
   return sync + (kCounterPages + xcd) * kFlagPage + which * kSyncStride;
 }
+// done word of a stage of n items: one bit per non-empty sub-counter
+__device__ __forceinline__ uint32_t done_mask(int n) { return (1u << (n < kSubCounters ? n : kSubCounters)) - 1u; }
 
-__device__ __forceinline__ void wait_done(uint32_t* sync, int which) {
+__device__ __forceinline__ void wait_done(uint32_t* sync, int which, int n) {
   if (threadIdx.x == 0) {
     uint32_t* f = flag_of(sync, xcc_id(), which);
+    const uint32_t want = done_mask(n);
     uint32_t spins = 0;
-    while (__hip_atomic_load(f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 0u) {
+    while (__hip_atomic_load(f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != want) {
       __builtin_amdgcn_s_sleep(1);
       if (++spins > (1u << 24)) {  // never expected; guarantees the launch drains
         __hip_atomic_store(counter_of(sync, SYNC_ERR, 0), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -81,31 +87,27 @@ __device__ __forceinline__ void signal_item(uint32_t* sync, int which, int item,
     const uint32_t sub_target = (uint32_t)((n - sub + kSubCounters - 1) / kSubCounters);
     const uint32_t old =
         __hip_atomic_fetch_add(counter_of(sync, which, sub), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    if (old == sub_target - 1) {
-      const uint32_t top_target = (uint32_t)(n < kSubCounters ? n : kSubCounters);
-      const uint32_t top = __hip_atomic_fetch_add(counter_of(sync, which, kSubCounters), 1u, __ATOMIC_RELAXED,
-                                                  __HIP_MEMORY_SCOPE_AGENT);
-      if (top == top_target - 1)
-        for (int x = 0; x < kXcds; ++x)
-          __hip_atomic_store(flag_of(sync, x, which), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
+    if (old == sub_target - 1)
+      for (int x = 0; x < kXcds; ++x)
+        __hip_atomic_fetch_or(flag_of(sync, x, which), 1u << sub, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 }
 
-// The workgroups of one role: those on XCDs [x0, x1) (the dispatcher places
-// block b on XCD b mod 8, and the XCDs start a launch at different times, so
-// the first stages go to the XCDs that start first).  When the grid is not a
-// whole number of XCD rounds every workgroup takes part, the role's items
-// starting `shift` blocks in (so two roles do not start on the same blocks).
+// The workgroups of one role.  Block b runs on XCD b mod 8 as local slot
+// b / 8; a role takes local slots [j0, j1) on every XCD, so each stage's loads
+// are spread over all eight L2s (whose miss tracking bounds a burst).  When
+// the grid is not a whole number of XCD rounds every workgroup takes part,
+// the role's items starting `shift` blocks in (so two roles do not start on
+// the same blocks).
 struct Role {
   int idx, count;  // this workgroup's index in the role (-1: not in it), role size
 };
-__device__ __forceinline__ Role role_of(int b, int nb, int x0, int x1, int shift) {
-  if (nb % kXcds != 0 || nb < 8 * kXcds) return Role{(b + nb - shift % nb) % nb, nb};
-  const int x = b % kXcds;
-  if (x < x0 || x >= x1) return Role{-1, (nb / kXcds) * (x1 - x0)};
-  return Role{(b / kXcds) * (x1 - x0) + (x - x0), (nb / kXcds) * (x1 - x0)};
+__device__ __forceinline__ Role role_slots(int b, int nb, int j0, int j1) {
+  const int x = b % kXcds, j = b / kXcds;
+  if (j < j0 || j >= j1) return Role{-1, (j1 - j0) * kXcds};
+  return Role{(j - j0) * kXcds + x, (j1 - j0) * kXcds};
 }
+__device__ __forceinline__ Role role_all(int b, int nb, int shift) { return Role{(b + nb - shift % nb) % nb, nb}; }
 
 // copy n halves (n multiple of 8) global -> LDS with 16-byte accesses
 __device__ __forceinline__ void copy_halves(_Float16* dst, const void* src, int n) {
@@ -134,32 +136,29 @@ __device__ __forceinline__ void gather_batched(Dst* dst, const float* src, int n
   }
 }
 
-// h_e (n_up items of he_cols floats, he_stride apart) -> act[ti][I] in
-// binary16, 16-byte loads, up to 8 in flight per thread (one round trip at
+// h_e (n_up items of he_cols binary16 values, he_stride floats apart) ->
+// act[ti][I], 16-byte loads, up to 8 in flight per thread (one round trip at
 // real widths)
 __device__ __forceinline__ void gather_h(_Float16* act, const float* h_e, const DecodePlan& p, int I) {
   constexpr int B = 8;
-  const int cpi = p.he_cols / 4;
+  const int cpi = p.he_cols / 8;  // 16-byte chunks per item
   const int n = p.n_up * cpi;
   for (int base = 0; base < n; base += B * 256) {
-    float4 v[B];
+    uint4 v[B];
 #pragma unroll
     for (int u = 0; u < B; ++u) {
       const int c = base + u * 256 + (int)threadIdx.x;
       const int item = c / cpi;
-      v[u] = c < n ? *reinterpret_cast<const float4*>(h_e + (size_t)item * p.he_stride + 4 * (c % cpi))
-                   : make_float4(0.f, 0.f, 0.f, 0.f);
+      v[u] = c < n ? *reinterpret_cast<const uint4*>(h_e + (size_t)item * p.he_stride + 4 * (c % cpi))
+                   : make_uint4(0, 0, 0, 0);
     }
 #pragma unroll
     for (int u = 0; u < B; ++u) {
       const int c = base + u * 256 + (int)threadIdx.x;
       const int item = c / cpi;
       const int ti = item / p.up_jblocks;
-      const int j = (item % p.up_jblocks) * p.he_cols + 4 * (c % cpi);
-      if (c < n && j < I) {
-        _Float16* d = act + (size_t)ti * I + j;
-        d[0] = (_Float16)v[u].x; d[1] = (_Float16)v[u].y; d[2] = (_Float16)v[u].z; d[3] = (_Float16)v[u].w;
-      }
+      const int j = (item % p.up_jblocks) * p.he_cols + 8 * (c % cpi);
+      if (c < n && j < I) *reinterpret_cast<uint4*>(act + (size_t)ti * I + j) = v[u];
     }
   }
 }
@@ -340,12 +339,12 @@ __device__ void up_item(const DecodeArgs& a, int H, int I, int item, const _Floa
   f.load(rows, srow, g, wbase);
   float acc[8][1];
   f.template dot_shared<1>(g, xs + (size_t)t * H, H, 1, acc);
-  float* dst = a.h_e + (size_t)item * a.p.he_stride;
+  uint16_t* dst = reinterpret_cast<uint16_t*>(a.h_e + (size_t)item * a.p.he_stride);  // binary16 values
 #pragma unroll
   for (int h = 0; h < 4; ++h) {
     const float gate = lane_group_sum(acc[h][0], g.lpr);
     const float up = lane_group_sum(acc[4 + h][0], g.lpr);
-    if (jblk * a.p.he_cols + jl[h] < I && (lane % g.lpr) == 0) st_co(dst + jl[h], e >= 0 ? silu_f(gate) * up : 0.f);
+    if (jblk * a.p.he_cols + jl[h] < I && (lane % g.lpr) == 0) st_co_h(dst + jl[h], e >= 0 ? silu_f(gate) * up : 0.f);
   }
 }
 
@@ -412,11 +411,15 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
   copy_halves(act, a.x, T * H);
   __syncthreads();
 
-  // Roles: router rows on XCDs 0-1 (they start first), shared gate/up on
-  // XCD 2, stage B (expert gate/up, shared down) on XCDs 3-7; the down rows
-  // on every workgroup.
-  const Role r_router = role_of(b, nb, 0, 2, 0), r_shup = role_of(b, nb, 2, 3, p.n_router);
-  const Role r_b = role_of(b, nb, 3, kXcds, 0);
+  // Roles by local slot: router rows, then shared gate/up rows, then stage B
+  // (expert gate/up, shared down) on the remaining slots of every XCD; the
+  // down rows on every workgroup.
+  const int nj = nb / kXcds;
+  const int jr = (p.n_router + kXcds - 1) / kXcds, js = (p.n_shup + kXcds - 1) / kXcds;
+  const bool split = nb % kXcds == 0 && jr + js < nj;  // uniform
+  const Role r_router = split ? role_slots(b, nb, 0, jr) : role_all(b, nb, 0);
+  const Role r_shup = split ? role_slots(b, nb, jr, jr + js) : role_all(b, nb, p.n_router);
+  const Role r_b = split ? role_slots(b, nb, jr + js, nj) : role_all(b, nb, 0);
 
   // ---------------- stage A
   if (MODE == DEC_FORWARD) {
@@ -434,7 +437,7 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
 
   // ---------------- routing into LDS
   if (MODE == DEC_FORWARD) {
-    wait_done(a.sync, SYNC_ROUTER);
+    wait_done(a.sync, SYNC_ROUTER, p.n_router);
     // wave t ranks token t, reading its logits straight from the router
     // items' regions (lane l: experts 4l..4l+3, one 16-byte load)
     if (wave < T) {
@@ -481,7 +484,7 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
         signal_item(a.sync, SYNC_UP, item, p.n_up);
       } else {
         if (!hs_ready) {
-          wait_done(a.sync, SYNC_SHUP);
+          wait_done(a.sync, SYNC_SHUP, p.n_shup);
           gather_batched(hs_lds, a.h_s, T * Is, [&](int q) {
             const int t = q / Is, j = q % Is;
             return ((size_t)(j / p.hs_cols) * T + t) * p.hs_stride + j % p.hs_cols;
@@ -521,8 +524,8 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
       f.load(rows, srow, g, a.w2_q);
       __builtin_amdgcn_sched_barrier(0);  // issue these loads before waiting
       if (!h_ready) {
-        wait_done(a.sync, SYNC_UP);
-        if (MODE == DEC_FORWARD) wait_done(a.sync, SYNC_SD);
+        wait_done(a.sync, SYNC_UP, p.n_up);
+        if (MODE == DEC_FORWARD) wait_done(a.sync, SYNC_SD, p.n_sd);
         gather_h(act, a.h_e, p, I);
         __syncthreads();
         h_ready = true;

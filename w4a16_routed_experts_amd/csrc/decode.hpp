@@ -29,7 +29,7 @@ struct DecodePlan {
   int up_jblocks;           // j-blocks per (token, slot)
   int lg_rows, lg_stride;   // router rows per item; floats per (item, token)
   int hs_cols, hs_stride;   // shared gate/up columns per item; floats per (item, token)
-  int he_cols, he_stride;   // expert gate/up columns per item; floats per item
+  int he_cols, he_stride;   // expert gate/up columns per item; floats (4-byte units) per item
   int ss_rows, ss_stride;   // shared down rows per item; floats per (item, token)
   int down_rows;            // output rows per down item
 };
@@ -69,7 +69,7 @@ struct DecodeArgs {
   uint32_t* sync;
   float* logits;   // router hand-off:      [n_router][T][lg_stride]
   float* h_s;      // shared gate/up:       [n_shup][T][hs_stride]
-  float* h_e;      // expert gate/up:       [n_up][he_stride]
+  float* h_e;      // expert gate/up:       [n_up][he_stride], he_cols binary16 values each
   float* s_sh;     // shared down:          [n_sd][T][ss_stride]
   DecodePlan p;
 };
