@@ -180,6 +180,42 @@ def cpu_baseline(gen, budget_s=12.0):
                       f"({dt:.1f} s; host has {len(os.sched_getaffinity(0))} cores available)"}
 
 
+# --------------------------------------------------------------- counter runs
+
+def profile_run(kind, steps, torch, m, gen):
+    """Untimed steps of one workload plus a calibration copy, for rocprofv3
+    counter passes: FETCH_SIZE / WRITE_SIZE of the layer's kernels are scaled by
+    what the same counters read for the copy, whose bytes are known."""
+    import ctypes
+    import numpy as np
+    cfg = 1 if kind == "decode" else 4
+    case = gen.make_config(cfg)
+    d, T = case.dims, case.T
+    dims = m.make_dims(d.H, d.E, d.k, d.I, d.Is, d.G)
+    R = 32 if cfg == 1 else 4
+    copies = make_copies(case, R, torch, m)
+    x = torch.from_numpy(case.x.view(np.int16)).cuda()
+    out = torch.empty((T, d.H), dtype=torch.int16, device="cuda")
+    ws = m.workspace(dims, T)
+    stream = torch.cuda.current_stream()
+    L = m.lib()
+    for s in range(steps):
+        st = L.moe_forward(ctypes.byref(dims), ctypes.byref(copies[s % R].struct), x.data_ptr(), T, out.data_ptr(),
+                           None, None, None, ws.data_ptr(), ws.numel(), stream.cuda_stream)
+        if st != 0:
+            raise RuntimeError(f"moe_forward: {m.moe_status_string(st)}")
+    torch.cuda.synchronize()
+    log(f"{steps} {kind} steps done")
+    # calibration: a plain device copy of 64 MiB (reads and writes 64 MiB each)
+    src = torch.randint(0, 1 << 30, (16 << 20,), dtype=torch.int32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    log("calibration copy of 64 MiB x 5 done")
+    print(json.dumps({"profile_run": kind, "steps": steps, "calibration_copy_bytes": src.numel() * 4}), flush=True)
+
+
 # --------------------------------------------------------------- main
 
 def main():
@@ -190,6 +226,8 @@ def main():
     ap.add_argument("--copies", type=int, default=32, help="weight copies rotated for cold-cache timing")
     ap.add_argument("--chunk-steps", type=int, default=300, help="steps of the 512-token workload")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--profile-run", choices=["decode", "chunk"], default=None,
+                    help="untimed steps plus a calibration copy, for rocprofv3 counter passes (no JSON metric line)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(json.dumps({"error": "this layer is measured on one GPU; multi-GPU runs are not part of this build",
@@ -200,6 +238,9 @@ def main():
     import w4a16_routed_experts_amd as m
     from workloads import gen
     build_if_missing()
+    if args.profile_run:
+        profile_run(args.profile_run, args.steps, torch, m, gen)
+        return
 
     digest = source_digest()
     log("decode T=1 ...")
