@@ -94,18 +94,29 @@ __device__ __forceinline__ void signal_item(uint32_t* sync, int which, int item,
 }
 
 // The workgroups of one role.  Block b runs on XCD b mod 8 as local slot
-// b / 8; a role takes local slots [j0, j1) on every XCD, so each stage's loads
-// are spread over all eight L2s (whose miss tracking bounds a burst).  When
-// the grid is not a whole number of XCD rounds every workgroup takes part,
-// the role's items starting `shift` blocks in (so two roles do not start on
-// the same blocks).
+// j = b / 8, and slots j and j + nj/2 share a CU.  A role takes local slots on
+// every XCD, so each stage's loads are spread over all eight L2s (whose miss
+// tracking bounds a burst): the expert gate/up items take the second half
+// of the slots (one per CU), router, shared gate/up and shared down items
+// the start of the first half, and any further expert gate/up items the rest
+// of it.  When the grid is not a whole number of XCD rounds every workgroup
+// takes part, the role's items starting `shift` blocks in (so two roles do
+// not start on the same blocks).
 struct Role {
   int idx, count;  // this workgroup's index in the role (-1: not in it), role size
 };
-__device__ __forceinline__ Role role_slots(int b, int nb, int j0, int j1) {
+__device__ __forceinline__ Role role_slots(int b, int j0, int j1) {
   const int x = b % kXcds, j = b / kXcds;
   if (j < j0 || j >= j1) return Role{-1, (j1 - j0) * kXcds};
   return Role{(j - j0) * kXcds + x, (j1 - j0) * kXcds};
+}
+// slots [h, nj) first, then [f, h)
+__device__ __forceinline__ Role role_two(int b, int f, int h, int nj) {
+  const int x = b % kXcds, j = b / kXcds;
+  const int count = (nj - f) * kXcds;
+  if (j >= h) return Role{(j - h) * kXcds + x, count};
+  if (j >= f) return Role{(nj - h + j - f) * kXcds + x, count};
+  return Role{-1, count};
 }
 __device__ __forceinline__ Role role_all(int b, int nb, int shift) { return Role{(b + nb - shift % nb) % nb, nb}; }
 
@@ -411,15 +422,15 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
   copy_halves(act, a.x, T * H);
   __syncthreads();
 
-  // Roles by local slot: router rows, then shared gate/up rows, then stage B
-  // (expert gate/up, shared down) on the remaining slots of every XCD; the
-  // down rows on every workgroup.
-  const int nj = nb / kXcds;
+  // Roles by local slot (see role_slots); the down rows on every workgroup.
+  const int nj = nb / kXcds, half = nj / 2;
   const int jr = (p.n_router + kXcds - 1) / kXcds, js = (p.n_shup + kXcds - 1) / kXcds;
-  const bool split = nb % kXcds == 0 && jr + js < nj;  // uniform
-  const Role r_router = split ? role_slots(b, nb, 0, jr) : role_all(b, nb, 0);
-  const Role r_shup = split ? role_slots(b, nb, jr, jr + js) : role_all(b, nb, p.n_router);
-  const Role r_b = split ? role_slots(b, nb, jr + js, nj) : role_all(b, nb, 0);
+  const int jd = MODE == DEC_FORWARD ? (p.n_sd + kXcds - 1) / kXcds : 0;
+  const bool split = nb % kXcds == 0 && nj % 2 == 0 && jr + js + jd < half;  // uniform
+  const Role r_router = split ? role_slots(b, 0, jr) : role_all(b, nb, 0);
+  const Role r_shup = split ? role_slots(b, jr, jr + js) : role_all(b, nb, p.n_router);
+  const Role r_sd = split ? role_slots(b, jr + js, jr + js + jd) : role_all(b, nb, p.n_up);
+  const Role r_up = split ? role_two(b, jr + js + jd, half, nj) : role_all(b, nb, 0);
 
   // ---------------- stage A
   if (MODE == DEC_FORWARD) {
@@ -475,26 +486,21 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
   }
 
   // ---------------- stage B
-  {
-    const int nB = p.n_up + (MODE == DEC_FORWARD ? p.n_sd : 0);
-    bool hs_ready = false;
-    for (int item = r_b.idx; r_b.idx >= 0 && item < nB; item += r_b.count) {
-      if (item < p.n_up) {
-        up_item<CPL4H>(a, H, I, item, act, s_ids);
-        signal_item(a.sync, SYNC_UP, item, p.n_up);
-      } else {
-        if (!hs_ready) {
-          wait_done(a.sync, SYNC_SHUP, p.n_shup);
-          gather_batched(hs_lds, a.h_s, T * Is, [&](int q) {
-            const int t = q / Is, j = q % Is;
-            return ((size_t)(j / p.hs_cols) * T + t) * p.hs_stride + j % p.hs_cols;
-          });
-          __syncthreads();
-          hs_ready = true;
-        }
-        sd_item<CPL8S>(a, H, Is, item - p.n_up, hs_lds);
-        signal_item(a.sync, SYNC_SD, item - p.n_up, p.n_sd);
-      }
+  if (r_up.idx >= 0)
+    for (int item = r_up.idx; item < p.n_up; item += r_up.count) {
+      up_item<CPL4H>(a, H, I, item, act, s_ids);
+      signal_item(a.sync, SYNC_UP, item, p.n_up);
+    }
+  if (MODE == DEC_FORWARD && r_sd.idx >= 0 && r_sd.idx < p.n_sd) {
+    wait_done(a.sync, SYNC_SHUP, p.n_shup);
+    gather_batched(hs_lds, a.h_s, T * Is, [&](int q) {
+      const int t = q / Is, j = q % Is;
+      return ((size_t)(j / p.hs_cols) * T + t) * p.hs_stride + j % p.hs_cols;
+    });
+    __syncthreads();
+    for (int item = r_sd.idx; item < p.n_sd; item += r_sd.count) {
+      sd_item<CPL8S>(a, H, Is, item, hs_lds);
+      signal_item(a.sync, SYNC_SD, item, p.n_sd);
     }
   }
 
