@@ -44,6 +44,34 @@ __device__ __forceinline__ h8 act_operand(uint4 v) {
 }
 
 // ---------------------------------------------------------------------------
+// Range-checked buffer loads.  A masked row, column or group gets an offset
+// outside its resource and reads zeros, so loads are issued unconditionally
+// and no load feeds a select (a load under a branch, or one whose value is
+// selected at once, makes the compiler wait for it where it is issued).
+// ---------------------------------------------------------------------------
+static constexpr uint32_t kOob = 0x80000000u;  // an offset outside every resource: reads return zero
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// the same for a buffer-load result
+__device__ __forceinline__ h8 act_operand(u32x4 v) {
+  const uint32_t x[4] = {v.x, v.y, v.z, v.w};
+  uint32_t o[4];
+  perm8_words(x, o);
+  return __builtin_bit_cast(h8, make_uint4(o[0], o[1], o[2], o[3]));
+}
+
+// raw (stride 0) resource; the config word selects 32-bit data format (gfx9).
+// Base and size must be workgroup-uniform: they are moved to scalar registers
+// here, so the compiler never wraps a load in a per-lane resource loop.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  const uint64_t b = reinterpret_cast<uint64_t>(base);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)b), hi = __builtin_amdgcn_readfirstlane((uint32_t)(b >> 32));
+  void* ub = reinterpret_cast<void*>(((uint64_t)hi << 32) | lo);
+  return __builtin_amdgcn_make_buffer_rsrc(ub, (short)0, (int)__builtin_amdgcn_readfirstlane(bytes), 0x00020000);
+}
+
+// ---------------------------------------------------------------------------
 // 1. router GEMM: 32 tokens x 32 rows per workgroup; the four waves take
 //    interleaved 64-groups of K and are summed through LDS.  The scales are
 //    applied per group to fp32 partial sums, so routing sees logits accurate to
@@ -56,26 +84,29 @@ __global__ __launch_bounds__(256) void router_gemm_kernel(ChunkArgs a) {
   const int t = blockIdx.x * 32 + m;  // A row (token)
   const int r = blockIdx.y * 32 + m;  // B row (router row)
   const int nrows = a.E + 1, H = a.H, ngr = H / kGroup;
-  const _Float16* xrow = t < a.T ? reinterpret_cast<const _Float16*>(a.x) + (size_t)t * H : nullptr;
-  const int8_t* rrow = r < nrows ? a.router_q + (size_t)r * H : nullptr;
+  const __amdgpu_buffer_rsrc_t rx = make_rsrc(a.x, (uint32_t)a.T * H * 2u);
+  const __amdgpu_buffer_rsrc_t rq = make_rsrc(a.router_q, (uint32_t)nrows * H);
+  const __amdgpu_buffer_rsrc_t rs = make_rsrc(a.router_s, (uint32_t)nrows * ngr * 2u);
+  const uint32_t xoff = t < a.T ? (uint32_t)t * H * 2u + 64u * g : kOob;  // lane's 32-half slice of a group
+  const uint32_t qoff = r < nrows ? (uint32_t)r * H + 32u * g : kOob;
+  const uint32_t soff = r < nrows ? (uint32_t)r * ngr * 2u : kOob;
   f16v acc = {};
   constexpr int BATCH = 4;
   for (int g0 = wave; g0 < ngr; g0 += 4 * BATCH) {
-    uint4 xa[BATCH][4], wb[BATCH][2];
-    float sc[BATCH];
+    u32x4 xa[BATCH][4], wb[BATCH][2];
+    uint16_t sc[BATCH];
 #pragma unroll
     for (int u = 0; u < BATCH; ++u) {
       const int gi = g0 + 4 * u;
-      const bool ok = gi < ngr;
-      const int k0 = gi * kGroup + 32 * g;
+      const bool ok = gi < ngr;  // uniform
+      const uint32_t kx = ok ? 128u * gi : kOob, kq = ok ? 64u * gi : kOob, ks = ok ? 2u * gi : kOob;
 #pragma unroll
-      for (int q = 0; q < 4; ++q)
-        xa[u][q] = (ok && xrow) ? reinterpret_cast<const uint4*>(xrow + k0)[q] : make_uint4(0, 0, 0, 0);
+      for (int q = 0; q < 4; ++q) xa[u][q] = __builtin_amdgcn_raw_buffer_load_b128(rx, xoff + kx + 16u * q, 0, 0);
 #pragma unroll
-      for (int q = 0; q < 2; ++q)
-        wb[u][q] = (ok && rrow) ? reinterpret_cast<const uint4*>(rrow + k0)[q] : make_uint4(0, 0, 0, 0);
-      sc[u] = (ok && rrow) ? half_bits_to_float(a.router_s[(size_t)r * ngr + gi]) : 0.f;
+      for (int q = 0; q < 2; ++q) wb[u][q] = __builtin_amdgcn_raw_buffer_load_b128(rq, qoff + kq + 16u * q, 0, 0);
+      sc[u] = __builtin_amdgcn_raw_buffer_load_b16(rs, soff + ks, 0, 0);
     }
+    __builtin_amdgcn_sched_barrier(0);  // the whole batch in flight before any use
 #pragma unroll
     for (int u = 0; u < BATCH; ++u) {
       f16v p = {};
@@ -87,8 +118,9 @@ __global__ __launch_bounds__(256) void router_gemm_kernel(ChunkArgs a) {
         int8x8_to_h2x4(ws[2 * s], ws[2 * s + 1], w);
         p = __builtin_amdgcn_mfma_f32_32x32x16_f16(act_operand(xa[u][s]), pack8(w), p, 0, 0, 0);
       }
+      const float scf = half_bits_to_float(sc[u]);
 #pragma unroll
-      for (int i = 0; i < 16; ++i) acc[i] = fmaf(p[i], sc[u], acc[i]);
+      for (int i = 0; i < 16; ++i) acc[i] = fmaf(p[i], scf, acc[i]);
     }
   }
 #pragma unroll
@@ -116,16 +148,19 @@ __global__ __launch_bounds__(256) void topk_kernel(ChunkArgs a) {
   if (t >= a.T) return;  // whole waves: no workgroup barrier below
   const int nrows = a.E + 1;
   const float* lg = a.logits + (size_t)t * nrows;
+  // all loads issued before any use (clamped indices: entries past E are
+  // ignored by the ranking)
+  const float gate = lg[a.E];
   float v[4];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) v[j] = 4 * lane + j < a.E ? lg[4 * lane + j] : 0.f;
+  for (int j = 0; j < 4; ++j) v[j] = lg[min(4 * lane + j, a.E)];
   wave_topk(v, a.E, a.k, ids[wave], w[wave], sc[wave]);
   __builtin_amdgcn_wave_barrier();
   if (lane < a.k) {
     a.ids[(size_t)t * a.k + lane] = ids[wave][lane];
     a.wts[(size_t)t * a.k + lane] = w[wave][lane];
   }
-  if (lane == 0) a.sigma[t] = sigmoid_f(lg[a.E]);
+  if (lane == 0) a.sigma[t] = sigmoid_f(gate);
 }
 
 // ---------------------------------------------------------------------------
@@ -165,13 +200,22 @@ __global__ __launch_bounds__(1024) void bucket_kernel(ChunkArgs a) {
 
   for (int i = threadIdx.x; i < 16 * (kMaxExperts + 1); i += blockDim.x) (&hist[0][0])[i] = 0;
   __syncthreads();
-  // per-wave histograms (ids outside [0, E) are dropped: they never index weights)
-  for (int p0 = p_begin; p0 < p_end; p0 += 64) {
-    const int p = p0 + lane;
-    const int e = p < p_end ? a.ids[p] : -1;
-    const bool ok = e >= 0 && e < E;
-    const uint64_t pe = peers_of(ok ? e : 255) & __ballot(ok);
-    if (ok && (pe & lt) == 0) hist[wave][e] += __popcll(pe);  // one leader per expert
+  // per-wave histograms (ids outside [0, E) are dropped: they never index
+  // weights).  Ids are loaded kBatch rounds at a time with clamped (always
+  // valid) indices, so the loads are in flight together.
+  constexpr int kBatch = 4;
+  for (int p0 = p_begin; p0 < p_end; p0 += 64 * kBatch) {
+    int ev[kBatch];
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) ev[u] = a.ids[min(p0 + 64 * u + lane, P - 1)];
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      const int p = p0 + 64 * u + lane;
+      const int e = p < p_end ? ev[u] : -1;
+      const bool ok = e >= 0 && e < E;
+      const uint64_t pe = peers_of(ok ? e : 255) & __ballot(ok);
+      if (ok && (pe & lt) == 0) hist[wave][e] += __popcll(pe);  // one leader per expert
+    }
   }
   __syncthreads();
   if (threadIdx.x < kMaxExperts + 1) {
@@ -223,19 +267,25 @@ __global__ __launch_bounds__(1024) void bucket_kernel(ChunkArgs a) {
     }
   }
   // stable scatter: position of pair p in expert-major order
-  for (int p0 = p_begin; p0 < p_end; p0 += 64) {
-    const int p = p0 + lane;
-    const int e = p < p_end ? a.ids[p] : -1;
-    const bool ok = e >= 0 && e < E;
-    const uint64_t pe = peers_of(ok ? e : 255) & __ballot(ok);
-    if (ok) {
-      const int pos = s_off[e] + hist[wave][e] + __popcll(pe & lt);
-      a.sorted_pair[pos] = p;
-      a.pos_of_pair[p] = pos;
-    } else if (p < p_end) {
-      a.pos_of_pair[p] = -1;
+  for (int p0 = p_begin; p0 < p_end; p0 += 64 * kBatch) {
+    int ev[kBatch];
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) ev[u] = a.ids[min(p0 + 64 * u + lane, P - 1)];
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      const int p = p0 + 64 * u + lane;
+      const int e = p < p_end ? ev[u] : -1;
+      const bool ok = e >= 0 && e < E;
+      const uint64_t pe = peers_of(ok ? e : 255) & __ballot(ok);
+      if (ok) {
+        const int pos = s_off[e] + hist[wave][e] + __popcll(pe & lt);
+        a.sorted_pair[pos] = p;
+        a.pos_of_pair[p] = pos;
+      } else if (p < p_end) {
+        a.pos_of_pair[p] = -1;
+      }
+      if (ok && (pe & lt) == 0) hist[wave][e] += __popcll(pe);
     }
-    if (ok && (pe & lt) == 0) hist[wave][e] += __popcll(pe);
   }
 }
 
@@ -255,27 +305,6 @@ __global__ __launch_bounds__(1024) void bucket_kernel(ChunkArgs a) {
 // ---------------------------------------------------------------------------
 static constexpr int kKS = 128;
 static constexpr int kAStride = kKS + 8;       // halves per LDS row (padding against bank conflicts)
-static constexpr uint32_t kOob = 0x80000000u;  // an offset outside every resource: reads return zero
-
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-
-// raw (stride 0) resource; the config word selects 32-bit data format (gfx9).
-// Base and size must be workgroup-uniform: they are moved to scalar registers
-// here, so the compiler never wraps a load in a per-lane resource loop.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
-  const uint64_t b = reinterpret_cast<uint64_t>(base);
-  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)b), hi = __builtin_amdgcn_readfirstlane((uint32_t)(b >> 32));
-  void* ub = reinterpret_cast<void*>(((uint64_t)hi << 32) | lo);
-  return __builtin_amdgcn_make_buffer_rsrc(ub, (short)0, (int)__builtin_amdgcn_readfirstlane(bytes), 0x00020000);
-}
-
-// the same for a buffer-load result
-__device__ __forceinline__ h8 act_operand(u32x4 v) {
-  const uint32_t x[4] = {v.x, v.y, v.z, v.w};
-  uint32_t o[4];
-  perm8_words(x, o);
-  return __builtin_bit_cast(h8, make_uint4(o[0], o[1], o[2], o[3]));
-}
 
 template <int MT>
 struct AStage {
