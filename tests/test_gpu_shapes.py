@@ -1,0 +1,97 @@
+"""Parity at other admitted widths, exact router ties and the path boundary.
+
+Same bar as test_gpu_parity: ids exact as sets off the near-tie rows, per-row
+relative L2 <= 2e-3 against the float64 oracle.  The exact-tie tests add an
+unexempted check: when two experts' router rows are identical, their logits
+are bit-identical on both sides, and the lower expert index must win the
+k-th place (the tie rule the oracle and the kernels share).
+"""
+from __future__ import annotations
+
+import dataclasses
+
+import numpy as np
+import pytest
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+import w4a16_routed_experts_amd as m  # noqa: E402
+from oracle import ref  # noqa: E402
+from tests import _gpu  # noqa: E402
+from workloads import gen  # noqa: E402
+from workloads.gen import Case, Dims  # noqa: E402
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _device():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    m.lib()  # raises if the library is missing
+
+
+# (H, E, k, I, Is): every width is 64 * 2^m or a multiple of 2048
+SHAPES = [
+    (512, 32, 4, 128, 256),
+    (1024, 128, 6, 256, 1024),
+    (4096, 64, 8, 1024, 128),
+]
+
+
+@pytest.mark.parametrize("shape", SHAPES, ids=lambda s: "H{}E{}k{}I{}Is{}".format(*s))
+@pytest.mark.parametrize("T,flags", [(1, m.PATH_AUTO), (3, m.PATH_DECODE), (0, m.PATH_AUTO), (2, m.PATH_CHUNK)])
+def test_other_widths(shape, T, flags):
+    H, E, k, I, Is = shape
+    if T == 0:  # a multi-token chunk, kept small where the float64 oracle is slow
+        T = 10 if H >= 4096 else 24
+    d = Dims(H=H, E=E, k=k, I=I, Is=Is)
+    case = gen.make_case(d, T, seed=3000 + H + E + T)
+    _gpu.log(f"shape {shape} T={T} flags={flags}")
+    r = ref.forward(case.x, case.weights, d)
+    g = _gpu.run_forward(case, flags=flags)
+    _gpu.check_forward(case, r, g, f"{shape}-T{T}-f{flags}")
+
+
+def _tie_case(base: Case, token: int = 0):
+    """Give token `token`'s (k+1)-th expert the router row of its k-th expert,
+    so the two boundary experts' logits tie exactly for every token."""
+    d = base.dims
+    r = ref.route(base.x, base.weights, d)
+    order = np.lexsort((np.arange(d.E), -r["logits"][token, : d.E]))
+    a, b = int(order[d.k - 1]), int(order[d.k])  # k-th and (k+1)-th
+    rq = base.weights.router_q.copy()
+    rs = base.weights.router_s.copy()
+    rq[b] = rq[a]
+    rs[b] = rs[a]
+    W = dataclasses.replace(base.weights, router_q=rq, router_s=rs)
+    return Case(name=base.name + "_tie", dims=d, weights=W, x=base.x, meta=dict(base.meta)), a, b
+
+
+@pytest.mark.parametrize("T,flags", [(1, m.PATH_AUTO), (1, m.PATH_CHUNK), (40, m.PATH_AUTO)])
+def test_exact_tie_takes_lower_index(T, flags):
+    base = gen.make_case(gen.REAL, T, seed=4000 + T, real_experts=True)
+    case, a, b = _tie_case(base)
+    d = case.dims
+    r = ref.forward(case.x, case.weights, d)
+    lg = r["logits"][0, : d.E]
+    assert lg[a] == lg[b], "the copied rows must tie exactly in float64"
+    assert r["gap"][0] == 0.0
+    winner, loser = min(a, b), max(a, b)
+    assert winner in r["ids"][0] and loser not in r["ids"][0]
+    _gpu.log(f"exact tie T={T} flags={flags}: experts {a} and {b}, lower index {winner} must be kept")
+    g = _gpu.run_forward(case, flags=flags)
+    assert set(g["ids"][0].tolist()) == set(r["ids"][0].tolist()), (sorted(g["ids"][0]), sorted(r["ids"][0]))
+    _gpu.check_forward(case, r, g, f"tie-T{T}-f{flags}")
+    # moe_route ranks the same way
+    rr = _gpu.run_route(case, flags=flags)
+    assert set(rr["ids"][0].tolist()) == set(r["ids"][0].tolist())
+
+
+@pytest.mark.parametrize("T", [4, 5])
+def test_path_boundary(T):
+    """T = 4 is the last size the single-launch path takes on its own, T = 5 the first grouped-GEMM one."""
+    case = gen.make_case(gen.REAL, T, seed=5000 + T, real_experts=True)
+    r = ref.forward(case.x, case.weights, case.dims)
+    g = _gpu.run_forward(case, flags=m.PATH_AUTO)
+    _gpu.check_forward(case, r, g, f"boundary-T{T}")
