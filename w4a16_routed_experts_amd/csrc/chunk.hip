@@ -333,37 +333,66 @@ template <int BITS, int NF>
 struct BStage {
   static constexpr int Q = BITS == 4 ? 1 : 2;  // 16-byte loads per lane per group
   u32x4 q[2][NF][Q];
-  uint16_t s[2][NF];  // raw binary16 scales of the stage's two groups
-  // qoff: byte offset of the lane's K slice in its weight row; soff: byte
-  // offset of the row's scales (kOob for a masked row).  kb: first K of the
-  // stage; live = false turns every load into an out-of-range one.
-  __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t rq, __amdgpu_buffer_rsrc_t rs, const uint32_t qoff[NF],
-                                       const uint32_t soff[NF], int kb, bool live) {
+  // qoff: byte offset of the lane's K slice in its weight row (kOob for a
+  // masked row).  kb: first K of the stage; live = false turns every load into
+  // an out-of-range one.
+  __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t rq, const uint32_t qoff[NF], int kb, bool live) {
     const uint32_t qk = live ? (uint32_t)kb * BITS / 8 : kOob;
-    const uint32_t sk = live ? 2u * (kb / kGroup) : kOob;
 #pragma unroll
     for (int gi = 0; gi < 2; ++gi)
 #pragma unroll
-      for (int f = 0; f < NF; ++f) {
+      for (int f = 0; f < NF; ++f)
 #pragma unroll
         for (int j = 0; j < Q; ++j)
           q[gi][f][j] = __builtin_amdgcn_raw_buffer_load_b128(rq, qoff[f] + qk + (uint32_t)(kGroup * gi * BITS / 8 + 16 * j), 0, 0);
-        s[gi][f] = __builtin_amdgcn_raw_buffer_load_b16(rs, soff[f] + sk + 2u * gi, 0, 0);
-      }
   }
-  // MFMA operand for step st of group gi, fragment f, scale applied
-  __device__ __forceinline__ h8 operand(int gi, int f, int st) const {
+  // MFMA operand for step st of group gi, fragment f; sw holds the binary16
+  // scales of the stage's two groups (group gi in half gi)
+  __device__ __forceinline__ h8 operand(int gi, int f, int st, uint32_t sw) const {
     h2 w[4];
     if (BITS == 4) {
       int4x8_to_h2x4(q[gi][f][0][st], w);
     } else {
       int8x8_to_h2x4(q[gi][f][st >> 1][2 * (st & 1)], q[gi][f][st >> 1][2 * (st & 1) + 1], w);
     }
-    const uint32_t sb = s[gi][f];
-    const h2 sc = as_h2(sb | (sb << 16));
+    const h2 sc = as_h2(__builtin_amdgcn_perm(sw, sw, gi ? 0x07060706u : 0x05040504u));
 #pragma unroll
     for (int i = 0; i < 4; ++i) w[i] *= sc;
     return pack8(w);
+  }
+};
+
+// Scales of 8 consecutive groups (4 stages) of each fragment's weight row: one
+// 16-byte load per fragment every 4 stages, instead of one 2-byte load per
+// group and fragment.  Word j covers stage j of the block.
+template <int NF>
+struct ScaleBlock {
+  u32x4 v[NF];
+  // soff: byte offset of the row's scales (kOob for a masked row); blk: block
+  // index (8 groups); live = false reads zeros.  Only for rows of at least 8
+  // groups, so the 16 bytes lie inside the row and are 16-byte aligned in it.
+  __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t rs, const uint32_t soff[NF], int blk, bool live) {
+    const uint32_t sk = live ? 16u * blk : kOob;
+#pragma unroll
+    for (int f = 0; f < NF; ++f) v[f] = __builtin_amdgcn_raw_buffer_load_b128(rs, soff[f] + sk, 0, 0);
+  }
+  // first block of a row of ng groups: a row shorter than 8 groups (ng = 1, 2
+  // or 4) is read with a load of its own size, so no load reaches past the
+  // row (or past the end of the tensor for the last row)
+  __device__ __forceinline__ void load_first(__amdgpu_buffer_rsrc_t rs, const uint32_t soff[NF], int ng) {
+#pragma unroll
+    for (int f = 0; f < NF; ++f) {
+      if (ng >= 8) {
+        v[f] = __builtin_amdgcn_raw_buffer_load_b128(rs, soff[f], 0, 0);
+      } else if (ng == 4) {
+        const auto d = __builtin_amdgcn_raw_buffer_load_b64(rs, soff[f], 0, 0);
+        v[f] = u32x4{d[0], d[1], 0u, 0u};
+      } else if (ng == 2) {
+        v[f] = u32x4{__builtin_amdgcn_raw_buffer_load_b32(rs, soff[f], 0, 0), 0u, 0u, 0u};
+      } else {
+        v[f] = u32x4{(uint32_t)__builtin_amdgcn_raw_buffer_load_b16(rs, soff[f], 0, 0), 0u, 0u, 0u};
+      }
+    }
   }
 };
 
@@ -377,8 +406,8 @@ struct GemmOperands {
 };
 
 template <int BITS, int NF, int MT>
-__device__ __forceinline__ void stage_mfma(const _Float16* L, const BStage<BITS, NF>& b, int kb, int K,
-                                           f16v acc[MT][NF]) {
+__device__ __forceinline__ void stage_mfma(const _Float16* L, const BStage<BITS, NF>& b, const uint32_t sw[NF], int kb,
+                                           int K, f16v acc[MT][NF]) {
   const int lane = threadIdx.x & 63;
   const int m = lane & 31, g = lane >> 5;
 #pragma unroll
@@ -392,7 +421,7 @@ __device__ __forceinline__ void stage_mfma(const _Float16* L, const BStage<BITS,
           av[mt] = *reinterpret_cast<const h8*>(L + (32 * mt + m) * kAStride + kGroup * gi + 32 * g + 8 * s);
 #pragma unroll
         for (int f = 0; f < NF; ++f) {
-          const h8 bv = b.operand(gi, f, s);
+          const h8 bv = b.operand(gi, f, s, sw[f]);
 #pragma unroll
           for (int mt = 0; mt < MT; ++mt)
             acc[mt][f] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av[mt], bv, acc[mt][f], 0, 0, 0);
@@ -409,38 +438,41 @@ __device__ __forceinline__ void tile_gemm(_Float16* lds, const GemmOperands<BITS
   const int nst = (K + kKS - 1) / kKS;
   AStage<MT> as;
   BStage<BITS, NF> b0, b1;
+  ScaleBlock<NF> sc, scn;
   as.load(op.ra, op.aoff, 0);
-  b0.load(op.rq, op.rs, op.qoff, op.soff, 0, true);
+  b0.load(op.rq, op.qoff, 0, true);
+  sc.load_first(op.rs, op.soff, K / kGroup);
   as.store(lds);
   __syncthreads();
-  // Two stages per iteration, so the register stages swap roles without
-  // copies.  The next stage's loads are issued unconditionally (out of range
-  // past the last stage): loads issued on one path only would make the
+  // Four stages per iteration: the register stages swap roles without copies
+  // and each iteration uses one scale block, whose successor is loaded with
+  // the last stage's prefetch.  The next stage's loads are issued unconditionally (out of
+  // range past the last stage): loads issued on one path only would make the
   // compiler drain the load queue where the paths join.
-  for (int st = 0; st < nst; st += 2) {
-    {
-      const int kb = st * kKS;
-      const bool more = st + 1 < nst;
-      as.load(op.ra, op.aoff, more ? 2u * (kb + kKS) : kOob);
-      b1.load(op.rq, op.rs, op.qoff, op.soff, kb + kKS, more);
-      // keep the next stage's loads ahead of this stage's arithmetic
-      __builtin_amdgcn_sched_barrier(0);
-      stage_mfma<BITS, NF, MT>(lds, b0, kb, K, acc);
-      as.store(lds + BUF);
-      __syncthreads();
-      if (!more) break;
-    }
-    {
-      const int kb = (st + 1) * kKS;
-      const bool more = st + 2 < nst;
-      as.load(op.ra, op.aoff, more ? 2u * (kb + kKS) : kOob);
-      b0.load(op.rq, op.rs, op.qoff, op.soff, kb + kKS, more);
-      __builtin_amdgcn_sched_barrier(0);
-      stage_mfma<BITS, NF, MT>(lds + BUF, b1, kb, K, acc);
-      as.store(lds);
-      __syncthreads();
-    }
+#define MOE_TILE_STAGE(J, BC, BN, LC, LN)                                      \
+  {                                                                            \
+    const int kb = (st + J) * kKS;                                             \
+    const bool more = st + J + 1 < nst;                                        \
+    as.load(op.ra, op.aoff, more ? 2u * (kb + kKS) : kOob);                    \
+    BN.load(op.rq, op.qoff, kb + kKS, more);                                   \
+    if (J == 3) scn.load(op.rs, op.soff, st / 4 + 1, st + 4 < nst);            \
+    /* keep the next stage's loads ahead of this stage's arithmetic */         \
+    __builtin_amdgcn_sched_barrier(0);                                         \
+    uint32_t sw[NF];                                                           \
+    _Pragma("unroll") for (int f = 0; f < NF; ++f) sw[f] = sc.v[f][J];         \
+    stage_mfma<BITS, NF, MT>(LC, BC, sw, kb, K, acc);                          \
+    as.store(LN);                                                              \
+    __syncthreads();                                                           \
+    if (!more) break;                                                          \
   }
+  for (int st = 0; st < nst; st += 4) {
+    MOE_TILE_STAGE(0, b0, b1, lds, lds + BUF)
+    MOE_TILE_STAGE(1, b1, b0, lds + BUF, lds)
+    MOE_TILE_STAGE(2, b0, b1, lds, lds + BUF)
+    MOE_TILE_STAGE(3, b1, b0, lds + BUF, lds)
+    sc = scn;
+  }
+#undef MOE_TILE_STAGE
 }
 
 // LDS of one GEMM workgroup: two A buffers of kTileRows rows
