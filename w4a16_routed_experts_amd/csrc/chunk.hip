@@ -170,7 +170,8 @@ __global__ __launch_bounds__(256) void topk_kernel(ChunkArgs a) {
 // wave owns a contiguous run of pairs; ranks inside a 64-pair batch come from
 // ballots over the 8 bits of the expert id.  Each expert's rows are cut into
 // kTileRows-row tiles and one last tile of 1..kTileRows rows, which uses only
-// as many 32-row MFMA blocks as it needs.
+// as many 32-row MFMA blocks as it needs (or the narrow path, for at most
+// kNarrowRows rows).
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ uint64_t peers_of(int e) {
   uint64_t peers = ~0ull;
@@ -184,7 +185,10 @@ __device__ __forceinline__ uint64_t peers_of(int e) {
 
 __device__ __forceinline__ int tiles_for(int c) { return (c + kTileRows - 1) / kTileRows; }
 
-__device__ __forceinline__ int4 make_tile(int e, int r0, int rows) { return make_int4(e, r0, rows, (rows + 31) / 32); }
+// the tile's MFMA row blocks of 32; 0 marks a narrow tile (at most kNarrowRows rows)
+__device__ __forceinline__ int4 make_tile(int e, int r0, int rows) {
+  return make_int4(e, r0, rows, rows <= kNarrowRows ? 0 : (rows + 31) / 32);
+}
 
 __global__ __launch_bounds__(1024) void bucket_kernel(ChunkArgs a) {
   __shared__ int hist[16][kMaxExperts + 1];  // per-wave counts, then per-wave bases
@@ -305,6 +309,7 @@ __global__ __launch_bounds__(1024) void bucket_kernel(ChunkArgs a) {
 // ---------------------------------------------------------------------------
 static constexpr int kKS = 128;
 static constexpr int kAStride = kKS + 8;       // halves per LDS row (padding against bank conflicts)
+static constexpr int kTilePF = 1;              // weight stages in flight in the 32-row-block path
 
 template <int MT>
 struct AStage {
@@ -435,48 +440,55 @@ template <int BITS, int NF, int MT>
 __device__ __forceinline__ void tile_gemm(_Float16* lds, const GemmOperands<BITS, NF, MT>& op, int K,
                                           f16v acc[MT][NF]) {
   constexpr int BUF = 32 * MT * kAStride;
+  constexpr int PF = kTilePF;  // weight stages in flight
+  static_assert(PF >= 1 && PF <= 3, "the stage ring holds four stages");
   const int nst = (K + kKS - 1) / kKS;
   AStage<MT> as;
-  BStage<BITS, NF> b0, b1;
+  BStage<BITS, NF> b[4];
   ScaleBlock<NF> sc, scn;
   as.load(op.ra, op.aoff, 0);
-  b0.load(op.rq, op.qoff, 0, true);
+#pragma unroll
+  for (int i = 0; i < PF; ++i) b[i].load(op.rq, op.qoff, i * kKS, i < nst);
   sc.load_first(op.rs, op.soff, K / kGroup);
   as.store(lds);
   __syncthreads();
-  // Four stages per iteration: the register stages swap roles without copies
-  // and each iteration uses one scale block, whose successor is loaded with
-  // the last stage's prefetch.  The next stage's loads are issued unconditionally (out of
+  // Four stages per iteration: stage s multiplies ring slot s % 4 and loads
+  // the weights of stage s + PF into slot (s + PF) % 4; each iteration uses
+  // one scale block, whose successor is loaded with the last stage's
+  // prefetch.  The next stage's loads are issued unconditionally (out of
   // range past the last stage): loads issued on one path only would make the
   // compiler drain the load queue where the paths join.
-#define MOE_TILE_STAGE(J, BC, BN, LC, LN)                                      \
+#define MOE_TILE_STAGE(J, LC, LN)                                              \
   {                                                                            \
     const int kb = (st + J) * kKS;                                             \
     const bool more = st + J + 1 < nst;                                        \
     as.load(op.ra, op.aoff, more ? 2u * (kb + kKS) : kOob);                    \
-    BN.load(op.rq, op.qoff, kb + kKS, more);                                   \
+    b[(J + PF) & 3].load(op.rq, op.qoff, kb + PF * kKS, st + J + PF < nst);   \
     if (J == 3) scn.load(op.rs, op.soff, st / 4 + 1, st + 4 < nst);            \
     /* keep the next stage's loads ahead of this stage's arithmetic */         \
     __builtin_amdgcn_sched_barrier(0);                                         \
     uint32_t sw[NF];                                                           \
     _Pragma("unroll") for (int f = 0; f < NF; ++f) sw[f] = sc.v[f][J];         \
-    stage_mfma<BITS, NF, MT>(LC, BC, sw, kb, K, acc);                          \
+    stage_mfma<BITS, NF, MT>(LC, b[J], sw, kb, K, acc);                        \
     as.store(LN);                                                              \
     __syncthreads();                                                           \
     if (!more) break;                                                          \
   }
   for (int st = 0; st < nst; st += 4) {
-    MOE_TILE_STAGE(0, b0, b1, lds, lds + BUF)
-    MOE_TILE_STAGE(1, b1, b0, lds + BUF, lds)
-    MOE_TILE_STAGE(2, b0, b1, lds, lds + BUF)
-    MOE_TILE_STAGE(3, b1, b0, lds + BUF, lds)
+    MOE_TILE_STAGE(0, lds, lds + BUF)
+    MOE_TILE_STAGE(1, lds + BUF, lds)
+    MOE_TILE_STAGE(2, lds, lds + BUF)
+    MOE_TILE_STAGE(3, lds + BUF, lds)
     sc = scn;
   }
 #undef MOE_TILE_STAGE
 }
 
-// LDS of one GEMM workgroup: two A buffers of kTileRows rows
-static constexpr int kGemmLds = 2 * kTileRows * kAStride;
+// LDS of one GEMM workgroup: two A buffers of kTileRows rows, or the rows
+// of a narrow tile for the whole K (below)
+static constexpr int kNarrowStride = kNarrowK + 8;  // halves per LDS row of a narrow tile
+static constexpr int kGemmLds = 2 * kTileRows * kAStride > kNarrowRows * kNarrowStride
+                                    ? 2 * kTileRows * kAStride : kNarrowRows * kNarrowStride;
 
 struct TileRows {
   uint32_t aoff[kTileRows];  // byte offset of each A row in its resource (kOob: zero row)
@@ -488,6 +500,140 @@ template <int BITS, int NF, int MT>
 __device__ __forceinline__ void set_a_offsets(GemmOperands<BITS, NF, MT>& op, const TileRows& tr) {
 #pragma unroll
   for (int i = 0; i < AStage<MT>::N; ++i) op.aoff[i] = tr.aoff[((int)threadIdx.x + 256 * i) / AStage<MT>::CH];
+}
+
+// ---------------------------------------------------------------------------
+// Narrow tiles (at most kNarrowRows rows, K a power of two in [kNarrowMinK,
+// kNarrowK]): the tile's
+// activation rows stay in LDS for the whole K, and each wave streams its own
+// weight rows kNarrowPF stages ahead with no workgroup barrier inside the K
+// loop.  MFMA 16x16x32 f16: lane l = 16q + n works on row n of each 16-row
+// operand, and in MFMA step t of a 128-K stage on K = 32q + 8t .. +8 (the
+// same for activations and weights, so the products pair up).  A lane's int4
+// weights of one stage are then 16 contiguous bytes of its row: one load per
+// fragment and stage, four lanes per 64-byte run of a row.  Accumulator
+// element i of lane l is row 4q + i, column n.
+// ---------------------------------------------------------------------------
+static constexpr int kNarrowMinK = 512;             // one scale block per row at least
+static constexpr int kNarrowPF = 2;                  // weight stages in flight
+
+// the tile's activation rows for K in [0, 128 N): N 16-byte chunks per thread
+template <int N>
+struct NarrowA {
+  u32x4 v[N];
+  __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t ra, const uint32_t* aoff, int K) {
+    constexpr int CPR = N * 256 / kNarrowRows;  // 16-byte chunks per row
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+      const int c = (int)threadIdx.x + 256 * i;
+      const int row = c / CPR, col = c % CPR;
+      v[i] = __builtin_amdgcn_raw_buffer_load_b128(ra, 8 * col < K ? aoff[row] + 16u * col : kOob, 0, 0);
+    }
+  }
+  __device__ __forceinline__ void store(_Float16* lds) const {
+    constexpr int CPR = N * 256 / kNarrowRows;
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+      const int c = (int)threadIdx.x + 256 * i;
+      *reinterpret_cast<h8*>(lds + (c / CPR) * kNarrowStride + 8 * (c % CPR)) = act_operand(v[i]);
+    }
+  }
+};
+
+// One stage of int4 weights: 16 bytes (32 K) per lane and fragment.  The
+// loads are coalesced (lane l reads part l % 4 of row l / 4 of the
+// fragment's 64-byte stage run, so four neighbouring lanes cover one run) and
+// the bytes are then moved to the MFMA lane (row l % 16, part l / 16) with a
+// cross-lane permute: neighbouring lanes reading different rows would make
+// the texture addresser take the lanes one by one.
+template <int NF>
+struct NarrowB {
+  u32x4 q[NF];
+  __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t rq, const uint32_t qoff[NF], int st, bool live) {
+    const uint32_t k = live ? 64u * st : kOob;
+#pragma unroll
+    for (int f = 0; f < NF; ++f) q[f] = __builtin_amdgcn_raw_buffer_load_b128(rq, qoff[f] + k, 0, 0);
+  }
+};
+
+// the 16 bytes that the coalesced load gave lane 4 (l % 16) + l / 16, in lane l
+__device__ __forceinline__ u32x4 to_mfma_lanes(u32x4 v, int src_byte) {
+  u32x4 r;
+  r.x = (uint32_t)__builtin_amdgcn_ds_bpermute(src_byte, (int)v.x);
+  r.y = (uint32_t)__builtin_amdgcn_ds_bpermute(src_byte, (int)v.y);
+  r.z = (uint32_t)__builtin_amdgcn_ds_bpermute(src_byte, (int)v.z);
+  r.w = (uint32_t)__builtin_amdgcn_ds_bpermute(src_byte, (int)v.w);
+  return r;
+}
+
+template <int N, int NF>
+__device__ __forceinline__ void narrow_prologue(_Float16* lds, __amdgpu_buffer_rsrc_t ra, const uint32_t* aoff, int K,
+                                                __amdgpu_buffer_rsrc_t rq, __amdgpu_buffer_rsrc_t rs,
+                                                const uint32_t qoff[NF], const uint32_t soff[NF], NarrowB<NF> b[4],
+                                                ScaleBlock<NF>& sc, int nst) {
+  NarrowA<N> a;
+  a.load(ra, aoff, K);  // activations first: their store below waits for them alone
+  sc.load(rs, soff, 0, true);  // K >= 512: a whole block of 8 groups
+#pragma unroll
+  for (int i = 0; i < kNarrowPF; ++i) b[i].load(rq, qoff, i, i < nst);
+  a.store(lds);
+}
+
+// acc[f] += A[16][K] . W_f[16][K]^T for the wave's NF weight fragments
+template <int NF>
+__device__ __forceinline__ void narrow_gemm(_Float16* lds, __amdgpu_buffer_rsrc_t ra, const uint32_t* aoff, int K,
+                                            __amdgpu_buffer_rsrc_t rq, __amdgpu_buffer_rsrc_t rs,
+                                            const uint32_t qoff[NF], const uint32_t soff[NF], f4 acc[NF]) {
+  static_assert(kNarrowPF >= 1 && kNarrowPF <= 3, "the stage ring holds four stages");
+  const int lane = threadIdx.x & 63, n = lane & 15, q = lane >> 4;
+  const uint32_t ssel = (q & 2) ? 0x07060706u : 0x05040504u;  // the lane's group in the stage: half q/2 of a scale word
+  const int src_byte = 4 * (4 * n + q);                          // coalesced lane holding this lane's weights
+  const int nst = (K + kKS - 1) / kKS;
+  NarrowB<NF> b[4];
+  ScaleBlock<NF> sc, scn;
+  // K is a multiple of 512 here, so the K loop runs whole iterations of four
+  // stages with no exit inside one: every path into the loop head has issued
+  // the same loads, and the compiler's wait counts keep kNarrowPF stages in
+  // flight.
+  switch (nst) {
+    case 4: narrow_prologue<4, NF>(lds, ra, aoff, K, rq, rs, qoff, soff, b, sc, nst); break;
+    case 8: narrow_prologue<8, NF>(lds, ra, aoff, K, rq, rs, qoff, soff, b, sc, nst); break;
+    default: narrow_prologue<16, NF>(lds, ra, aoff, K, rq, rs, qoff, soff, b, sc, nst); break;
+  }
+  __syncthreads();
+  const _Float16* La = lds + n * kNarrowStride + 32 * q;
+  // Four stages per iteration (one scale block): stage s computes from ring
+  // slot s % 4 and loads stage s + kNarrowPF into slot (s + kNarrowPF) % 4.
+#define MOE_NARROW_STAGE(J)                                                                \
+  {                                                                                        \
+    const int s_ = st + J;                                                                 \
+    b[(J + kNarrowPF) & 3].load(rq, qoff, s_ + kNarrowPF, s_ + kNarrowPF < nst);           \
+    if (J == 0) scn.load(rs, soff, st / 4 + 1, st + 4 < nst);                              \
+    __builtin_amdgcn_sched_barrier(0);                                                     \
+    h2 scl[NF];                                                                            \
+    u32x4 bw[NF];                                                                          \
+    _Pragma("unroll") for (int f = 0; f < NF; ++f) {                                       \
+      scl[f] = as_h2(__builtin_amdgcn_perm(sc.v[f][J], sc.v[f][J], ssel));                 \
+      bw[f] = to_mfma_lanes(b[J].q[f], src_byte);                                          \
+    }                                                                                      \
+    _Pragma("unroll") for (int t = 0; t < 4; ++t) {                                        \
+      const h8 av = *reinterpret_cast<const h8*>(La + kKS * s_ + 8 * t);                  \
+      _Pragma("unroll") for (int f = 0; f < NF; ++f) {                                     \
+        h2 w[4];                                                                           \
+        int4x8_to_h2x4(bw[f][t], w);                                                       \
+        _Pragma("unroll") for (int i = 0; i < 4; ++i) w[i] *= scl[f];                      \
+        acc[f] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, pack8(w), acc[f], 0, 0, 0);    \
+      }                                                                                    \
+    }                                                                                      \
+  }
+  for (int st = 0; st < nst; st += 4) {
+    MOE_NARROW_STAGE(0)
+    MOE_NARROW_STAGE(1)
+    MOE_NARROW_STAGE(2)
+    MOE_NARROW_STAGE(3)
+    sc = scn;
+  }
+#undef MOE_NARROW_STAGE
 }
 
 // ---------------------------------------------------------------------------
@@ -540,6 +686,41 @@ __device__ __forceinline__ void up_tile(const ChunkArgs& a, _Float16* lds, const
     }
 }
 
+// a narrow routed tile: each wave takes 32 gate and the same 32 up columns as
+// four 16-column fragments (gate j0.., gate j0+16.., up j0.., up j0+16..)
+__device__ __forceinline__ void up_narrow(const ChunkArgs& a, _Float16* lds, const TileRows& tr,
+                                          __amdgpu_buffer_rsrc_t ra, const uint8_t* wq, const uint16_t* wsc, int inter,
+                                          int jb, _Float16* hout, int rows) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, n = lane & 15, q = lane >> 4;
+  const uint32_t rb = (uint32_t)a.H / 2;
+  const uint32_t ng = a.H / kGroup;
+  const __amdgpu_buffer_rsrc_t rq = make_rsrc(wq, 2u * inter * rb);
+  const __amdgpu_buffer_rsrc_t rs = make_rsrc(wsc, 2u * inter * ng * 2u);
+  const int j0 = jb * 128 + wave * 32;
+  uint32_t qoff[4], soff[4];
+#pragma unroll
+  for (int f = 0; f < 4; ++f) {
+    const int j = j0 + 16 * (f & 1) + n;              // the MFMA lane's column (scales)
+    const int jl = j0 + 16 * (f & 1) + (lane >> 2);   // the row this lane loads (weights)
+    qoff[f] = jl < inter ? (uint32_t)((f >> 1) * inter + jl) * rb + 16u * (lane & 3) : kOob;
+    soff[f] = j < inter ? (uint32_t)((f >> 1) * inter + j) * ng * 2u : kOob;
+  }
+  f4 acc[4];
+#pragma unroll
+  for (int f = 0; f < 4; ++f) acc[f] = f4{0.f, 0.f, 0.f, 0.f};
+  narrow_gemm<4>(lds, ra, tr.aoff, a.H, rq, rs, qoff, soff, acc);
+#pragma unroll
+  for (int ff = 0; ff < 2; ++ff) {
+    const int j = j0 + 16 * ff + n;
+    if (j >= inter) continue;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = 4 * q + i;
+      if (r < rows) hout[(size_t)tr.out_row[r] * inter + j] = (_Float16)(silu_f(acc[ff][i]) * acc[ff + 2][i]);
+    }
+  }
+}
+
 __global__ __launch_bounds__(256, 2) void up_gemm_kernel(ChunkArgs a) {
   __shared__ __attribute__((aligned(16))) _Float16 lds[kGemmLds];
   __shared__ TileRows tr;
@@ -581,6 +762,12 @@ __global__ __launch_bounds__(256, 2) void up_gemm_kernel(ChunkArgs a) {
       case 4: up_tile<4, 4>(a, lds, tr, ra, wq, wsc, a.I, jb, a.h, rows); break;
       case 3: up_tile<4, 3>(a, lds, tr, ra, wq, wsc, a.I, jb, a.h, rows); break;
       case 2: up_tile<4, 2>(a, lds, tr, ra, wq, wsc, a.I, jb, a.h, rows); break;
+      case 0:
+        if (a.H >= kNarrowMinK && a.H <= kNarrowK) {
+          up_narrow(a, lds, tr, ra, wq, wsc, a.I, jb, a.h, rows);
+          break;
+        }
+        [[fallthrough]];
       default: up_tile<4, 1>(a, lds, tr, ra, wq, wsc, a.I, jb, a.h, rows); break;
     }
   } else {
@@ -633,6 +820,39 @@ __device__ __forceinline__ void down_tile(const ChunkArgs& a, _Float16* lds, con
   }
 }
 
+// a narrow routed tile: each wave takes 64 outputs as four 16-column fragments
+__device__ __forceinline__ void down_narrow(const ChunkArgs& a, _Float16* lds, const TileRows& tr,
+                                            __amdgpu_buffer_rsrc_t ra, const uint8_t* wq, const uint16_t* wsc, int K,
+                                            int nb, _Float16* yout, int rows) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, n = lane & 15, q = lane >> 4;
+  const uint32_t rb = (uint32_t)K / 2;
+  const uint32_t ng = K / kGroup;
+  const __amdgpu_buffer_rsrc_t rq = make_rsrc(wq, (uint32_t)a.H * rb);
+  const __amdgpu_buffer_rsrc_t rs = make_rsrc(wsc, (uint32_t)a.H * ng * 2u);
+  int col[4];
+  uint32_t qoff[4], soff[4];
+#pragma unroll
+  for (int f = 0; f < 4; ++f) {
+    col[f] = nb * 256 + wave * 64 + 16 * f + n;             // the MFMA lane's column (scales, output)
+    const int cl = nb * 256 + wave * 64 + 16 * f + (lane >> 2);  // the row this lane loads (weights)
+    qoff[f] = cl < a.H ? (uint32_t)cl * rb + 16u * (lane & 3) : kOob;
+    soff[f] = col[f] < a.H ? (uint32_t)col[f] * ng * 2u : kOob;
+  }
+  f4 acc[4];
+#pragma unroll
+  for (int f = 0; f < 4; ++f) acc[f] = f4{0.f, 0.f, 0.f, 0.f};
+  narrow_gemm<4>(lds, ra, tr.aoff, K, rq, rs, qoff, soff, acc);
+#pragma unroll
+  for (int f = 0; f < 4; ++f) {
+    if (col[f] >= a.H) continue;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = 4 * q + i;
+      if (r < rows) yout[(size_t)tr.out_row[r] * a.H + col[f]] = (_Float16)(tr.scale[r] * acc[f][i]);
+    }
+  }
+}
+
 __global__ __launch_bounds__(256, 2) void down_gemm_kernel(ChunkArgs a) {
   __shared__ __attribute__((aligned(16))) _Float16 lds[kGemmLds];
   __shared__ TileRows tr;
@@ -677,6 +897,12 @@ __global__ __launch_bounds__(256, 2) void down_gemm_kernel(ChunkArgs a) {
       case 4: down_tile<4, 4>(a, lds, tr, ra, wq, wsc, a.I, nb, a.y, rows); break;
       case 3: down_tile<4, 3>(a, lds, tr, ra, wq, wsc, a.I, nb, a.y, rows); break;
       case 2: down_tile<4, 2>(a, lds, tr, ra, wq, wsc, a.I, nb, a.y, rows); break;
+      case 0:
+        if (a.I >= kNarrowMinK && a.I <= kNarrowK) {
+          down_narrow(a, lds, tr, ra, wq, wsc, a.I, nb, a.y, rows);
+          break;
+        }
+        [[fallthrough]];
       default: down_tile<4, 1>(a, lds, tr, ra, wq, wsc, a.I, nb, a.y, rows); break;
     }
   } else {

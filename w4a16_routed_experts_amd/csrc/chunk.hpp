@@ -6,6 +6,8 @@ namespace moe {
 
 static constexpr int kTileRows = 128;  // rows of a routed grouped-GEMM tile (4 MFMA row blocks of 32)
 static constexpr int kSharedRows = 64;  // rows of a shared-expert tile (int8 weights need more registers)
+static constexpr int kNarrowRows = 16;  // routed tiles of at most this many rows take the narrow path
+static constexpr int kNarrowK = 2048;   // ... when K is at most this (the tile's rows stay in LDS)
 
 struct ChunkArgs {
   int H, E, k, I, Is, T;
