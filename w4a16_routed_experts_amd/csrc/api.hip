@@ -109,7 +109,7 @@ void carve_chunk(const moe_dims* d, int T, Carve& c, ChunkArgs& a) {
   a.offsets = c.take<int32_t>((size_t)(d->num_experts + 1) * 4);
   a.sorted_pair = c.take<int32_t>(P * 4);
   a.pos_of_pair = c.take<int32_t>(P * 4);
-  a.tiles = c.take<int4>((size_t)max_route_tiles(d, T) * 16);
+  a.tiles = c.take<int4>((size_t)(max_route_tiles(d, T) + (T + kSharedRows - 1) / kSharedRows) * 16);
   a.n_tiles = c.take<int32_t>(4);
   a.h = c.take<_Float16>(P * d->expert_inter * 2);
   a.hs = c.take<_Float16>((size_t)T * d->shared_inter * 2);
@@ -293,8 +293,8 @@ MOE_API int moe_experts_w4a16(const moe_dims* dims, const moe_weights* w, const 
   ChunkArgs a = chunk_args(dims, w, x, T, out, ws);
   a.ids = const_cast<int32_t*>(ids);
   a.wts = const_cast<float*>(weights);
-  a.route_tiles = 1;
   a.shared_tiles = 0;
+  a.cus = di->cus;
   a.ys = nullptr;
   return launch_experts_chunk(a, stream);
 }
@@ -320,8 +320,8 @@ MOE_API int moe_forward(const moe_dims* dims, const moe_weights* w, const uint16
   if (ids) a.ids = ids;
   if (weights) a.wts = weights;
   if (shared_gate) a.sigma = shared_gate;
-  a.route_tiles = 1;
   a.shared_tiles = (T + kSharedRows - 1) / kSharedRows;
+  a.cus = di->cus;
   int r = launch_route_chunk(a, stream);
   if (r != MOE_OK) return r;
   return launch_experts_chunk(a, stream);

@@ -183,17 +183,23 @@ __device__ __forceinline__ uint64_t peers_of(int e) {
   return peers;
 }
 
-__device__ __forceinline__ int tiles_for(int c) { return (c + kTileRows - 1) / kTileRows; }
-
 // the tile's MFMA row blocks of 32; 0 marks a narrow tile (at most kNarrowRows rows)
 __device__ __forceinline__ int4 make_tile(int e, int r0, int rows) {
   return make_int4(e, r0, rows, rows <= kNarrowRows ? 0 : (rows + 31) / 32);
 }
 
+// shared-expert tile st: tokens st * kSharedRows .. (expert -1; never narrow)
+__device__ __forceinline__ int4 shared_tile(int st, int T) {
+  const int r0 = st * kSharedRows, rows = min(kSharedRows, T - r0);
+  return make_int4(-1, r0, rows, (rows + 31) / 32);
+}
+
+static constexpr int kTileClasses = kTileRows / 32 + 1;  // cost classes: 32-row blocks, 0 = narrow
+
 __global__ __launch_bounds__(1024) void bucket_kernel(ChunkArgs a) {
   __shared__ int hist[16][kMaxExperts + 1];  // per-wave counts, then per-wave bases
   __shared__ int s_off[kMaxExperts + 1];
-  __shared__ int s_tiles[kMaxExperts + 1];
+  __shared__ int s_cls[2][kTileClasses];  // tiles per cost class, then each class's next slot
   __shared__ int s_total;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int P = a.T * a.k;
@@ -203,6 +209,7 @@ __global__ __launch_bounds__(1024) void bucket_kernel(ChunkArgs a) {
   const uint64_t lt = (1ull << lane) - 1ull;
 
   for (int i = threadIdx.x; i < 16 * (kMaxExperts + 1); i += blockDim.x) (&hist[0][0])[i] = 0;
+  if (threadIdx.x < kTileClasses) s_cls[0][threadIdx.x] = 0;
   __syncthreads();
   // per-wave histograms (ids outside [0, E) are dropped: they never index
   // weights).  Ids are loaded kBatch rounds at a time with clamped (always
@@ -228,46 +235,65 @@ __global__ __launch_bounds__(1024) void bucket_kernel(ChunkArgs a) {
     if (e < E)
       for (int w = 0; w < 16; ++w) { const int c = hist[w][e]; hist[w][e] = tot; tot += c; }
     s_off[e] = e < E ? tot : 0;  // counts for now
-    s_tiles[e] = e < E ? tiles_for(tot) : 0;
+    if (e < E && tot > 0) {        // tiles per cost class: full tiles, then the last one
+      if (tot >= kTileRows) atomicAdd(&s_cls[0][kTileRows / 32], tot / kTileRows);
+      if (tot % kTileRows) atomicAdd(&s_cls[0][make_tile(e, 0, tot % kTileRows).w], 1);
+    }
   }
+  for (int st = threadIdx.x; st < a.shared_tiles; st += blockDim.x) atomicAdd(&s_cls[0][shared_tile(st, a.T).w], 1);
   __syncthreads();
-  if (wave == 0) {  // exclusive scans of counts and tile counts (E <= 256: 4 per lane)
-    int c[4], tl[4];
-    int sc = 0, st = 0;
+  if (wave == 0) {  // exclusive scan of counts (E <= 256: 4 per lane)
+    int c[4];
+    int sc = 0;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int e = 4 * lane + j;
       c[j] = e < E ? s_off[e] : 0;
-      tl[j] = e < E ? s_tiles[e] : 0;
       sc += c[j];
-      st += tl[j];
     }
-    int ic = sc, it = st;
+    int ic = sc;
     for (int d = 1; d < 64; d <<= 1) {
-      const int uc = __shfl_up(ic, d, 64), ut = __shfl_up(it, d, 64);
-      if (lane >= d) { ic += uc; it += ut; }
+      const int uc = __shfl_up(ic, d, 64);
+      if (lane >= d) ic += uc;
     }
-    int ec = ic - sc, et = it - st;
+    int ec = ic - sc;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int e = 4 * lane + j;
-      if (e <= kMaxExperts) { s_off[e] = ec; s_tiles[e] = et; }
+      if (e <= kMaxExperts) s_off[e] = ec;
       ec += c[j];
-      et += tl[j];
     }
-    if (lane == 63) {
-      s_total = ic;
-      *a.n_tiles = it;
+    if (lane == 63) s_total = ic;
+    if (lane == 0) {  // classes in decreasing cost: the tile list starts with the heaviest tiles
+      int base = 0;
+      for (int c2 = kTileClasses - 1; c2 >= 0; --c2) {
+        s_cls[1][c2] = base;
+        base += s_cls[0][c2];
+      }
+      *a.n_tiles = base;
     }
   }
   __syncthreads();
   {
+    // Tiles in cost order (the order inside a class is immaterial: every
+    // output row and column belongs to exactly one tile).  An expert's full
+    // tiles take one run of slots.
     const int total = s_total;
     for (int e = threadIdx.x; e < E; e += blockDim.x) {
       const int start = s_off[e];
       const int end = (e + 1 < E) ? s_off[e + 1] : total;
-      int ti = s_tiles[e];
-      for (int r = start; r < end; r += kTileRows, ++ti) a.tiles[ti] = make_tile(e, r, min(kTileRows, end - r));
+      const int nfull = (end - start) / kTileRows;
+      int ti = nfull ? atomicAdd(&s_cls[1][kTileRows / 32], nfull) : 0;
+      int r = start;
+      for (int i = 0; i < nfull; ++i, r += kTileRows) a.tiles[ti++] = make_tile(e, r, kTileRows);
+      if (r < end) {
+        const int4 t = make_tile(e, r, end - r);
+        a.tiles[atomicAdd(&s_cls[1][t.w], 1)] = t;
+      }
+    }
+    for (int st = threadIdx.x; st < a.shared_tiles; st += blockDim.x) {
+      const int4 t = shared_tile(st, a.T);
+      a.tiles[atomicAdd(&s_cls[1][t.w], 1)] = t;
     }
   }
   // stable scatter: position of pair p in expert-major order
@@ -637,16 +663,40 @@ __device__ __forceinline__ void narrow_gemm(_Float16* lds, __amdgpu_buffer_rsrc_
 }
 
 // ---------------------------------------------------------------------------
-// XCD-aware work order.  The dispatcher hands block b to XCD b % 8 in order of
-// b; item w = (b % 8) * ceil(n/8) + b / 8 gives each XCD a contiguous run of
-// the item list, so the tiles that share one expert's weight slice (adjacent
-// items) run together on one L2.
+// Work order.  Tiles are listed heaviest first.  Item r is (tile, column
+// block) with the tiles taken in groups of 8: inside a group the 8 tiles of
+// one column block are consecutive, so r % 8 = tile % 8.  The dispatcher
+// hands block b to XCD b % 8; with C compute units and two GEMM workgroups
+// per unit, blocks 0..C-1 start one per unit and block C + i takes the second
+// slot of block i's unit.  Block b < C takes item b; block C + i takes the
+// item i'-th from the end, where i' reverses i inside its group of 8, so each
+// unit pairs a heavy item with a light one and every item of a tile runs on
+// XCD tile % 8 (one L2 holds the tile's activation rows).  Blocks from 2C on
+// take the middle of the list as slots free up.  For any C the map is
+// one-to-one onto the n items (n a multiple of 8); for C not a multiple of 8
+// the reversal is dropped.
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ int xcd_item(int n_items) {
+__device__ __forceinline__ int paired_item(int n_items, int cus) {
   const int b = blockIdx.x;
-  const int per = (n_items + 7) / 8;
-  const int w = (b & 7) * per + (b >> 3);
-  return ((b >> 3) < per && w < n_items) ? w : -1;
+  int r;
+  if (b < cus) {
+    r = b;
+  } else if (b < 2 * cus) {
+    const int i = b - cus;
+    r = n_items - 1 - (cus % 8 == 0 ? (i & ~7) | (7 - (i & 7)) : i);
+    if (r < cus) return -1;
+  } else {
+    r = b - cus;
+    if (r >= n_items - cus) return -1;
+  }
+  return r < n_items ? r : -1;
+}
+
+// item r of nb column blocks per tile -> (tile, column block)
+__device__ __forceinline__ void item_of(int r, int nb, int& tile, int& cb) {
+  const int g = r / (8 * nb), rem = r - g * 8 * nb;
+  cb = rem >> 3;
+  tile = 8 * g + (rem & 7);
 }
 
 // ---------------------------------------------------------------------------
@@ -724,23 +774,17 @@ __device__ __forceinline__ void up_narrow(const ChunkArgs& a, _Float16* lds, con
 __global__ __launch_bounds__(256, 2) void up_gemm_kernel(ChunkArgs a) {
   __shared__ __attribute__((aligned(16))) _Float16 lds[kGemmLds];
   __shared__ TileRows tr;
-  const int n_routed = a.route_tiles ? *a.n_tiles : 0;
-  const int nbi = (a.I + 127) / 128, nbs = (a.Is + 127) / 128;
-  const int n_items = n_routed * nbi + a.shared_tiles * nbs;
-  int w = xcd_item(n_items);
+  // items: (tile, column block of 128) over the cost-ordered tiles
+  const int nbi = (a.I + 127) / 128, nbs = (a.Is + 127) / 128, nbm = max(nbi, nbs);
+  const int nt = *a.n_tiles;
+  const int w = paired_item(((nt + 7) & ~7) * nbm, a.cus);
   if (w < 0) return;
-  int e = -1, r0, rows, mt, jb;
-  if (w < n_routed * nbi) {
-    jb = w / n_routed;
-    const int4 td = a.tiles[w - jb * n_routed];
-    e = td.x; r0 = td.y; rows = td.z; mt = td.w;
-  } else {
-    w -= n_routed * nbi;
-    jb = w / a.shared_tiles;
-    r0 = (w - jb * a.shared_tiles) * kSharedRows;
-    rows = min(kSharedRows, a.T - r0);
-    mt = (rows + 31) / 32;
-  }
+  int tile, jb;
+  item_of(w, nbm, tile, jb);
+  if (tile >= nt) return;
+  const int4 td = a.tiles[tile];
+  const int e = td.x, r0 = td.y, rows = td.z, mt = td.w;
+  if (jb >= (e >= 0 ? nbi : nbs)) return;
   if (threadIdx.x < kTileRows) {
     const int r = threadIdx.x;
     int tok = -1;
@@ -856,21 +900,16 @@ __device__ __forceinline__ void down_narrow(const ChunkArgs& a, _Float16* lds, c
 __global__ __launch_bounds__(256, 2) void down_gemm_kernel(ChunkArgs a) {
   __shared__ __attribute__((aligned(16))) _Float16 lds[kGemmLds];
   __shared__ TileRows tr;
-  const int n_routed = a.route_tiles ? *a.n_tiles : 0;
+  // items: (tile, block of 256 outputs) over the cost-ordered tiles
   const int nbh = (a.H + 255) / 256;
-  const int n_tiles = n_routed + a.shared_tiles;
-  int w = xcd_item(n_tiles * nbh);
+  const int nt = *a.n_tiles;
+  const int w = paired_item(((nt + 7) & ~7) * nbh, a.cus);
   if (w < 0) return;
-  const int nb = w / n_tiles, tile = w - nb * n_tiles;
-  int e = -1, r0, rows, mt;
-  if (tile < n_routed) {
-    const int4 td = a.tiles[tile];
-    e = td.x; r0 = td.y; rows = td.z; mt = td.w;
-  } else {
-    r0 = (tile - n_routed) * kSharedRows;
-    rows = min(kSharedRows, a.T - r0);
-    mt = (rows + 31) / 32;
-  }
+  int tile, nb;
+  item_of(w, nbh, tile, nb);
+  if (tile >= nt) return;
+  const int4 td = a.tiles[tile];
+  const int e = td.x, r0 = td.y, rows = td.z, mt = td.w;
   const int K = e >= 0 ? a.I : a.Is;
   if (threadIdx.x < kTileRows) {
     const int r = threadIdx.x;
@@ -953,10 +992,11 @@ int launch_route_chunk(const ChunkArgs& a, hipStream_t s) {
 
 int launch_experts_chunk(const ChunkArgs& a, hipStream_t s) {
   hipLaunchKernelGGL(bucket_kernel, dim3(1), dim3(1024), 0, s, a);
-  // 1-D grids over the item lists (rounded up to whole XCD rounds); blocks
+  // grids over the item lists (tile count rounded up to a group of 8); blocks
   // beyond the items the bucketing produced exit at once
-  const int up_items = a.max_route_tiles * ((a.I + 127) / 128) + a.shared_tiles * ((a.Is + 127) / 128);
-  const int down_items = (a.max_route_tiles + a.shared_tiles) * ((a.H + 255) / 256);
+  const int max_tiles = (a.max_route_tiles + a.shared_tiles + 7) & ~7;
+  const int up_items = max_tiles * max((a.I + 127) / 128, (a.Is + 127) / 128);
+  const int down_items = max_tiles * ((a.H + 255) / 256);
   hipLaunchKernelGGL(up_gemm_kernel, dim3((up_items + 7) & ~7), dim3(256), 0, s, a);
   hipLaunchKernelGGL(down_gemm_kernel, dim3((down_items + 7) & ~7), dim3(256), 0, s, a);
   hipLaunchKernelGGL(combine_kernel, dim3((a.H / 8 + 255) / 256, a.T), dim3(256), 0, s, a);

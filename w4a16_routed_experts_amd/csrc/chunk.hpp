@@ -25,15 +25,16 @@ struct ChunkArgs {
   int32_t* offsets;    // [E+1]
   int32_t* sorted_pair;  // [T*k]  pair index at each expert-major position
   int32_t* pos_of_pair;  // [T*k]  expert-major position of each pair (-1: dropped)
-  int4* tiles;         // [max_route_tiles] (expert, first row, rows, 32-row blocks)
-  int32_t* n_tiles;    // routed tiles written by the bucketing kernel
+  int4* tiles;         // [max_route_tiles + shared_tiles] (expert or -1 for the shared expert, first
+                       // row, rows, 32-row blocks or 0 for a narrow tile), heaviest first
+  int32_t* n_tiles;    // tiles written by the bucketing kernel
   _Float16* h;         // [T*k][I]  expert-major rows
   _Float16* hs;        // [T][Is]
   _Float16* y;         // [T*k][H]  weighted expert outputs, expert-major rows
   _Float16* ys;        // [T][H]    sigma * shared output, or null (routed half only)
-  int route_tiles;     // 1: routed tiles present
   int shared_tiles;    // number of kSharedRows-token shared-expert tiles (0: routed half only)
   int max_route_tiles; // bound on routed tiles for the grid
+  int cus;             // compute units of the device (work pairing in the GEMM kernels)
 };
 
 int launch_route_chunk(const ChunkArgs& a, hipStream_t s);
