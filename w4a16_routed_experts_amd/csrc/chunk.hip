@@ -725,15 +725,21 @@ __device__ __forceinline__ void up_tile(const ChunkArgs& a, _Float16* lds, const
   f16v acc[MT][2];
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) acc[mt][0] = acc[mt][1] = f16v{};
-  tile_gemm<BITS, 2, MT>(lds, op, a.H, acc);
-  if (!ok) return;
+  tile_gemm<BITS, 2, MT>(lds, op, a.H, acc);  // ends with a workgroup barrier: the LDS is free
+  // The wave's h tile goes through LDS (row-major, 32 halves a row) so that
+  // the stores are whole 16-byte pieces of rows, not one 2-byte value a lane.
+  _Float16* ht = lds + wave * (32 * MT) * 32;
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int r = 32 * mt + acc_row(i);
-      if (r < rows) hout[(size_t)tr.out_row[r] * inter + j] = (_Float16)(silu_f(acc[mt][0][i]) * acc[mt][1][i]);
-    }
+    for (int i = 0; i < 16; ++i)
+      ht[(32 * mt + acc_row(i)) * 32 + (lane & 31)] = (_Float16)(silu_f(acc[mt][0][i]) * acc[mt][1][i]);
+  __syncthreads();
+  if (jb * 128 + wave * 32 >= inter) return;  // widths are multiples of 64: a wave's columns are all in or all out
+  const int c = lane & 3;
+  for (int r = lane >> 2; r < rows; r += 16)
+    *reinterpret_cast<uint4*>(hout + (size_t)tr.out_row[r] * inter + jb * 128 + wave * 32 + 8 * c) =
+        *reinterpret_cast<const uint4*>(ht + r * 32 + 8 * c);
 }
 
 // a narrow routed tile: each wave takes 32 gate and the same 32 up columns as
@@ -759,16 +765,19 @@ __device__ __forceinline__ void up_narrow(const ChunkArgs& a, _Float16* lds, con
 #pragma unroll
   for (int f = 0; f < 4; ++f) acc[f] = f4{0.f, 0.f, 0.f, 0.f};
   narrow_gemm<4>(lds, ra, tr.aoff, a.H, rq, rs, qoff, soff, acc);
+  // h through LDS (16 rows of 32 halves per wave) for 16-byte row stores;
+  // the barrier first: other waves may still read the tile's rows
+  __syncthreads();
+  _Float16* ht = lds + wave * kNarrowRows * 32;
 #pragma unroll
-  for (int ff = 0; ff < 2; ++ff) {
-    const int j = j0 + 16 * ff + n;
-    if (j >= inter) continue;
+  for (int ff = 0; ff < 2; ++ff)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int r = 4 * q + i;
-      if (r < rows) hout[(size_t)tr.out_row[r] * inter + j] = (_Float16)(silu_f(acc[ff][i]) * acc[ff + 2][i]);
-    }
-  }
+    for (int i = 0; i < 4; ++i) ht[(4 * q + i) * 32 + 16 * ff + n] = (_Float16)(silu_f(acc[ff][i]) * acc[ff + 2][i]);
+  __syncthreads();
+  const int r = lane >> 2, c = lane & 3;
+  if (j0 < inter && r < rows)
+    *reinterpret_cast<uint4*>(hout + (size_t)tr.out_row[r] * inter + j0 + 8 * c) =
+        *reinterpret_cast<const uint4*>(ht + r * 32 + 8 * c);
 }
 
 __global__ __launch_bounds__(256, 2) void up_gemm_kernel(ChunkArgs a) {
@@ -850,18 +859,26 @@ __device__ __forceinline__ void down_tile(const ChunkArgs& a, _Float16* lds, con
   f16v acc[MT][2];
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) acc[mt][0] = acc[mt][1] = f16v{};
-  tile_gemm<BITS, 2, MT>(lds, op, K, acc);
+  tile_gemm<BITS, 2, MT>(lds, op, K, acc);  // ends with a workgroup barrier: the LDS is free
+  // the wave's 64 outputs of each row through LDS (row-major, 64 halves a
+  // row) for 16-byte row stores
+  _Float16* yt = lds + wave * (32 * MT) * 64;
 #pragma unroll
-  for (int f = 0; f < 2; ++f) {
-    if (n[f] >= a.H) continue;
+  for (int f = 0; f < 2; ++f)
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         const int r = 32 * mt + acc_row(i);
-        if (r < rows) yout[(size_t)tr.out_row[r] * a.H + n[f]] = (_Float16)(tr.scale[r] * acc[mt][f][i]);
+        yt[r * 64 + 32 * f + (lane & 31)] = (_Float16)(tr.scale[r] * acc[mt][f][i]);
       }
-  }
+  __syncthreads();
+  const int c0 = nb * 256 + wave * 64;
+  if (c0 >= a.H) return;  // H is a multiple of 64: a wave's outputs are all in or all out
+  const int c = lane & 7;
+  for (int r = lane >> 3; r < rows; r += 8)
+    *reinterpret_cast<uint4*>(yout + (size_t)tr.out_row[r] * a.H + c0 + 8 * c) =
+        *reinterpret_cast<const uint4*>(yt + r * 64 + 8 * c);
 }
 
 // a narrow routed tile: each wave takes 64 outputs as four 16-column fragments
@@ -886,15 +903,23 @@ __device__ __forceinline__ void down_narrow(const ChunkArgs& a, _Float16* lds, c
 #pragma unroll
   for (int f = 0; f < 4; ++f) acc[f] = f4{0.f, 0.f, 0.f, 0.f};
   narrow_gemm<4>(lds, ra, tr.aoff, K, rq, rs, qoff, soff, acc);
+  // outputs through LDS (16 rows of 64 halves per wave) for 16-byte row
+  // stores; the barrier first: other waves may still read the tile's rows
+  __syncthreads();
+  _Float16* yt = lds + wave * kNarrowRows * 64;
 #pragma unroll
-  for (int f = 0; f < 4; ++f) {
-    if (col[f] >= a.H) continue;
+  for (int f = 0; f < 4; ++f)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int r = 4 * q + i;
-      if (r < rows) yout[(size_t)tr.out_row[r] * a.H + col[f]] = (_Float16)(tr.scale[r] * acc[f][i]);
-    }
-  }
+    for (int i = 0; i < 4; ++i) yt[(4 * q + i) * 64 + 16 * f + n] = (_Float16)(tr.scale[4 * q + i] * acc[f][i]);
+  __syncthreads();
+  const int c0 = nb * 256 + wave * 64;
+  if (c0 >= a.H) return;
+  const int c = lane & 7;
+#pragma unroll
+  for (int r = lane >> 3; r < kNarrowRows; r += 8)
+    if (r < rows)
+      *reinterpret_cast<uint4*>(yout + (size_t)tr.out_row[r] * a.H + c0 + 8 * c) =
+          *reinterpret_cast<const uint4*>(yt + r * 64 + 8 * c);
 }
 
 __global__ __launch_bounds__(256, 2) void down_gemm_kernel(ChunkArgs a) {
