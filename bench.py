@@ -51,12 +51,19 @@ def algorithmic_flops(d, T):
     return T * (2 * (d.E + 1) * d.H + d.k * 6 * d.I * d.H + 6 * d.Is * d.H)
 
 
+# the sources the single-token kernel and its launch are built from: the
+# decode kernel, the headers it includes, and the host code that sizes its grid
+DECODE_SOURCES = ("api.hip", "common.hpp", "decode.hip", "decode.hpp", "gemv.hpp")
+
+
 def source_digest():
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "w4a16_routed_experts_amd", "csrc")
-    for name in sorted(os.listdir(csrc)):
+    for name in DECODE_SOURCES:
         with open(os.path.join(csrc, name), "rb") as f:
             h.update(name.encode() + f.read())
+    with open(os.path.join(ROOT, "include", "moe_w4a16.h"), "rb") as f:
+        h.update(b"moe_w4a16.h" + f.read())
     return h.hexdigest()[:16]
 
 

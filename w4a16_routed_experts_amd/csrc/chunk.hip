@@ -8,8 +8,8 @@
 //   3. bucketing            (token, slot) pairs sorted by expert, then pair
 //                           index; 64- or 32-row tiles per expert; shared tiles
 //   4. gate/up GEMM         h[row][I] = silu(x W_gate^T) * (x W_up^T)   (fp16)
-//   5. down GEMM            y[row][H] = w * (h W_down^T)                 (fp16)
-//   6. combine              out[t] = sum_i y[pos(t,i)] + sigma_t * s[t]
+//   5. down GEMM            y[t*k+i][H] = w * (h W_down^T)                (fp16)
+//   6. combine              out[t] = sum_i y[t*k+i] + sigma_t * s[t]
 // Each tile streams its expert's weights once; a tile's rows are the tokens
 // routed to that expert.
 #include "chunk.hpp"
@@ -307,13 +307,7 @@ __global__ __launch_bounds__(1024) void bucket_kernel(ChunkArgs a) {
       const int e = p < p_end ? ev[u] : -1;
       const bool ok = e >= 0 && e < E;
       const uint64_t pe = peers_of(ok ? e : 255) & __ballot(ok);
-      if (ok) {
-        const int pos = s_off[e] + hist[wave][e] + __popcll(pe & lt);
-        a.sorted_pair[pos] = p;
-        a.pos_of_pair[p] = pos;
-      } else if (p < p_end) {
-        a.pos_of_pair[p] = -1;
-      }
+      if (ok) a.sorted_pair[s_off[e] + hist[wave][e] + __popcll(pe & lt)] = p;
       if (ok && (pe & lt) == 0) hist[wave][e] += __popcll(pe);
     }
   }
@@ -939,16 +933,17 @@ __global__ __launch_bounds__(256, 2) void down_gemm_kernel(ChunkArgs a) {
   if (threadIdx.x < kTileRows) {
     const int r = threadIdx.x;
     bool ok;
-    if (e >= 0) {
+    if (e >= 0) {  // routed rows of y are indexed by pair t * k + i, so the combine reads a token's rows directly
       const int p = r < rows ? a.sorted_pair[r0 + r] : -1;
       ok = p >= 0;
       tr.scale[r] = ok ? a.wts[p] : 0.f;
+      tr.out_row[r] = p;
     } else {
       ok = r < rows;
       tr.scale[r] = ok ? a.sigma[r0 + r] : 0.f;
+      tr.out_row[r] = r0 + r;
     }
     tr.aoff[r] = ok ? (uint32_t)r * K * 2u : kOob;
-    tr.out_row[r] = r0 + r;
   }
   __syncthreads();
   // A: the tile's own rows of h (or h_s), which start at row r0
@@ -977,7 +972,7 @@ __global__ __launch_bounds__(256, 2) void down_gemm_kernel(ChunkArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// 6. combine: out[t][n] = sum_i y[pos(t,i)][n] (+ ys[t][n]); 8 outputs/thread
+// 6. combine: out[t][n] = sum_i y[t*k+i][n] (+ ys[t][n]); 8 outputs/thread
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ void add8(float acc[8], uint4 v) {
   const h8 h = __builtin_bit_cast(h8, v);
@@ -990,16 +985,21 @@ __global__ __launch_bounds__(256) void combine_kernel(ChunkArgs a) {
   const int n = (blockIdx.x * blockDim.x + threadIdx.x) * 8;
   if (n >= a.H) return;
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  // the token's k rows of y (row t * k + i) and its ids are loaded together;
+  // a pair whose id is outside [0, E) was dropped and its row never written
   uint4 v[kMaxTopK];
-  int pos[kMaxTopK];
+  int id[kMaxTopK];
+  const int i_last = (int)(((size_t)t + 1) * a.k - 1);
 #pragma unroll
-  for (int i = 0; i < kMaxTopK; ++i) pos[i] = i < a.k ? a.pos_of_pair[(size_t)t * a.k + i] : -1;
-#pragma unroll
-  for (int i = 0; i < kMaxTopK; ++i)
-    v[i] = pos[i] >= 0 ? *reinterpret_cast<const uint4*>(a.y + (size_t)pos[i] * a.H + n) : make_uint4(0, 0, 0, 0);
+  for (int i = 0; i < kMaxTopK; ++i) {
+    const int p = min(t * a.k + i, i_last);  // clamped: always a row of this token
+    id[i] = a.ids[p];
+    v[i] = *reinterpret_cast<const uint4*>(a.y + (size_t)p * a.H + n);
+  }
   if (a.ys) add8(acc, *reinterpret_cast<const uint4*>(a.ys + (size_t)t * a.H + n));
 #pragma unroll
-  for (int i = 0; i < kMaxTopK; ++i) add8(acc, v[i]);
+  for (int i = 0; i < kMaxTopK; ++i)
+    if (i < a.k && id[i] >= 0 && id[i] < a.E) add8(acc, v[i]);
   h8 o;
 #pragma unroll
   for (int i = 0; i < 8; ++i) o[i] = (_Float16)acc[i];

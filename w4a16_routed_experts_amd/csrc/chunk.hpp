@@ -24,13 +24,12 @@ struct ChunkArgs {
   float* sigma;        // [T]
   int32_t* offsets;    // [E+1]
   int32_t* sorted_pair;  // [T*k]  pair index at each expert-major position
-  int32_t* pos_of_pair;  // [T*k]  expert-major position of each pair (-1: dropped)
   int4* tiles;         // [max_route_tiles + shared_tiles] (expert or -1 for the shared expert, first
                        // row, rows, 32-row blocks or 0 for a narrow tile), heaviest first
   int32_t* n_tiles;    // tiles written by the bucketing kernel
   _Float16* h;         // [T*k][I]  expert-major rows
   _Float16* hs;        // [T][Is]
-  _Float16* y;         // [T*k][H]  weighted expert outputs, expert-major rows
+  _Float16* y;         // [T*k][H]  weighted expert outputs, row t*k+i for pair (t, i)
   _Float16* ys;        // [T][H]    sigma * shared output, or null (routed half only)
   int shared_tiles;    // number of kSharedRows-token shared-expert tiles (0: routed half only)
   int max_route_tiles; // bound on routed tiles for the grid
