@@ -108,6 +108,7 @@ void carve_chunk(const moe_dims* d, int T, Carve& c, ChunkArgs& a) {
   a.sigma = c.take<float>((size_t)T * 4);
   a.offsets = c.take<int32_t>((size_t)(d->num_experts + 1) * 4);
   a.sorted_pair = c.take<int32_t>(P * 4);
+  a.sorted_wt = c.take<float>(P * 4);
   a.tiles = c.take<int4>((size_t)(max_route_tiles(d, T) + (T + kSharedRows - 1) / kSharedRows) * 16);
   a.n_tiles = c.take<int32_t>(4);
   a.h = c.take<_Float16>(P * d->expert_inter * 2);

@@ -296,18 +296,27 @@ __global__ __launch_bounds__(1024) void bucket_kernel(ChunkArgs a) {
       a.tiles[atomicAdd(&s_cls[1][t.w], 1)] = t;
     }
   }
-  // stable scatter: position of pair p in expert-major order
+  // stable scatter: position of pair p in expert-major order, with its
+  // routing weight (so the down GEMM reads both by position)
   for (int p0 = p_begin; p0 < p_end; p0 += 64 * kBatch) {
     int ev[kBatch];
+    float wv[kBatch];
 #pragma unroll
-    for (int u = 0; u < kBatch; ++u) ev[u] = a.ids[min(p0 + 64 * u + lane, P - 1)];
+    for (int u = 0; u < kBatch; ++u) {
+      ev[u] = a.ids[min(p0 + 64 * u + lane, P - 1)];
+      wv[u] = a.wts[min(p0 + 64 * u + lane, P - 1)];
+    }
 #pragma unroll
     for (int u = 0; u < kBatch; ++u) {
       const int p = p0 + 64 * u + lane;
       const int e = p < p_end ? ev[u] : -1;
       const bool ok = e >= 0 && e < E;
       const uint64_t pe = peers_of(ok ? e : 255) & __ballot(ok);
-      if (ok) a.sorted_pair[s_off[e] + hist[wave][e] + __popcll(pe & lt)] = p;
+      if (ok) {
+        const int pos = s_off[e] + hist[wave][e] + __popcll(pe & lt);
+        a.sorted_pair[pos] = p;
+        a.sorted_wt[pos] = wv[u];
+      }
       if (ok && (pe & lt) == 0) hist[wave][e] += __popcll(pe);
     }
   }
@@ -829,10 +838,21 @@ __global__ __launch_bounds__(256, 2) void up_gemm_kernel(ChunkArgs a) {
 //    ys[t][n] = sigma_t * (h_s[t] . S_down[n]).  Items: (block of 256
 //    outputs, tile), output-block major.
 // ---------------------------------------------------------------------------
+// The destination row and scale of tile row threadIdx.x (< kTileRows) come
+// in registers (my_row, my_scale): they were loaded before the K loop and
+// are published to the TileRows of the epilogue after it, so their loads
+// never delay the GEMM.
+__device__ __forceinline__ void publish_rows(TileRows& tr, int my_row, float my_scale) {
+  if (threadIdx.x < kTileRows) {
+    tr.out_row[threadIdx.x] = my_row;
+    tr.scale[threadIdx.x] = my_scale;
+  }
+}
+
 template <int BITS, int MT>
-__device__ __forceinline__ void down_tile(const ChunkArgs& a, _Float16* lds, const TileRows& tr,
+__device__ __forceinline__ void down_tile(const ChunkArgs& a, _Float16* lds, TileRows& tr,
                                           __amdgpu_buffer_rsrc_t ra, const uint8_t* wq, const uint16_t* wsc, int K,
-                                          int nb, _Float16* yout, int rows) {
+                                          int nb, _Float16* yout, int rows, int my_row, float my_scale) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const uint32_t rb = (uint32_t)K * BITS / 8;
   const uint32_t ng = K / kGroup;
@@ -854,6 +874,8 @@ __device__ __forceinline__ void down_tile(const ChunkArgs& a, _Float16* lds, con
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) acc[mt][0] = acc[mt][1] = f16v{};
   tile_gemm<BITS, 2, MT>(lds, op, K, acc);  // ends with a workgroup barrier: the LDS is free
+  publish_rows(tr, my_row, my_scale);
+  __syncthreads();
   // the wave's 64 outputs of each row through LDS (row-major, 64 halves a
   // row) for 16-byte row stores
   _Float16* yt = lds + wave * (32 * MT) * 64;
@@ -876,9 +898,9 @@ __device__ __forceinline__ void down_tile(const ChunkArgs& a, _Float16* lds, con
 }
 
 // a narrow routed tile: each wave takes 64 outputs as four 16-column fragments
-__device__ __forceinline__ void down_narrow(const ChunkArgs& a, _Float16* lds, const TileRows& tr,
+__device__ __forceinline__ void down_narrow(const ChunkArgs& a, _Float16* lds, TileRows& tr,
                                             __amdgpu_buffer_rsrc_t ra, const uint8_t* wq, const uint16_t* wsc, int K,
-                                            int nb, _Float16* yout, int rows) {
+                                            int nb, _Float16* yout, int rows, int my_row, float my_scale) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, n = lane & 15, q = lane >> 4;
   const uint32_t rb = (uint32_t)K / 2;
   const uint32_t ng = K / kGroup;
@@ -899,6 +921,7 @@ __device__ __forceinline__ void down_narrow(const ChunkArgs& a, _Float16* lds, c
   narrow_gemm<4>(lds, ra, tr.aoff, K, rq, rs, qoff, soff, acc);
   // outputs through LDS (16 rows of 64 halves per wave) for 16-byte row
   // stores; the barrier first: other waves may still read the tile's rows
+  publish_rows(tr, my_row, my_scale);
   __syncthreads();
   _Float16* yt = lds + wave * kNarrowRows * 64;
 #pragma unroll
@@ -930,20 +953,22 @@ __global__ __launch_bounds__(256, 2) void down_gemm_kernel(ChunkArgs a) {
   const int4 td = a.tiles[tile];
   const int e = td.x, r0 = td.y, rows = td.z, mt = td.w;
   const int K = e >= 0 ? a.I : a.Is;
+  // A is the tile's own rows of h (or h_s): its offsets need no loads.  The
+  // destination row (routed rows of y are indexed by pair t * k + i, so the
+  // combine reads a token's rows directly) and the scale of each row are
+  // loaded now, with clamped indices, and used only in the epilogue.
+  int my_row = 0;
+  float my_scale = 0.f;
   if (threadIdx.x < kTileRows) {
-    const int r = threadIdx.x;
-    bool ok;
-    if (e >= 0) {  // routed rows of y are indexed by pair t * k + i, so the combine reads a token's rows directly
-      const int p = r < rows ? a.sorted_pair[r0 + r] : -1;
-      ok = p >= 0;
-      tr.scale[r] = ok ? a.wts[p] : 0.f;
-      tr.out_row[r] = p;
+    const int r = threadIdx.x, rc = r0 + min(r, rows - 1);
+    if (e >= 0) {
+      my_row = a.sorted_pair[rc];
+      my_scale = a.sorted_wt[rc];
     } else {
-      ok = r < rows;
-      tr.scale[r] = ok ? a.sigma[r0 + r] : 0.f;
-      tr.out_row[r] = r0 + r;
+      my_row = r0 + r;
+      my_scale = a.sigma[rc];
     }
-    tr.aoff[r] = ok ? (uint32_t)r * K * 2u : kOob;
+    tr.aoff[r] = r < rows ? (uint32_t)r * K * 2u : kOob;
   }
   __syncthreads();
   // A: the tile's own rows of h (or h_s), which start at row r0
@@ -953,21 +978,21 @@ __global__ __launch_bounds__(256, 2) void down_gemm_kernel(ChunkArgs a) {
     const uint8_t* wq = a.w2_q + (size_t)e * a.H * (a.I / 2);
     const uint16_t* wsc = a.w2_s + (size_t)e * a.H * (a.I / kGroup);
     switch (mt) {
-      case 4: down_tile<4, 4>(a, lds, tr, ra, wq, wsc, a.I, nb, a.y, rows); break;
-      case 3: down_tile<4, 3>(a, lds, tr, ra, wq, wsc, a.I, nb, a.y, rows); break;
-      case 2: down_tile<4, 2>(a, lds, tr, ra, wq, wsc, a.I, nb, a.y, rows); break;
+      case 4: down_tile<4, 4>(a, lds, tr, ra, wq, wsc, a.I, nb, a.y, rows, my_row, my_scale); break;
+      case 3: down_tile<4, 3>(a, lds, tr, ra, wq, wsc, a.I, nb, a.y, rows, my_row, my_scale); break;
+      case 2: down_tile<4, 2>(a, lds, tr, ra, wq, wsc, a.I, nb, a.y, rows, my_row, my_scale); break;
       case 0:
         if (a.I >= kNarrowMinK && a.I <= kNarrowK) {
-          down_narrow(a, lds, tr, ra, wq, wsc, a.I, nb, a.y, rows);
+          down_narrow(a, lds, tr, ra, wq, wsc, a.I, nb, a.y, rows, my_row, my_scale);
           break;
         }
         [[fallthrough]];
-      default: down_tile<4, 1>(a, lds, tr, ra, wq, wsc, a.I, nb, a.y, rows); break;
+      default: down_tile<4, 1>(a, lds, tr, ra, wq, wsc, a.I, nb, a.y, rows, my_row, my_scale); break;
     }
   } else {
     const uint8_t* wq = reinterpret_cast<const uint8_t*>(a.sh2_q);
-    if (mt == 2) down_tile<8, 2>(a, lds, tr, ra, wq, a.sh2_s, a.Is, nb, a.ys, rows);
-    else down_tile<8, 1>(a, lds, tr, ra, wq, a.sh2_s, a.Is, nb, a.ys, rows);
+    if (mt == 2) down_tile<8, 2>(a, lds, tr, ra, wq, a.sh2_s, a.Is, nb, a.ys, rows, my_row, my_scale);
+    else down_tile<8, 1>(a, lds, tr, ra, wq, a.sh2_s, a.Is, nb, a.ys, rows, my_row, my_scale);
   }
 }
 

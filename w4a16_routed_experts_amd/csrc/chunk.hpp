@@ -24,6 +24,7 @@ struct ChunkArgs {
   float* sigma;        // [T]
   int32_t* offsets;    // [E+1]
   int32_t* sorted_pair;  // [T*k]  pair index at each expert-major position
+  float* sorted_wt;    // [T*k]  routing weight of each pair, in the same order
   int4* tiles;         // [max_route_tiles + shared_tiles] (expert or -1 for the shared expert, first
                        // row, rows, 32-row blocks or 0 for a narrow tile), heaviest first
   int32_t* n_tiles;    // tiles written by the bucketing kernel
