@@ -213,12 +213,18 @@ __global__ __launch_bounds__(1024) void bucket_kernel(ChunkArgs a) {
   __syncthreads();
   // per-wave histograms (ids outside [0, E) are dropped: they never index
   // weights).  Ids are loaded kBatch rounds at a time with clamped (always
-  // valid) indices, so the loads are in flight together.
+  // valid) indices, so the loads are in flight together.  The first batch of
+  // ids and routing weights stays in registers for the scatter below (with
+  // T * k <= 16 * 64 * kBatch it is the wave's whole share).
   constexpr int kBatch = 4;
-  for (int p0 = p_begin; p0 < p_end; p0 += 64 * kBatch) {
-    int ev[kBatch];
+  int ev0[kBatch];
+  float wv0[kBatch];
 #pragma unroll
-    for (int u = 0; u < kBatch; ++u) ev[u] = a.ids[min(p0 + 64 * u + lane, P - 1)];
+  for (int u = 0; u < kBatch; ++u) {
+    ev0[u] = a.ids[min(p_begin + 64 * u + lane, P - 1)];
+    wv0[u] = a.wts[min(p_begin + 64 * u + lane, P - 1)];
+  }
+  auto count = [&](int p0, const int* ev) {
 #pragma unroll
     for (int u = 0; u < kBatch; ++u) {
       const int p = p0 + 64 * u + lane;
@@ -227,6 +233,13 @@ __global__ __launch_bounds__(1024) void bucket_kernel(ChunkArgs a) {
       const uint64_t pe = peers_of(ok ? e : 255) & __ballot(ok);
       if (ok && (pe & lt) == 0) hist[wave][e] += __popcll(pe);  // one leader per expert
     }
+  };
+  count(p_begin, ev0);
+  for (int p0 = p_begin + 64 * kBatch; p0 < p_end; p0 += 64 * kBatch) {
+    int ev[kBatch];
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) ev[u] = a.ids[min(p0 + 64 * u + lane, P - 1)];
+    count(p0, ev);
   }
   __syncthreads();
   if (threadIdx.x < kMaxExperts + 1) {
@@ -298,14 +311,7 @@ __global__ __launch_bounds__(1024) void bucket_kernel(ChunkArgs a) {
   }
   // stable scatter: position of pair p in expert-major order, with its
   // routing weight (so the down GEMM reads both by position)
-  for (int p0 = p_begin; p0 < p_end; p0 += 64 * kBatch) {
-    int ev[kBatch];
-    float wv[kBatch];
-#pragma unroll
-    for (int u = 0; u < kBatch; ++u) {
-      ev[u] = a.ids[min(p0 + 64 * u + lane, P - 1)];
-      wv[u] = a.wts[min(p0 + 64 * u + lane, P - 1)];
-    }
+  auto scatter = [&](int p0, const int* ev, const float* wv) {
 #pragma unroll
     for (int u = 0; u < kBatch; ++u) {
       const int p = p0 + 64 * u + lane;
@@ -319,6 +325,17 @@ __global__ __launch_bounds__(1024) void bucket_kernel(ChunkArgs a) {
       }
       if (ok && (pe & lt) == 0) hist[wave][e] += __popcll(pe);
     }
+  };
+  scatter(p_begin, ev0, wv0);
+  for (int p0 = p_begin + 64 * kBatch; p0 < p_end; p0 += 64 * kBatch) {
+    int ev[kBatch];
+    float wv[kBatch];
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      ev[u] = a.ids[min(p0 + 64 * u + lane, P - 1)];
+      wv[u] = a.wts[min(p0 + 64 * u + lane, P - 1)];
+    }
+    scatter(p0, ev, wv);
   }
 }
 
