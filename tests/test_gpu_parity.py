@@ -140,21 +140,25 @@ def test_deterministic(cfg):
 
 
 def test_workspace_reused_across_token_counts():
-    """The counters a call leaves in the workspace let the next call run."""
+    """The counters a call leaves in the workspace let the next call run, on
+    either path and at any token count."""
     case4 = gen.make_case(gen.REAL, 4, seed=6004, real_experts=True)
     case1 = gen.make_case(gen.REAL, 1, seed=6001, real_experts=True)
+    case8 = gen.make_case(gen.REAL, 8, seed=6008, real_experts=True)  # the multi-token path
     d = case4.dims
     dims = _gpu.dims_of(d)
     W = _gpu.device_weights(_gpu.config_case(1))
-    ws = m.workspace(dims, 4)
+    ws = torch.zeros(max(m.moe_workspace_bytes(dims, 4), m.moe_workspace_bytes(dims, 8)), dtype=torch.uint8,
+                     device="cuda")
+    seq = (case4, case1, case8, case1, case4)
     res = []
-    for case in (case4, case1, case4):
+    for case in seq:
         out = torch.zeros((case.T, d.H), dtype=torch.int16, device="cuda")
         m.moe_forward(dims, W.struct, _gpu.x_tensor(case), case.T, out, ws=ws)
         torch.cuda.synchronize()
         res.append(_gpu.half_to_f64(out))
     W_host = _gpu.config_case(1).weights
-    for case, o in zip((case4, case1, case4), res):
+    for case, o in zip(seq, res):
         want = ref.forward(case.x, W_host, d)["out"]
         assert _gpu.row_rel_l2(o, want).max() <= _gpu.ROW_TOL
     # the workspace's counters and done flags are back to zero

@@ -101,7 +101,9 @@ DecodeWs carve_decode(const moe_dims* d, int T, Carve& c) {
 
 void carve_chunk(const moe_dims* d, int T, Carve& c, ChunkArgs& a) {
   const size_t P = (size_t)T * d->top_k;
-  c.take<uint32_t>(kSyncBytes);
+  // counters (zero between calls): the last slot is the chunk path's
+  uint32_t* sync = c.take<uint32_t>(kSyncBytes);
+  a.route_done = sync ? sync + (kCounterPages * kFlagPage - kSyncStride) : nullptr;
   a.logits = c.take<float>((size_t)T * (d->num_experts + 1) * 4);
   a.ids = c.take<int32_t>(P * 4);
   a.wts = c.take<float>(P * 4);
@@ -322,9 +324,7 @@ MOE_API int moe_forward(const moe_dims* dims, const moe_weights* w, const uint16
   if (shared_gate) a.sigma = shared_gate;
   a.shared_tiles = (T + kSharedRows - 1) / kSharedRows;
   a.cus = di->cus;
-  int r = launch_route_chunk(a, stream);
-  if (r != MOE_OK) return r;
-  return launch_experts_chunk(a, stream);
+  return launch_forward_chunk(a, stream);
 }
 
 }  // extern "C"

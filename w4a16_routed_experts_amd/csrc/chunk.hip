@@ -72,13 +72,16 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
 }
 
 // ---------------------------------------------------------------------------
-// 1. router GEMM: 32 tokens x 32 rows per workgroup; the four waves take
-//    interleaved 64-groups of K and are summed through LDS.  The scales are
-//    applied per group to fp32 partial sums, so routing sees logits accurate to
-//    fp32 rounding.
+// 1. router GEMM: 32 tokens x 32 rows per workgroup; the kRouterWaves waves
+//    take interleaved 64-groups of K and are summed through LDS.  At hidden
+//    2048 each wave's four groups are one batch of loads, so the kernel waits
+//    on memory once.  The scales are applied per group to fp32 partial sums,
+//    so routing sees logits accurate to fp32 rounding.
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void router_gemm_kernel(ChunkArgs a) {
-  __shared__ float red[4][16][64];
+static constexpr int kRouterWaves = 8;
+
+__global__ __launch_bounds__(64 * kRouterWaves) void router_gemm_kernel(ChunkArgs a) {
+  __shared__ float red[kRouterWaves][16][64];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int m = lane & 31, g = lane >> 5;
   const int t = blockIdx.x * 32 + m;  // A row (token)
@@ -92,12 +95,12 @@ __global__ __launch_bounds__(256) void router_gemm_kernel(ChunkArgs a) {
   const uint32_t soff = r < nrows ? (uint32_t)r * ngr * 2u : kOob;
   f16v acc = {};
   constexpr int BATCH = 4;
-  for (int g0 = wave; g0 < ngr; g0 += 4 * BATCH) {
+  for (int g0 = wave; g0 < ngr; g0 += kRouterWaves * BATCH) {
     u32x4 xa[BATCH][4], wb[BATCH][2];
     uint16_t sc[BATCH];
 #pragma unroll
     for (int u = 0; u < BATCH; ++u) {
-      const int gi = g0 + 4 * u;
+      const int gi = g0 + kRouterWaves * u;
       const bool ok = gi < ngr;  // uniform
       const uint32_t kx = ok ? 128u * gi : kOob, kq = ok ? 64u * gi : kOob, ks = ok ? 2u * gi : kOob;
 #pragma unroll
@@ -130,7 +133,9 @@ __global__ __launch_bounds__(256) void router_gemm_kernel(ChunkArgs a) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       const int tt = blockIdx.x * 32 + acc_row(i);
-      const float v = (red[0][i][lane] + red[1][i][lane]) + (red[2][i][lane] + red[3][i][lane]);
+      float v = 0.f;
+#pragma unroll
+      for (int w2 = 0; w2 < kRouterWaves; ++w2) v += red[w2][i][lane];
       if (tt < a.T) a.logits[(size_t)tt * nrows + r] = v;
     }
   }
@@ -196,7 +201,40 @@ __device__ __forceinline__ int4 shared_tile(int st, int T) {
 
 static constexpr int kTileClasses = kTileRows / 32 + 1;  // cost classes: 32-row blocks, 0 = narrow
 
-__global__ __launch_bounds__(1024) void bucket_kernel(ChunkArgs a) {
+// Slot of the j-th tile of the heaviest class (n tiles, slots 0..n-1).  The
+// GEMM kernels run tile s on XCD s % 8, so the class is filled column by
+// column of an 8-wide grid: consecutive j, which are one expert's tiles, share
+// an XCD, and its L2 fetches the expert's weights once for all of them.
+__device__ __forceinline__ int top_slot(int j, int n) {
+  const int R = (n + 7) / 8;       // rows of the grid
+  const int fc = n - 8 * (R - 1);  // columns with R rows (the others have R - 1)
+  int c, rho;
+  if (j < fc * R) {
+    c = j / R; rho = j % R;
+  } else {
+    const int jj = j - fc * R;
+    c = fc + jj / (R - 1); rho = jj % (R - 1);
+  }
+  return 8 * rho + c;
+}
+
+// ids and routing weights of pairs: ordinary loads, or device-coherent loads
+// when other workgroups of the same launch wrote them
+template <bool CO>
+__device__ __forceinline__ int load_id(const int32_t* p) {
+  if (CO) return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return *p;
+}
+template <bool CO>
+__device__ __forceinline__ float load_wt(const float* p) {
+  if (CO)
+    return __builtin_bit_cast(float, __hip_atomic_load(reinterpret_cast<const uint32_t*>(p), __ATOMIC_RELAXED,
+                                                       __HIP_MEMORY_SCOPE_AGENT));
+  return *p;
+}
+
+template <bool CO>
+__device__ __forceinline__ void bucket_body(const ChunkArgs& a) {
   __shared__ int hist[16][kMaxExperts + 1];  // per-wave counts, then per-wave bases
   __shared__ int s_off[kMaxExperts + 1];
   __shared__ int s_cls[2][kTileClasses];  // tiles per cost class, then each class's next slot
@@ -221,8 +259,8 @@ __global__ __launch_bounds__(1024) void bucket_kernel(ChunkArgs a) {
   float wv0[kBatch];
 #pragma unroll
   for (int u = 0; u < kBatch; ++u) {
-    ev0[u] = a.ids[min(p_begin + 64 * u + lane, P - 1)];
-    wv0[u] = a.wts[min(p_begin + 64 * u + lane, P - 1)];
+    ev0[u] = load_id<CO>(a.ids + min(p_begin + 64 * u + lane, P - 1));
+    wv0[u] = load_wt<CO>(a.wts + min(p_begin + 64 * u + lane, P - 1));
   }
   auto count = [&](int p0, const int* ev) {
 #pragma unroll
@@ -238,7 +276,7 @@ __global__ __launch_bounds__(1024) void bucket_kernel(ChunkArgs a) {
   for (int p0 = p_begin + 64 * kBatch; p0 < p_end; p0 += 64 * kBatch) {
     int ev[kBatch];
 #pragma unroll
-    for (int u = 0; u < kBatch; ++u) ev[u] = a.ids[min(p0 + 64 * u + lane, P - 1)];
+    for (int u = 0; u < kBatch; ++u) ev[u] = load_id<CO>(a.ids + min(p0 + 64 * u + lane, P - 1));
     count(p0, ev);
   }
   __syncthreads();
@@ -292,13 +330,17 @@ __global__ __launch_bounds__(1024) void bucket_kernel(ChunkArgs a) {
     // output row and column belongs to exactly one tile).  An expert's full
     // tiles take one run of slots.
     const int total = s_total;
+    constexpr int top = kTileRows / 32;  // the heaviest class: slots [0, n_top)
+    const int n_top = s_cls[0][top];
     for (int e = threadIdx.x; e < E; e += blockDim.x) {
       const int start = s_off[e];
       const int end = (e + 1 < E) ? s_off[e + 1] : total;
       const int nfull = (end - start) / kTileRows;
-      int ti = nfull ? atomicAdd(&s_cls[1][kTileRows / 32], nfull) : 0;
+      const bool tail_top = (end - start) % kTileRows != 0 && make_tile(e, 0, (end - start) % kTileRows).w == top;
+      const int run = nfull + (tail_top ? 1 : 0);  // the expert's tiles of the heaviest class
+      int ti = run ? atomicAdd(&s_cls[1][top], run) : 0;
       int r = start;
-      for (int i = 0; i < nfull; ++i, r += kTileRows) a.tiles[ti++] = make_tile(e, r, kTileRows);
+      for (int i = 0; i < run; ++i, r += kTileRows) a.tiles[top_slot(ti++, n_top)] = make_tile(e, r, min(kTileRows, end - r));
       if (r < end) {
         const int4 t = make_tile(e, r, end - r);
         a.tiles[atomicAdd(&s_cls[1][t.w], 1)] = t;
@@ -332,11 +374,57 @@ __global__ __launch_bounds__(1024) void bucket_kernel(ChunkArgs a) {
     float wv[kBatch];
 #pragma unroll
     for (int u = 0; u < kBatch; ++u) {
-      ev[u] = a.ids[min(p0 + 64 * u + lane, P - 1)];
-      wv[u] = a.wts[min(p0 + 64 * u + lane, P - 1)];
+      ev[u] = load_id<CO>(a.ids + min(p0 + 64 * u + lane, P - 1));
+      wv[u] = load_wt<CO>(a.wts + min(p0 + 64 * u + lane, P - 1));
     }
     scatter(p0, ev, wv);
   }
+}
+
+// caller-supplied routing (the routed half alone)
+__global__ __launch_bounds__(1024) void bucket_kernel(ChunkArgs a) { bucket_body<false>(a); }
+
+// ---------------------------------------------------------------------------
+// 2 + 3 in one launch (the complete block): each wave ranks one token as in
+// topk_kernel, and the last workgroup to finish, found with a device-scope
+// counter, sorts the pairs.  ids and weights are written with device-coherent
+// stores and acknowledged before the counter moves, and that workgroup reads
+// them back with device-coherent loads, so no L2 serves it a stale copy.  No
+// workgroup waits for another: the kernel always drains.
+// ---------------------------------------------------------------------------
+static constexpr int kTopkBucketWaves = 16;
+
+__global__ __launch_bounds__(64 * kTopkBucketWaves) void topk_bucket_kernel(ChunkArgs a) {
+  __shared__ TopkScratch sc[kTopkBucketWaves];
+  __shared__ int ids[kTopkBucketWaves][kMaxTopK];
+  __shared__ float w[kTopkBucketWaves][kMaxTopK];
+  __shared__ int s_last;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int t = blockIdx.x * kTopkBucketWaves + wave;
+  if (t < a.T) {
+    const int nrows = a.E + 1;
+    const float* lg = a.logits + (size_t)t * nrows;
+    const float gate = lg[a.E];
+    float v[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) v[j] = lg[min(4 * lane + j, a.E)];
+    wave_topk(v, a.E, a.k, ids[wave], w[wave], sc[wave]);
+    __builtin_amdgcn_wave_barrier();
+    if (lane < a.k) {
+      __hip_atomic_store(a.ids + (size_t)t * a.k + lane, ids[wave][lane], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(reinterpret_cast<uint32_t*>(a.wts) + (size_t)t * a.k + lane,
+                         __builtin_bit_cast(uint32_t, w[wave][lane]), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    if (lane == 0) a.sigma[t] = sigmoid_f(gate);
+  }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's stores are acknowledged
+  __syncthreads();
+  if (threadIdx.x == 0)
+    s_last = __hip_atomic_fetch_add(a.route_done, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == gridDim.x - 1;
+  __syncthreads();
+  if (!s_last) return;
+  if (threadIdx.x == 0) __hip_atomic_store(a.route_done, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  bucket_body<true>(a);
 }
 
 // ---------------------------------------------------------------------------
@@ -355,7 +443,7 @@ __global__ __launch_bounds__(1024) void bucket_kernel(ChunkArgs a) {
 // ---------------------------------------------------------------------------
 static constexpr int kKS = 128;
 static constexpr int kAStride = kKS + 8;       // halves per LDS row (padding against bank conflicts)
-static constexpr int kTilePF = 1;              // weight stages in flight in the 32-row-block path
+static constexpr int kTilePF = 1;  // weight stages in flight in the 32-row-block path (more spills at 256 VGPRs)
 
 template <int MT>
 struct AStage {
@@ -1052,13 +1140,28 @@ __global__ __launch_bounds__(256) void combine_kernel(ChunkArgs a) {
 // launchers
 // ---------------------------------------------------------------------------
 int launch_route_chunk(const ChunkArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL(router_gemm_kernel, dim3((a.T + 31) / 32, (a.E + 1 + 31) / 32), dim3(256), 0, s, a);
+  hipLaunchKernelGGL(router_gemm_kernel, dim3((a.T + 31) / 32, (a.E + 1 + 31) / 32), dim3(64 * kRouterWaves), 0, s, a);
   hipLaunchKernelGGL(topk_kernel, dim3((a.T + 3) / 4), dim3(256), 0, s, a);
   return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_LAUNCH;
 }
 
+static void launch_gemms(const ChunkArgs& a, hipStream_t s);
+
 int launch_experts_chunk(const ChunkArgs& a, hipStream_t s) {
   hipLaunchKernelGGL(bucket_kernel, dim3(1), dim3(1024), 0, s, a);
+  launch_gemms(a, s);
+  return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_LAUNCH;
+}
+
+int launch_forward_chunk(const ChunkArgs& a, hipStream_t s) {
+  hipLaunchKernelGGL(router_gemm_kernel, dim3((a.T + 31) / 32, (a.E + 1 + 31) / 32), dim3(64 * kRouterWaves), 0, s, a);
+  hipLaunchKernelGGL(topk_bucket_kernel, dim3((a.T + kTopkBucketWaves - 1) / kTopkBucketWaves),
+                     dim3(64 * kTopkBucketWaves), 0, s, a);
+  launch_gemms(a, s);
+  return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_LAUNCH;
+}
+
+static void launch_gemms(const ChunkArgs& a, hipStream_t s) {
   // grids over the item lists (tile count rounded up to a group of 8); blocks
   // beyond the items the bucketing produced exit at once
   const int max_tiles = (a.max_route_tiles + a.shared_tiles + 7) & ~7;
@@ -1067,7 +1170,6 @@ int launch_experts_chunk(const ChunkArgs& a, hipStream_t s) {
   hipLaunchKernelGGL(up_gemm_kernel, dim3((up_items + 7) & ~7), dim3(256), 0, s, a);
   hipLaunchKernelGGL(down_gemm_kernel, dim3((down_items + 7) & ~7), dim3(256), 0, s, a);
   hipLaunchKernelGGL(combine_kernel, dim3((a.H / 8 + 255) / 256, a.T), dim3(256), 0, s, a);
-  return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_LAUNCH;
 }
 
 }  // namespace moe

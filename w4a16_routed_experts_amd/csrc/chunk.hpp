@@ -35,9 +35,11 @@ struct ChunkArgs {
   int shared_tiles;    // number of kSharedRows-token shared-expert tiles (0: routed half only)
   int max_route_tiles; // bound on routed tiles for the grid
   int cus;             // compute units of the device (work pairing in the GEMM kernels)
+  uint32_t* route_done;  // counter of finished top-k workgroups (zero between calls)
 };
 
 int launch_route_chunk(const ChunkArgs& a, hipStream_t s);
 int launch_experts_chunk(const ChunkArgs& a, hipStream_t s);
+int launch_forward_chunk(const ChunkArgs& a, hipStream_t s);
 
 }  // namespace moe
