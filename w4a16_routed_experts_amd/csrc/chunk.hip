@@ -75,24 +75,44 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
 // 1. router GEMM: 32 tokens x 32 rows per workgroup; the kRouterWaves waves
 //    take interleaved 64-groups of K and are summed through LDS.  At hidden
 //    2048 each wave's four groups are one batch of loads, so the kernel waits
-//    on memory once.  The scales are applied per group to fp32 partial sums,
-//    so routing sees logits accurate to fp32 rounding.
+//    on memory once.  The loads are coalesced (consecutive lanes read
+//    consecutive 16-byte pieces of one row) and go through the wave's own LDS
+//    slice into the MFMA operand layout, where each lane works on its own row:
+//    loads in that layout make the texture addresser take the lanes one at a
+//    time.  The scales are applied per group to fp32 partial sums, so routing
+//    sees logits accurate to fp32 rounding.
 // ---------------------------------------------------------------------------
 static constexpr int kRouterWaves = 8;
+static constexpr int kRxStride = 9;  // 16-byte chunks per LDS row of activations (8 + 1 against bank conflicts)
+static constexpr int kRwStride = 5;  // ... of router codes (4 + 1)
 
 __global__ __launch_bounds__(64 * kRouterWaves) void router_gemm_kernel(ChunkArgs a) {
   __shared__ float red[kRouterWaves][16][64];
+  __shared__ uint4 stage[kRouterWaves][32 * (kRxStride + kRwStride)];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int m = lane & 31, g = lane >> 5;
-  const int t = blockIdx.x * 32 + m;  // A row (token)
-  const int r = blockIdx.y * 32 + m;  // B row (router row)
+  const int t0 = blockIdx.x * 32, r0 = blockIdx.y * 32;
+  const int r = r0 + m;  // B row (router row) of this MFMA lane
   const int nrows = a.E + 1, H = a.H, ngr = H / kGroup;
   const __amdgpu_buffer_rsrc_t rx = make_rsrc(a.x, (uint32_t)a.T * H * 2u);
   const __amdgpu_buffer_rsrc_t rq = make_rsrc(a.router_q, (uint32_t)nrows * H);
   const __amdgpu_buffer_rsrc_t rs = make_rsrc(a.router_s, (uint32_t)nrows * ngr * 2u);
-  const uint32_t xoff = t < a.T ? (uint32_t)t * H * 2u + 64u * g : kOob;  // lane's 32-half slice of a group
-  const uint32_t qoff = r < nrows ? (uint32_t)r * H + 32u * g : kOob;
+  // coalesced pieces: activations 32 rows x 8 chunks of a group (4 per lane),
+  // codes 32 rows x 4 chunks (2 per lane)
+  uint32_t xoff[4], qoff[2];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int idx = 64 * j + lane, row = idx >> 3;
+    xoff[j] = t0 + row < a.T ? (uint32_t)(t0 + row) * H * 2u + 16u * (idx & 7) : kOob;
+  }
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int idx = 64 * j + lane, row = idx >> 2;
+    qoff[j] = r0 + row < nrows ? (uint32_t)(r0 + row) * H + 16u * (idx & 3) : kOob;
+  }
   const uint32_t soff = r < nrows ? (uint32_t)r * ngr * 2u : kOob;
+  uint4* xs = stage[wave];
+  uint4* wsl = stage[wave] + 32 * kRxStride;
   f16v acc = {};
   constexpr int BATCH = 4;
   for (int g0 = wave; g0 < ngr; g0 += kRouterWaves * BATCH) {
@@ -104,23 +124,37 @@ __global__ __launch_bounds__(64 * kRouterWaves) void router_gemm_kernel(ChunkArg
       const bool ok = gi < ngr;  // uniform
       const uint32_t kx = ok ? 128u * gi : kOob, kq = ok ? 64u * gi : kOob, ks = ok ? 2u * gi : kOob;
 #pragma unroll
-      for (int q = 0; q < 4; ++q) xa[u][q] = __builtin_amdgcn_raw_buffer_load_b128(rx, xoff + kx + 16u * q, 0, 0);
+      for (int j = 0; j < 4; ++j) xa[u][j] = __builtin_amdgcn_raw_buffer_load_b128(rx, xoff[j] + kx, 0, 0);
 #pragma unroll
-      for (int q = 0; q < 2; ++q) wb[u][q] = __builtin_amdgcn_raw_buffer_load_b128(rq, qoff + kq + 16u * q, 0, 0);
+      for (int j = 0; j < 2; ++j) wb[u][j] = __builtin_amdgcn_raw_buffer_load_b128(rq, qoff[j] + kq, 0, 0);
       sc[u] = __builtin_amdgcn_raw_buffer_load_b16(rs, soff + ks, 0, 0);
     }
     __builtin_amdgcn_sched_barrier(0);  // the whole batch in flight before any use
 #pragma unroll
     for (int u = 0; u < BATCH; ++u) {
-      f16v p = {};
-      const uint32_t ws[8] = {wb[u][0].x, wb[u][0].y, wb[u][0].z, wb[u][0].w,
-                              wb[u][1].x, wb[u][1].y, wb[u][1].z, wb[u][1].w};
+      // the wave's slice: written by all its lanes, then read in MFMA layout
+      // (LDS operations of one wave complete in order)
 #pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        h2 w[4];
-        int8x8_to_h2x4(ws[2 * s], ws[2 * s + 1], w);
-        p = __builtin_amdgcn_mfma_f32_32x32x16_f16(act_operand(xa[u][s]), pack8(w), p, 0, 0, 0);
+      for (int j = 0; j < 4; ++j) {
+        const int idx = 64 * j + lane;
+        xs[(idx >> 3) * kRxStride + (idx & 7)] = __builtin_bit_cast(uint4, act_operand(xa[u][j]));
       }
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int idx = 64 * j + lane;
+        wsl[(idx >> 2) * kRwStride + (idx & 3)] = __builtin_bit_cast(uint4, wb[u][j]);
+      }
+      __builtin_amdgcn_wave_barrier();
+      f16v p = {};
+#pragma unroll
+      for (int st = 0; st < 4; ++st) {
+        const h8 av = __builtin_bit_cast(h8, xs[m * kRxStride + 4 * g + st]);
+        const uint2 wq = reinterpret_cast<const uint2*>(wsl + m * kRwStride + 2 * g + (st >> 1))[st & 1];
+        h2 w[4];
+        int8x8_to_h2x4(wq.x, wq.y, w);
+        p = __builtin_amdgcn_mfma_f32_32x32x16_f16(av, pack8(w), p, 0, 0, 0);
+      }
+      __builtin_amdgcn_wave_barrier();
       const float scf = half_bits_to_float(sc[u]);
 #pragma unroll
       for (int i = 0; i < 16; ++i) acc[i] = fmaf(p[i], scf, acc[i]);
@@ -132,7 +166,7 @@ __global__ __launch_bounds__(64 * kRouterWaves) void router_gemm_kernel(ChunkArg
   if (wave == 0 && r < nrows) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-      const int tt = blockIdx.x * 32 + acc_row(i);
+      const int tt = t0 + acc_row(i);
       float v = 0.f;
 #pragma unroll
       for (int w2 = 0; w2 < kRouterWaves; ++w2) v += red[w2][i][lane];
