@@ -160,6 +160,30 @@ def time_config(cfg, steps, warmup, R, torch, m, gen, per_launch_events):
         durs = np.array([a.elapsed_time(b) for a, b in ev]) * 1e3
         res["us_per_launch"] = float(durs.mean())
         res["us_per_launch_median"] = float(np.median(durs))
+
+        # the same steps replayed from one HIP graph (R steps captured, one per
+        # weight copy); informational beside the plain-stream figure.  Every
+        # replay ends with the same output as eager execution, which is checked.
+        try:
+            torch.cuda.synchronize()
+            want = out.clone()
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                cs = torch.cuda.current_stream().cuda_stream
+                for s in range(R):
+                    fwd(*(args[s][:-1] + (cs,)))
+            g.replay()
+            torch.cuda.synchronize()
+            reps = max(1, n // R)
+            e0.record(stream)
+            for _ in range(reps):
+                g.replay()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            res["us_per_step_graph"] = e0.elapsed_time(e1) * 1e3 / (reps * R)
+            res["graph_matches_eager"] = bool(torch.equal(out, want))
+        except Exception as ex:  # a runtime without graph capture: report, do not fail
+            res["graph_error"] = repr(ex)
     del copies
     torch.cuda.empty_cache()
     return res
@@ -293,6 +317,9 @@ def main():
                      "kernel": "decode_kernel<0> (the whole layer in one launch)",
                      "algorithmic_bytes_per_launch": b1, "us_per_launch": round(us_launch, 3),
                      "us_per_launch_event_pairs": round(r1["us_per_launch"], 3),
+                     "us_per_step_hip_graph": (round(r1["us_per_step_graph"], 3) if "us_per_step_graph" in r1
+                                               else r1.get("graph_error")),
+                     "hip_graph_matches_eager": r1.get("graph_matches_eager"),
                      "mfma_pct": round(100 * f1 / (us_launch * 1e-6) / (MFMA_F16_PEAK_TFLOPS * 1e12), 4)},
         "chunk_t512": {"workload": "512-token chunk, Zipf(1.1) expert popularity, same widths",
                        "tokens_per_s": round(r4["T"] / t4, 1), "us_per_step": round(r4["us_per_step"], 3),
