@@ -20,4 +20,7 @@ from .ref import (  # noqa: F401
     forward_dense,
     routed_expert_weights,
     swiglu_ffn,
+    f64_to_half_bits,
+    rmsnorm,
+    block_forward,
 )

@@ -12,6 +12,9 @@ What it computes (all in float64, no intermediate rounding):
 * The router ordering (same notebook, section 5.2): softmax over the router
   logits, then top-k, then renormalise the k kept probabilities; SwiGLU
   experts; the sigmoid output gate.
+* The MoE sub-block of a decoder layer (the Chimera notebook, sections 7 and
+  10, the decoder-layer assemblies): post-attention RMSNorm, the MoE block on
+  the normalised activations, then the residual add.
 * The router and the shared-gate row are stored 8-bit, group-64 rows, stacked
   (the TensorFold PR, "Design").  Routed experts int4, shared expert int8,
   activations fp16 (the Chimera notebook, pipeline intro and "Key takeaways").
@@ -20,7 +23,9 @@ Readings where the pages are silent (each is stated where it is used):
 top-k ties go to the lower expert index; int4 codes are two's-complement
 nibbles with the even element in the low nibble; a dequantised weight is
 code x scale with one binary16 scale per 64 consecutive K elements of a row;
-there is no router bias term and no zero point.
+there is no router bias term and no zero point; the RMSNorm is
+h / sqrt(mean(h^2) + eps) * gain with the gain vector as applied, and its output
+is rounded to binary16 (the MoE input everywhere else) before the block.
 
 Every function below is pinned by the ``-m "not gpu"`` tests (hand-derived
 fixtures, brute force, closed forms and invariants).
@@ -209,3 +214,38 @@ def forward_dense(x_bits, W, dims) -> np.ndarray:
         w13, w2 = routed_expert_weights(W, dims, e)
         routed += gates[:, e : e + 1] * swiglu_ffn(X, w13, w2, dims.I)
     return routed + sigmoid(lg[:, dims.E])[:, None] * shared_expert(x_bits, W, dims)
+
+
+# ---------------------------------------------------------------------------
+# the MoE sub-block of a decoder layer: RMSNorm -> MoE block -> residual add
+# ---------------------------------------------------------------------------
+
+
+def f64_to_half_bits(v) -> np.ndarray:
+    """float64 -> binary16 bit patterns, rounded to nearest even."""
+    return np.asarray(v, dtype=np.float64).astype(np.float16).view(np.uint16)
+
+
+def rmsnorm(h_bits, gain_bits, eps: float) -> np.ndarray:
+    """Post-attention RMSNorm (the Chimera notebook, sections 7 and 10: the
+    norm in front of the MoE FFN), float64 [T, H]: each token's row divided by
+    the square root of (the mean of its squares + eps), times the gain vector."""
+    X = half_bits_to_f64(h_bits)
+    g = half_bits_to_f64(gain_bits)
+    ms = np.mean(X * X, axis=1, keepdims=True)
+    return X / np.sqrt(ms + eps) * g
+
+
+def block_forward(h_bits, gain_bits, eps: float, W, dims):
+    """The MoE sub-block (same sections: post-attn RMSNorm -> MoE FFN ->
+    residual): a = binary16(rmsnorm(h)), out = h + forward(a)["out"].
+
+    Returns forward's dict with out replaced by the sub-block's output, the
+    block's own output as moe, and the normalised activations as a_bits.
+    """
+    a_bits = f64_to_half_bits(rmsnorm(h_bits, gain_bits, eps))
+    r = forward(a_bits, W, dims)
+    r["moe"] = r["out"]
+    r["out"] = half_bits_to_f64(h_bits) + r["moe"]
+    r["a_bits"] = a_bits
+    return r

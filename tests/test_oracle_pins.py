@@ -335,3 +335,90 @@ def test_planted_mistakes_are_caught(monkeypatch, name, attr, bad):
     monkeypatch.setattr(ref, attr, bad)
     with pytest.raises(AssertionError):
         _check_hand_case(ref.forward)
+
+
+# ---------------------------------------------------------------------------
+# the MoE sub-block: post-attention RMSNorm -> block -> residual add
+# ---------------------------------------------------------------------------
+
+
+def _rmsnorm_pins(norm):
+    # hand-derived: h = (3, 4), gain = (1, 2), eps = 0 -> mean of squares 12.5
+    h = f16_bits(np.array([[3.0, 4.0]]))
+    g = f16_bits(np.array([1.0, 2.0]))
+    want = np.array([[3.0, 8.0]]) / math.sqrt(12.5)
+    assert np.abs(norm(h, g, 0.0) - want).max() < 1e-15
+    # constant row c with eps > 0: sign(c) * gain / sqrt(1 + eps / c^2)
+    c, eps = -0.25, 1e-2
+    hc = f16_bits(np.full((1, 64), c))
+    gc = f16_bits(np.linspace(0.5, 1.5, 64))
+    want_c = -ref.half_bits_to_f64(gc) / math.sqrt(1.0 + eps / c ** 2)
+    assert np.abs(norm(hc, gc, eps)[0] - want_c).max() < 1e-15
+    # with eps = 0 a power-of-two scaling of a row changes nothing, exactly
+    rng = np.random.default_rng(11)
+    x = rng.standard_normal((3, 128))
+    hx, hy = f16_bits(x), f16_bits(x * 8.0)
+    gr = f16_bits(rng.uniform(0.5, 1.5, 128))
+    assert np.array_equal(norm(hx, gr, 0.0), norm(hy, gr, 0.0))
+
+
+def test_rmsnorm_pins():
+    _rmsnorm_pins(ref.rmsnorm)
+
+
+def _block_pins(block):
+    case = _tiny_case(seed=21, T=4)
+    d = case.dims
+    # a row of +-1 has unit RMS: with gain 1 and eps 0 the normalised
+    # activations are the row itself, so the sub-block is h + the block of h
+    signs = np.where(np.random.default_rng(3).random((4, d.H)) < 0.5, -1.0, 1.0)
+    h = f16_bits(signs)
+    ones = f16_bits(np.ones(d.H))
+    r = block(h, ones, 0.0, case.weights, d)
+    assert np.array_equal(r["a_bits"], h)
+    assert np.abs(r["out"] - (signs + ref.forward(h, case.weights, d)["out"])).max() < 1e-12
+    # all-zero routed and shared weights: the output is the residual exactly
+    W0 = Weights(**{f: (np.zeros_like(v) if f in ("w13_q", "w2_q", "sh13_q", "sh2_q") else v)
+                    for f, v in case.weights.items()})
+    h2 = f16_bits(np.random.default_rng(4).standard_normal((4, d.H)) * 3.0)
+    r0 = block(h2, ones, 1e-6, W0, d)
+    assert np.array_equal(r0["out"], ref.half_bits_to_f64(h2))
+
+
+def test_block_forward_pins():
+    _block_pins(ref.block_forward)
+
+
+def _norm_sum_not_mean(h_bits, gain_bits, eps):
+    X = ref.half_bits_to_f64(h_bits)
+    return X / np.sqrt(np.sum(X * X, axis=1, keepdims=True) + eps) * ref.half_bits_to_f64(gain_bits)
+
+
+def _norm_eps_outside(h_bits, gain_bits, eps):
+    X = ref.half_bits_to_f64(h_bits)
+    return X / (np.sqrt(np.mean(X * X, axis=1, keepdims=True)) + eps) * ref.half_bits_to_f64(gain_bits)
+
+
+def _norm_no_gain(h_bits, gain_bits, eps):
+    X = ref.half_bits_to_f64(h_bits)
+    return X / np.sqrt(np.mean(X * X, axis=1, keepdims=True) + eps)
+
+
+@pytest.mark.parametrize("name,bad", [
+    ("sum of squares instead of mean", _norm_sum_not_mean),
+    ("eps outside the square root", _norm_eps_outside),
+    ("gain dropped", _norm_no_gain),
+])
+def test_planted_rmsnorm_mistakes_are_caught(monkeypatch, name, bad):
+    monkeypatch.setattr(ref, "rmsnorm", bad)
+    with pytest.raises(AssertionError):
+        _rmsnorm_pins(ref.rmsnorm)
+
+
+def test_planted_residual_mistake_is_caught():
+    def no_residual(h_bits, gain_bits, eps, W, dims):
+        r = ref.block_forward(h_bits, gain_bits, eps, W, dims)
+        r["out"] = r["moe"]
+        return r
+    with pytest.raises(AssertionError):
+        _block_pins(no_residual)
