@@ -136,6 +136,21 @@ MOE_API int moe_forward(const moe_dims* dims, const moe_weights* w, const uint16
                         int32_t* ids, float* weights, float* shared_gate, void* ws, size_t ws_bytes,
                         hipStream_t stream);
 
+/* The MoE sub-block of a decoder layer (the Chimera notebook, sections 7 and
+ * 10: post-attention RMSNorm -> MoE FFN -> residual), fused into the block:
+ *   a[t]   = binary16( h[t] / sqrt(mean_j h[t][j]^2 + eps) * gain )
+ *   out[t] = binary16( h[t] + moe_forward's block applied to a[t] )
+ * with one rounding of out.
+ *   h     [T][H] binary16, the residual stream (16-byte aligned; must not alias out)
+ *   gain  [H] binary16, the norm's multiplier as applied (16-byte aligned); a
+ *         model that stores w for a (1 + w) multiplier passes 1 + w
+ *   eps   finite, >= 0; anything else is refused with MOE_ERR_SHAPE
+ * ids, weights and shared_gate receive the routing of a[t] when non-NULL, as
+ * for moe_forward. */
+MOE_API int moe_block_forward(const moe_dims* dims, const moe_weights* w, const uint16_t* h, const uint16_t* gain,
+                              float eps, int32_t T, uint16_t* out, int32_t* ids, float* weights,
+                              float* shared_gate, void* ws, size_t ws_bytes, hipStream_t stream);
+
 /* Static description of a status code. */
 MOE_API const char* moe_status_string(int status);
 

@@ -42,7 +42,8 @@ def _weights(addr=FAKE, **override):
 def test_every_declared_symbol_is_exported(L):
     text = open(HEADER).read()
     names = re.findall(r"MOE_API\s+[\w\s\*]+?\b(moe_\w+)\s*\(", text)
-    assert set(names) == {"moe_workspace_bytes", "moe_route", "moe_experts_w4a16", "moe_forward", "moe_status_string"}
+    assert set(names) == {"moe_workspace_bytes", "moe_route", "moe_experts_w4a16", "moe_forward", "moe_block_forward",
+                          "moe_status_string"}
     for n in names:
         assert hasattr(L, n), n
 
@@ -107,6 +108,27 @@ def test_refusals_route_and_experts(L):
     Wr = _weights(router_q=None, router_s=None, sh13_q=None, sh13_s=None, sh2_q=None, sh2_s=None, w2_q=None)
     r = L.moe_experts_w4a16(ctypes.byref(d), ctypes.byref(Wr), FAKE, 1, FAKE, FAKE, FAKE, FAKE, 1 << 30, None)
     assert r == -1
+
+
+def _block(L, dims, W, h=FAKE, gain=FAKE + (1 << 20), eps=1e-6, T=1, out=FAKE + (2 << 20), ws=FAKE, ws_bytes=1 << 30):
+    return L.moe_block_forward(ctypes.byref(dims), ctypes.byref(W) if W is not None else None, h, gain, eps, T, out,
+                               None, None, None, ws, ws_bytes, None)
+
+
+def test_refusals_block_forward(L):
+    d, W = _dims(), _weights()
+    assert _block(L, d, W, gain=None) == -1
+    assert _block(L, d, W, h=None) == -1
+    assert _block(L, d, W, out=None) == -1
+    assert _block(L, d, _weights(sh2_s=None)) == -1
+    assert _block(L, d, W, gain=FAKE + (1 << 20) + 2) == -3
+    assert _block(L, d, W, eps=-1.0) == -2
+    assert _block(L, d, W, eps=float("nan")) == -2
+    assert _block(L, d, W, eps=float("inf")) == -2
+    assert _block(L, d, W, out=FAKE) == -2                          # out is the residual stream itself
+    assert _block(L, d, W, T=4, out=FAKE + 2048 * 2 * 3) == -2      # out overlaps its last row
+    assert _block(L, d, W, T=7, ws_bytes=m.moe_workspace_bytes(d, 7) - 1) == -4
+    assert L.moe_block_forward(ctypes.byref(d), None, None, None, 0.0, 0, None, None, None, None, None, 0, None) == 0
 
 
 def test_zero_tokens_is_a_noop(L):

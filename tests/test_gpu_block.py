@@ -1,0 +1,92 @@
+"""GPU parity of the MoE sub-block (post-attention RMSNorm -> block -> residual
+add) against the float64 oracle's block_forward, on both paths."""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+import w4a16_routed_experts_amd as m  # noqa: E402
+from oracle import ref  # noqa: E402
+from tests import _gpu  # noqa: E402
+from workloads import gen  # noqa: E402
+from workloads.gen import f16_bits  # noqa: E402
+
+EPS = 1e-6
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu_present():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    m.lib()
+
+
+def _inputs(case, seed):
+    """Residual rows at varied scales (the norm has work to do) and a gain vector."""
+    rng = np.random.default_rng(seed)
+    scale = rng.uniform(0.25, 4.0, size=(case.T, 1))
+    h_bits = f16_bits(gen_x(case) * scale)
+    gain_bits = f16_bits(rng.uniform(0.5, 1.5, size=case.dims.H))
+    return h_bits, gain_bits
+
+
+def gen_x(case):
+    return ref.half_bits_to_f64(case.x)
+
+
+def _run_block(case, h_bits, gain_bits, flags):
+    T, d = case.T, case.dims
+    dims = _gpu.dims_of(d, flags)
+    W = _gpu.device_weights(case)
+    h = torch.from_numpy(h_bits.view(np.int16)).cuda()
+    g = torch.from_numpy(gain_bits.view(np.int16)).cuda()
+    out = torch.full((T, d.H), 0x7E00, dtype=torch.int16, device="cuda")  # NaN fill
+    ids = torch.full((T, d.k), -7, dtype=torch.int32, device="cuda")
+    w = torch.full((T, d.k), -1.0, dtype=torch.float32, device="cuda")
+    sig = torch.full((T,), -1.0, dtype=torch.float32, device="cuda")
+    ws = m.workspace(dims, T)
+    m.moe_block_forward(dims, W.struct, h, g, EPS, T, out, ids, w, sig, ws)
+    torch.cuda.synchronize()
+    assert torch.equal(h.cpu(), torch.from_numpy(h_bits.view(np.int16))), "the residual stream was modified"
+    return dict(out=_gpu.half_to_f64(out), ids=ids.cpu().numpy(), w=w.cpu().numpy().astype(np.float64),
+                sigma=sig.cpu().numpy().astype(np.float64))
+
+
+def _check(case, h_bits, gain_bits, gpu, label):
+    d = case.dims
+    r = ref.block_forward(h_bits, gain_bits, EPS, case.weights, d)
+    differ = _gpu.check_routing(case, r, gpu, label)
+    want = r["out"].copy()
+    lr = r["logits"][:, : d.E]
+    for t in differ:  # near-tie rows the GPU routed otherwise: the oracle with the GPU's ids
+        ids_g = gpu["ids"][t : t + 1].astype(np.int64)
+        w_g = ref.softmax_renormalised(lr[t : t + 1], ids_g)
+        routed = ref.experts(r["a_bits"][t : t + 1], ids_g, w_g, case.weights, d)
+        want[t] = ref.half_bits_to_f64(h_bits[t]) + routed[0] + r["sigma"][t] * r["shared"][t]
+    err = _gpu.row_rel_l2(gpu["out"], want)
+    _gpu.log(f"{label}: per-row rel L2 max {err.max():.3e} median {np.median(err):.3e}")
+    assert np.all(np.isfinite(gpu["out"])), f"{label}: non-finite output"
+    assert err.max() <= _gpu.ROW_TOL, f"{label}: row {int(err.argmax())} rel L2 {err.max():.3e}"
+
+
+@pytest.mark.parametrize("cfg,flags", [(0, m.PATH_AUTO), (1, m.PATH_AUTO), (2, m.PATH_AUTO), (3, m.PATH_AUTO),
+                                       (4, m.PATH_AUTO), (0, m.PATH_CHUNK), (1, m.PATH_CHUNK)])
+def test_block_configs(cfg, flags):
+    case = _gpu.config_case(cfg)
+    _gpu.log(f"sub-block config {cfg} ({case.name}) T={case.T} flags={flags}")
+    h_bits, gain_bits = _inputs(case, 700 + cfg)
+    gpu = _run_block(case, h_bits, gain_bits, flags)
+    _check(case, h_bits, gain_bits, gpu, f"block-cfg{cfg}-f{flags}")
+
+
+@pytest.mark.parametrize("T,flags", [(3, m.PATH_DECODE), (3, m.PATH_CHUNK), (70, m.PATH_AUTO)])
+def test_block_token_counts(T, flags):
+    case = gen.make_case(gen.REAL, T, seed=7100 + T, real_experts=True)
+    _gpu.log(f"sub-block T={T} flags={flags}")
+    h_bits, gain_bits = _inputs(case, 7200 + T)
+    gpu = _run_block(case, h_bits, gain_bits, flags)
+    _check(case, h_bits, gain_bits, gpu, f"block-T{T}-f{flags}")

@@ -64,6 +64,8 @@ def lib() -> ctypes.CDLL:
         L.moe_experts_w4a16.restype = ctypes.c_int
         L.moe_forward.argtypes = [dims_p, w_p, vp, i32, vp, vp, vp, vp, vp, sz, vp]
         L.moe_forward.restype = ctypes.c_int
+        L.moe_block_forward.argtypes = [dims_p, w_p, vp, vp, ctypes.c_float, i32, vp, vp, vp, vp, vp, sz, vp]
+        L.moe_block_forward.restype = ctypes.c_int
         _lib = L
     return _lib
 
@@ -137,6 +139,14 @@ def moe_forward(dims, weights, x, T, out, ids=None, w=None, shared_gate=None, ws
     st = lib().moe_forward(ctypes.byref(dims), ctypes.byref(weights), _ptr(x), T, _ptr(out), _ptr(ids), _ptr(w),
                            _ptr(shared_gate), _ptr(ws), _nbytes(ws), _stream(stream))
     return _check(st, "moe_forward", raise_on_error)
+
+
+def moe_block_forward(dims, weights, h, gain, eps, T, out, ids=None, w=None, shared_gate=None, ws=None, stream=None,
+                      raise_on_error=True) -> int:
+    st = lib().moe_block_forward(ctypes.byref(dims), ctypes.byref(weights), _ptr(h), _ptr(gain), float(eps), T,
+                                 _ptr(out), _ptr(ids), _ptr(w), _ptr(shared_gate), _ptr(ws), _nbytes(ws),
+                                 _stream(stream))
+    return _check(st, "moe_block_forward", raise_on_error)
 
 
 class DeviceWeights:

@@ -117,6 +117,7 @@ void carve_chunk(const moe_dims* d, int T, Carve& c, ChunkArgs& a) {
   a.hs = c.take<_Float16>((size_t)T * d->shared_inter * 2);
   a.y = c.take<_Float16>(P * d->hidden * 2);
   a.ys = c.take<_Float16>((size_t)T * d->hidden * 2);
+  a.xn = c.take<uint16_t>((size_t)T * d->hidden * 2);
 }
 
 size_t workspace_bytes(const moe_dims* d, int T) {
@@ -177,7 +178,7 @@ void fill_weights(const moe_weights* w, int8_t const** rq, uint16_t const** rs, 
 
 int run_decode(const moe_dims* d, const moe_weights* w, const uint16_t* x, int T, uint16_t* out, int mode,
                int32_t* ids_out, float* w_out, float* sig_out, const int32_t* ids_in, const float* w_in, void* ws,
-               hipStream_t s) {
+               hipStream_t s, const uint16_t* gain = nullptr, float eps = 0.f) {
   DeviceInfo* di = nullptr;
   int st = device_info(&di);
   if (st != MOE_OK) return st;
@@ -186,6 +187,7 @@ int run_decode(const moe_dims* d, const moe_weights* w, const uint16_t* x, int T
   fill_weights(w, &a.router_q, &a.router_s, &a.w13_q, &a.w13_s, &a.w2_q, &a.w2_s, &a.sh13_q, &a.sh13_s, &a.sh2_q,
                &a.sh2_s);
   a.x = x; a.out = out;
+  a.gain = gain; a.eps = eps;
   a.ids_out = ids_out; a.w_out = w_out; a.sigma_out = sig_out;
   a.ids_in = ids_in; a.w_in = w_in;
   Carve c{static_cast<char*>(ws)};
@@ -206,7 +208,7 @@ ChunkArgs chunk_args(const moe_dims* d, const moe_weights* w, const uint16_t* x,
   a.H = d->hidden; a.E = d->num_experts; a.k = d->top_k; a.I = d->expert_inter; a.Is = d->shared_inter; a.T = T;
   fill_weights(w, &a.router_q, &a.router_s, &a.w13_q, &a.w13_s, &a.w2_q, &a.w2_s, &a.sh13_q, &a.sh13_s, &a.sh2_q,
                &a.sh2_s);
-  a.x = x; a.out = out;
+  a.x = x; a.xa = x; a.out = out;
   Carve c{static_cast<char*>(ws)};
   carve_chunk(d, T, c, a);
   a.max_route_tiles = max_route_tiles(d, T);
@@ -322,6 +324,43 @@ MOE_API int moe_forward(const moe_dims* dims, const moe_weights* w, const uint16
   if (ids) a.ids = ids;
   if (weights) a.wts = weights;
   if (shared_gate) a.sigma = shared_gate;
+  a.shared_tiles = (T + kSharedRows - 1) / kSharedRows;
+  a.cus = di->cus;
+  return launch_forward_chunk(a, stream);
+}
+
+MOE_API int moe_block_forward(const moe_dims* dims, const moe_weights* w, const uint16_t* h, const uint16_t* gain,
+                              float eps, int32_t T, uint16_t* out, int32_t* ids, float* weights,
+                              float* shared_gate, void* ws, size_t ws_bytes, hipStream_t stream) {
+  int st = check_common(dims, h, T, ws, ws_bytes);
+  if (st != MOE_OK || T == 0) return st;
+  if (!w) return MOE_ERR_NULL;
+  if (any_null({w->router_q, w->router_s, w->w13_q, w->w13_s, w->w2_q, w->w2_s, w->sh13_q, w->sh13_s, w->sh2_q,
+                w->sh2_s, out, gain}))
+    return MOE_ERR_NULL;
+  if (!all16({w->router_q, w->router_s, w->w13_q, w->w13_s, w->w2_q, w->w2_s, w->sh13_q, w->sh13_s, w->sh2_q,
+              w->sh2_s, out, gain}) ||
+      !all4({ids, weights, shared_gate}))
+    return MOE_ERR_ALIGN;
+  if (!(eps >= 0.f && eps <= 3.0e38f)) return MOE_ERR_SHAPE;  // also refuses NaN and infinity
+  {
+    const uintptr_t hb = reinterpret_cast<uintptr_t>(h), ob = reinterpret_cast<uintptr_t>(out);
+    const uintptr_t n = (uintptr_t)T * dims->hidden * 2;
+    if (hb < ob + n && ob < hb + n) return MOE_ERR_SHAPE;  // out overlaps the residual stream
+  }
+  if (use_decode(dims, T))
+    return run_decode(dims, w, h, T, out, DEC_FORWARD, ids, weights, shared_gate, nullptr, nullptr, ws, stream, gain,
+                      eps);
+  DeviceInfo* di = nullptr;
+  if ((st = device_info(&di)) != MOE_OK) return st;
+  ChunkArgs a = chunk_args(dims, w, h, T, out, ws);
+  if (ids) a.ids = ids;
+  if (weights) a.wts = weights;
+  if (shared_gate) a.sigma = shared_gate;
+  a.gain = gain;
+  a.eps = eps;
+  a.xa = a.xn;   // the expert GEMMs read the normalised activations the router GEMM writes
+  a.resid = h;   // and the combine adds the residual stream
   a.shared_tiles = (T + kSharedRows - 1) / kSharedRows;
   a.cus = di->cus;
   return launch_forward_chunk(a, stream);

@@ -111,12 +111,51 @@ __global__ __launch_bounds__(64 * kRouterWaves) void router_gemm_kernel(ChunkArg
     qoff[j] = r0 + row < nrows ? (uint32_t)(r0 + row) * H + 16u * (idx & 3) : kOob;
   }
   const uint32_t soff = r < nrows ? (uint32_t)r * ngr * 2u : kOob;
+  // The sub-block (the Chimera notebook, sections 7 and 10: post-attention
+  // RMSNorm in front of the block): a first pass sums each token's squares
+  // (fixed order, so every row block derives the same binary16 activations);
+  // the GEMM then scales each activation piece by its token's reciprocal RMS
+  // and the gain, and the first row block writes them out for the expert GEMMs.
+  __shared__ float s_rn[32];
+  const bool sub = a.gain != nullptr;  // uniform
+  const __amdgpu_buffer_rsrc_t rg = make_rsrc(a.gain, sub ? (uint32_t)H * 2u : 0u);
+  if (sub) {
+    float ss[4] = {0.f, 0.f, 0.f, 0.f};
+    for (int gi = wave; gi < ngr; gi += kRouterWaves) {
+      u32x4 v[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) v[j] = __builtin_amdgcn_raw_buffer_load_b128(rx, xoff[j] + 128u * gi, 0, 0);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const h8 hv = __builtin_bit_cast(h8, v[j]);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) ss[j] = fmaf((float)hv[i], (float)hv[i], ss[j]);
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {  // the 8 lanes of one row (lanes 8m .. 8m + 7)
+      ss[j] += __shfl_xor(ss[j], 1, 64);
+      ss[j] += __shfl_xor(ss[j], 2, 64);
+      ss[j] += __shfl_xor(ss[j], 4, 64);
+      if ((lane & 7) == 0) red[wave][j][lane >> 3] = ss[j];
+    }
+    __syncthreads();
+    if (threadIdx.x < 32) {
+      const int row = threadIdx.x;
+      float t = 0.f;
+#pragma unroll
+      for (int w2 = 0; w2 < kRouterWaves; ++w2) t += red[w2][row >> 3][row & 7];
+      s_rn[row] = 1.0f / sqrtf(t / (float)H + a.eps);
+    }
+    __syncthreads();
+  }
+  const __amdgpu_buffer_rsrc_t rxn = make_rsrc(a.xn, sub && blockIdx.y == 0 ? (uint32_t)a.T * H * 2u : 0u);
   uint4* xs = stage[wave];
   uint4* wsl = stage[wave] + 32 * kRxStride;
   f16v acc = {};
   constexpr int BATCH = 4;
   for (int g0 = wave; g0 < ngr; g0 += kRouterWaves * BATCH) {
-    u32x4 xa[BATCH][4], wb[BATCH][2];
+    u32x4 xa[BATCH][4], wb[BATCH][2], gn[BATCH];
     uint16_t sc[BATCH];
 #pragma unroll
     for (int u = 0; u < BATCH; ++u) {
@@ -128,10 +167,24 @@ __global__ __launch_bounds__(64 * kRouterWaves) void router_gemm_kernel(ChunkArg
 #pragma unroll
       for (int j = 0; j < 2; ++j) wb[u][j] = __builtin_amdgcn_raw_buffer_load_b128(rq, qoff[j] + kq, 0, 0);
       sc[u] = __builtin_amdgcn_raw_buffer_load_b16(rs, soff + ks, 0, 0);
+      gn[u] = __builtin_amdgcn_raw_buffer_load_b128(rg, ok ? 128u * gi + 16u * (lane & 7) : kOob, 0, 0);
     }
     __builtin_amdgcn_sched_barrier(0);  // the whole batch in flight before any use
 #pragma unroll
     for (int u = 0; u < BATCH; ++u) {
+      if (sub) {  // binary16(x * rsqrt(mean x^2 + eps) * gain), kept for the expert GEMMs
+        const h8 gv = __builtin_bit_cast(h8, gn[u]);
+        const int gi = g0 + kRouterWaves * u;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const float rn = s_rn[(64 * j + lane) >> 3];
+          h8 hv = __builtin_bit_cast(h8, xa[u][j]);
+#pragma unroll
+          for (int i = 0; i < 8; ++i) hv[i] = (_Float16)((float)hv[i] * rn * (float)gv[i]);
+          xa[u][j] = __builtin_bit_cast(u32x4, hv);
+          if (gi < ngr) __builtin_amdgcn_raw_buffer_store_b128(xa[u][j], rxn, xoff[j] + 128u * gi, 0, 0);
+        }
+      }
       // the wave's slice: written by all its lanes, then read in MFMA layout
       // (LDS operations of one wave complete in order)
 #pragma unroll
@@ -949,7 +1002,7 @@ __global__ __launch_bounds__(256, 2) void up_gemm_kernel(ChunkArgs a) {
     tr.out_row[r] = r0 + r;
   }
   __syncthreads();
-  const __amdgpu_buffer_rsrc_t ra = make_rsrc(a.x, (uint32_t)a.T * a.H * 2u);
+  const __amdgpu_buffer_rsrc_t ra = make_rsrc(a.xa, (uint32_t)a.T * a.H * 2u);
   if (e >= 0) {
     const uint8_t* wq = a.w13_q + (size_t)e * 2 * a.I * (a.H / 2);
     const uint16_t* wsc = a.w13_s + (size_t)e * 2 * a.I * (a.H / kGroup);
@@ -1161,6 +1214,7 @@ __global__ __launch_bounds__(256) void combine_kernel(ChunkArgs a) {
     v[i] = *reinterpret_cast<const uint4*>(a.y + (size_t)p * a.H + n);
   }
   if (a.ys) add8(acc, *reinterpret_cast<const uint4*>(a.ys + (size_t)t * a.H + n));
+  if (a.resid) add8(acc, *reinterpret_cast<const uint4*>(a.resid + (size_t)t * a.H + n));
 #pragma unroll
   for (int i = 0; i < kMaxTopK; ++i)
     if (i < a.k && id[i] >= 0 && id[i] < a.E) add8(acc, v[i]);

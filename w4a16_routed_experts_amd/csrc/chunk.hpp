@@ -16,8 +16,13 @@ struct ChunkArgs {
   const uint8_t* w2_q; const uint16_t* w2_s;
   const int8_t* sh13_q; const uint16_t* sh13_s;
   const int8_t* sh2_q; const uint16_t* sh2_s;
-  const uint16_t* x;   // [T][H]
+  const uint16_t* x;   // [T][H] router input (the residual stream in the sub-block)
+  const uint16_t* xa;  // [T][H] activations of the expert GEMMs: x, or xn in the sub-block
   uint16_t* out;       // [T][H]
+  const uint16_t* gain;  // sub-block: RMSNorm gain [H], or null
+  float eps;             // sub-block: RMSNorm epsilon
+  uint16_t* xn;          // sub-block: normalised activations [T][H], written by the router GEMM
+  const uint16_t* resid; // sub-block: residual added by the combine, or null
   float* logits;       // [T][E+1]
   int32_t* ids;        // [T][k]
   float* wts;          // [T][k]

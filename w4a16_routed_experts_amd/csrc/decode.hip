@@ -421,6 +421,27 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
 
   copy_halves(act, a.x, T * H);
   __syncthreads();
+  if (a.gain) {
+    // The sub-block (the Chimera notebook, sections 7 and 10: post-attention
+    // RMSNorm in front of the block): wave t sums token t's squares in a
+    // fixed order, so every workgroup derives the same binary16 activations.
+    __shared__ float s_rn[kDecMaxT];
+    if (wave < T) {
+      float ss = 0.f;
+      for (int j = lane; j < H; j += 64) {
+        const float v = (float)act[(size_t)wave * H + j];
+        ss = fmaf(v, v, ss);
+      }
+      ss = lane_group_sum(ss, 64);
+      if (lane == 0) s_rn[wave] = 1.0f / sqrtf(ss / (float)H + a.eps);
+    }
+    __syncthreads();
+    for (int q = tid; q < T * H; q += blockDim.x) {
+      const int t = q / H, j = q - t * H;
+      act[q] = (_Float16)((float)act[q] * s_rn[t] * half_bits_to_float(a.gain[j]));
+    }
+    __syncthreads();
+  }
 
   // Roles by local slot (see role_slots); the down rows on every workgroup.
   const int nj = nb / kXcds, half = nj / 2;
@@ -528,6 +549,10 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
       }
       Frag<4, 2, CPL4I> f;
       f.load(rows, srow, g, a.w2_q);
+      // the sub-block's residual for this item's outputs, loaded with the
+      // weights (unconditionally, from a valid element: a load whose value is
+      // selected at once would be waited for here)
+      const uint16_t resid_bits = a.x[(size_t)t * H + n0 + (tid < g.rpb ? tid : 0)];
       __builtin_amdgcn_sched_barrier(0);  // issue these loads before waiting
       if (!h_ready) {
         wait_done(a.sync, SYNC_UP, p.n_up);
@@ -554,6 +579,7 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
         const int nn = n0 + tid;
         if (MODE == DEC_FORWARD)
           v += s_sig[t] * a.s_sh[((size_t)(nn / p.ss_rows) * T + t) * p.ss_stride + nn % p.ss_rows];
+        if (a.gain) v += half_bits_to_float(resid_bits);
         const _Float16 hv = (_Float16)v;
         a.out[(size_t)t * H + nn] = __builtin_bit_cast(uint16_t, hv);
       }

@@ -64,6 +64,8 @@ struct DecodeArgs {
   const int8_t* sh2_q; const uint16_t* sh2_s;
   const uint16_t* x;
   uint16_t* out;
+  const uint16_t* gain;  // sub-block: RMSNorm gain [H] (x is the residual stream), or null
+  float eps;             // sub-block: RMSNorm epsilon
   int32_t* ids_out; float* w_out; float* sigma_out;  // nullable
   const int32_t* ids_in; const float* w_in;          // routing given by the caller
   uint32_t* sync;
