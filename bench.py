@@ -110,6 +110,40 @@ def make_copies(case, R, torch, m):
     return copies
 
 
+def time_block(cfg, steps, warmup, R, torch, m, gen):
+    """Per-call time of the MoE sub-block (RMSNorm -> block -> residual add)
+    on the same workload, weights rotated the same way."""
+    import ctypes
+    import numpy as np
+    case = gen.make_config(cfg)
+    d, T = case.dims, case.T
+    dims = m.make_dims(d.H, d.E, d.k, d.I, d.Is, d.G)
+    copies = make_copies(case, R, torch, m)
+    x = torch.from_numpy(case.x.view(np.int16)).cuda()
+    gain = torch.from_numpy(np.ones(d.H, dtype=np.float16).view(np.int16)).cuda()
+    out = torch.empty((T, d.H), dtype=torch.int16, device="cuda")
+    ws = m.workspace(dims, T)
+    stream = torch.cuda.current_stream()
+    fn = m.lib().moe_block_forward
+    args = [(ctypes.byref(dims), ctypes.byref(c.struct), x.data_ptr(), gain.data_ptr(), 1e-6, T, out.data_ptr(),
+             None, None, None, ws.data_ptr(), ws.numel(), stream.cuda_stream) for c in copies]
+    for s in range(warmup):
+        st = fn(*args[s % R])
+        if st != 0:
+            raise RuntimeError(f"moe_block_forward: {m.moe_status_string(st)}")
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for s in range(steps):
+        fn(*args[s % R])
+    e1.record(stream)
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / steps
+    del copies
+    torch.cuda.empty_cache()
+    return us
+
+
 def time_config(cfg, steps, warmup, R, torch, m, gen, per_launch_events):
     import ctypes
     import numpy as np
@@ -257,6 +291,8 @@ def main():
     ap.add_argument("--copies", type=int, default=32, help="weight copies rotated for cold-cache timing")
     ap.add_argument("--chunk-steps", type=int, default=300, help="steps of the 512-token workload")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--no-sub-block", action="store_true",
+                    help="skip the RMSNorm + residual sub-block timing (its launches share the block's kernel names)")
     ap.add_argument("--profile-run", choices=["decode", "chunk"], default=None,
                     help="untimed steps plus a calibration copy, for rocprofv3 counter passes (no JSON metric line)")
     args = ap.parse_args()
@@ -281,6 +317,13 @@ def main():
     r4 = time_config(4, args.chunk_steps, max(10, args.warmup // 10), max(4, args.copies // 8), torch, m, gen,
                      per_launch_events=False)
     log(f"  {r4['us_per_step']:.3f} us/step")
+
+    sb1 = sb4 = None
+    if not args.no_sub_block:
+        log("sub-block (RMSNorm -> block -> residual) T=1 and T=512 ...")
+        sb1 = time_block(1, args.steps, args.warmup, args.copies, torch, m, gen)
+        sb4 = time_block(4, args.chunk_steps, max(10, args.warmup // 10), max(4, args.copies // 8), torch, m, gen)
+        log(f"  {sb1:.3f} / {sb4:.3f} us/step")
 
     d1 = r1["dims"]
     b1 = algorithmic_bytes(d1, 1, r1["distinct_experts"])
@@ -330,6 +373,12 @@ def main():
                                               4)},
         "source_digest": digest,
     }
+    if sb1 is not None:
+        line["sub_block"] = {"workload": "post-attention RMSNorm -> the same block -> residual add, same inputs",
+                             "t1_us_per_step": round(sb1, 3), "t512_us_per_step": round(sb4, 3),
+                             "t1_tokens_per_s": round(1e6 / sb1, 1), "t512_tokens_per_s": round(512e6 / sb4, 1),
+                             "t1_extra_us_vs_block": round(sb1 - r1["us_per_step"], 3),
+                             "t512_extra_us_vs_block": round(sb4 - r4["us_per_step"], 3)}
     if not args.no_cpu:
         log("cpu baseline ...")
         line["cpu_baseline"] = cpu_baseline(gen)

@@ -64,8 +64,9 @@ def lib() -> ctypes.CDLL:
         L.moe_experts_w4a16.restype = ctypes.c_int
         L.moe_forward.argtypes = [dims_p, w_p, vp, i32, vp, vp, vp, vp, vp, sz, vp]
         L.moe_forward.restype = ctypes.c_int
-        L.moe_block_forward.argtypes = [dims_p, w_p, vp, vp, ctypes.c_float, i32, vp, vp, vp, vp, vp, sz, vp]
-        L.moe_block_forward.restype = ctypes.c_int
+        if hasattr(L, "moe_block_forward"):  # a library without it raises when it is called
+            L.moe_block_forward.argtypes = [dims_p, w_p, vp, vp, ctypes.c_float, i32, vp, vp, vp, vp, vp, sz, vp]
+            L.moe_block_forward.restype = ctypes.c_int
         _lib = L
     return _lib
 

@@ -140,7 +140,7 @@ struct DeviceInfo {
   bool checked = false;
   bool ok = false;
   int cus = 0;
-  int occ[2][2][17] = {};  // blocks per CU by mode, width specialisation and LDS (4 KiB steps)
+  int occ[kDecModes][2][17] = {};  // blocks per CU by mode, width specialisation and LDS (4 KiB steps)
 };
 
 std::mutex g_dev_mu;
@@ -157,7 +157,7 @@ int device_info(DeviceInfo** out) {
     if (hipGetDeviceProperties(&prop, dev) == hipSuccess && strncmp(prop.gcnArchName, "gfx950", 6) == 0) {
       di.ok = true;
       di.cus = prop.multiProcessorCount;
-      for (int m = 0; m < 2; ++m)
+      for (int m = 0; m < kDecModes; ++m)
         for (int r = 0; r < 2; ++r)
           for (int s = 0; s <= 16; ++s) di.occ[m][r][s] = decode_blocks_per_cu(m, r == 1, (size_t)s * 4096);
     }
@@ -349,7 +349,7 @@ MOE_API int moe_block_forward(const moe_dims* dims, const moe_weights* w, const 
     if (hb < ob + n && ob < hb + n) return MOE_ERR_SHAPE;  // out overlaps the residual stream
   }
   if (use_decode(dims, T))
-    return run_decode(dims, w, h, T, out, DEC_FORWARD, ids, weights, shared_gate, nullptr, nullptr, ws, stream, gain,
+    return run_decode(dims, w, h, T, out, DEC_BLOCK, ids, weights, shared_gate, nullptr, nullptr, ws, stream, gain,
                       eps);
   DeviceInfo* di = nullptr;
   if ((st = device_info(&di)) != MOE_OK) return st;

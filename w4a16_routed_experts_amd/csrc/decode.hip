@@ -419,13 +419,17 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int nb = gridDim.x, b = blockIdx.x;
 
+  // DEC_BLOCK (the Chimera notebook, sections 7 and 10: post-attention
+  // RMSNorm in front of the block, residual after it): the gain comes into
+  // LDS with x, wave t sums token t's squares in a fixed order (so every
+  // workgroup derives the same binary16 activations), and act is normalised in
+  // place.
+  __shared__ _Float16 s_gain[MODE == DEC_BLOCK ? kMaxHidden : 1];
+  __shared__ float s_rn[kDecMaxT];
   copy_halves(act, a.x, T * H);
+  if (MODE == DEC_BLOCK) copy_halves(s_gain, a.gain, H);
   __syncthreads();
-  if (a.gain) {
-    // The sub-block (the Chimera notebook, sections 7 and 10: post-attention
-    // RMSNorm in front of the block): wave t sums token t's squares in a
-    // fixed order, so every workgroup derives the same binary16 activations.
-    __shared__ float s_rn[kDecMaxT];
+  if (MODE == DEC_BLOCK) {
     if (wave < T) {
       float ss = 0.f;
       for (int j = lane; j < H; j += 64) {
@@ -436,17 +440,16 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
       if (lane == 0) s_rn[wave] = 1.0f / sqrtf(ss / (float)H + a.eps);
     }
     __syncthreads();
-    for (int q = tid; q < T * H; q += blockDim.x) {
-      const int t = q / H, j = q - t * H;
-      act[q] = (_Float16)((float)act[q] * s_rn[t] * half_bits_to_float(a.gain[j]));
-    }
+    for (int t = 0; t < T; ++t)
+      for (int j = tid; j < H; j += blockDim.x)
+        act[(size_t)t * H + j] = (_Float16)((float)act[(size_t)t * H + j] * s_rn[t] * (float)s_gain[j]);
     __syncthreads();
   }
 
   // Roles by local slot (see role_slots); the down rows on every workgroup.
   const int nj = nb / kXcds, half = nj / 2;
   const int jr = (p.n_router + kXcds - 1) / kXcds, js = (p.n_shup + kXcds - 1) / kXcds;
-  const int jd = MODE == DEC_FORWARD ? (p.n_sd + kXcds - 1) / kXcds : 0;
+  const int jd = MODE != DEC_EXPERTS ? (p.n_sd + kXcds - 1) / kXcds : 0;
   const bool split = nb % kXcds == 0 && nj % 2 == 0 && jr + js + jd < half;  // uniform
   const Role r_router = split ? role_slots(b, 0, jr) : role_all(b, nb, 0);
   const Role r_shup = split ? role_slots(b, jr, jr + js) : role_all(b, nb, p.n_router);
@@ -454,7 +457,7 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
   const Role r_up = split ? role_two(b, jr + js + jd, half, nj) : role_all(b, nb, 0);
 
   // ---------------- stage A
-  if (MODE == DEC_FORWARD) {
+  if (MODE != DEC_EXPERTS) {
     if (r_router.idx >= 0)
       for (int item = r_router.idx; item < p.n_router; item += r_router.count) {
         router_item<CPL8H>(a, H, item, act);
@@ -468,7 +471,7 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
   }
 
   // ---------------- routing into LDS
-  if (MODE == DEC_FORWARD) {
+  if (MODE != DEC_EXPERTS) {
     wait_done(a.sync, SYNC_ROUTER, p.n_router);
     // wave t ranks token t, reading its logits straight from the router
     // items' regions (lane l: experts 4l..4l+3, one 16-byte load)
@@ -512,7 +515,7 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
       up_item<CPL4H>(a, H, I, item, act, s_ids);
       signal_item(a.sync, SYNC_UP, item, p.n_up);
     }
-  if (MODE == DEC_FORWARD && r_sd.idx >= 0 && r_sd.idx < p.n_sd) {
+  if (MODE != DEC_EXPERTS && r_sd.idx >= 0 && r_sd.idx < p.n_sd) {
     wait_done(a.sync, SYNC_SHUP, p.n_shup);
     gather_batched(hs_lds, a.h_s, T * Is, [&](int q) {
       const int t = q / Is, j = q % Is;
@@ -549,14 +552,14 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
       }
       Frag<4, 2, CPL4I> f;
       f.load(rows, srow, g, a.w2_q);
-      // the sub-block's residual for this item's outputs, loaded with the
-      // weights (unconditionally, from a valid element: a load whose value is
+      // DEC_BLOCK: the residual of this item's outputs, loaded with the
+      // weights (from a valid element for every thread: a load whose value is
       // selected at once would be waited for here)
-      const uint16_t resid_bits = a.x[(size_t)t * H + n0 + (tid < g.rpb ? tid : 0)];
+      const uint16_t resid_bits = MODE == DEC_BLOCK ? a.x[(size_t)t * H + n0 + (tid < g.rpb ? tid : 0)] : 0;
       __builtin_amdgcn_sched_barrier(0);  // issue these loads before waiting
       if (!h_ready) {
         wait_done(a.sync, SYNC_UP, p.n_up);
-        if (MODE == DEC_FORWARD) wait_done(a.sync, SYNC_SD, p.n_sd);
+        if (MODE != DEC_EXPERTS) wait_done(a.sync, SYNC_SD, p.n_sd);
         gather_h(act, a.h_e, p, I);
         __syncthreads();
         h_ready = true;
@@ -577,9 +580,9 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
       if (tid < g.rpb) {
         float v = s_red[0][tid] + s_red[1][tid] + s_red[2][tid] + s_red[3][tid];
         const int nn = n0 + tid;
-        if (MODE == DEC_FORWARD)
+        if (MODE != DEC_EXPERTS)
           v += s_sig[t] * a.s_sh[((size_t)(nn / p.ss_rows) * T + t) * p.ss_stride + nn % p.ss_rows];
-        if (a.gain) v += half_bits_to_float(resid_bits);
+        if (MODE == DEC_BLOCK) v += half_bits_to_float(resid_bits);
         const _Float16 hv = (_Float16)v;
         a.out[(size_t)t * H + nn] = __builtin_bit_cast(uint16_t, hv);
       }
@@ -628,6 +631,7 @@ static int occupancy(bool real, size_t lds) {
 }
 
 int decode_blocks_per_cu(int mode, bool real, size_t lds_bytes) {
+  if (mode == DEC_BLOCK) return occupancy<DEC_BLOCK>(real, lds_bytes);
   return mode == DEC_FORWARD ? occupancy<DEC_FORWARD>(real, lds_bytes) : occupancy<DEC_EXPERTS>(real, lds_bytes);
 }
 
@@ -636,6 +640,9 @@ int launch_decode(const DecodeArgs& a, int mode, int grid, size_t lds_bytes, hip
   if (mode == DEC_FORWARD) {
     if (real) hipLaunchKernelGGL((decode_kernel<DEC_FORWARD, 2048, 512, 512>), dim3(grid), dim3(256), lds_bytes, s, a);
     else hipLaunchKernelGGL((decode_kernel<DEC_FORWARD, 0, 0, 0>), dim3(grid), dim3(256), lds_bytes, s, a);
+  } else if (mode == DEC_BLOCK) {
+    if (real) hipLaunchKernelGGL((decode_kernel<DEC_BLOCK, 2048, 512, 512>), dim3(grid), dim3(256), lds_bytes, s, a);
+    else hipLaunchKernelGGL((decode_kernel<DEC_BLOCK, 0, 0, 0>), dim3(grid), dim3(256), lds_bytes, s, a);
   } else {
     if (real) hipLaunchKernelGGL((decode_kernel<DEC_EXPERTS, 2048, 512, 512>), dim3(grid), dim3(256), lds_bytes, s, a);
     else hipLaunchKernelGGL((decode_kernel<DEC_EXPERTS, 0, 0, 0>), dim3(grid), dim3(256), lds_bytes, s, a);

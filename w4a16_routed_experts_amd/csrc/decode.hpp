@@ -12,7 +12,9 @@ static constexpr int kCounterPages = 2;   // 64 counter slots
 static constexpr int kSubCounters = 8;    // items of a stage count on 8 sub-counters, then one top counter
 static constexpr int kSyncBytes = (kCounterPages + kXcds) * kFlagPage * 4;  // counters, then one flag page per XCD
 enum { SYNC_ROUTER = 0, SYNC_SHUP = 1, SYNC_UP = 2, SYNC_SD = 3, SYNC_EXIT = 4, SYNC_ERR = 5, SYNC_COUNT = 6 };
-enum { DEC_FORWARD = 0, DEC_EXPERTS = 1 };
+enum { DEC_FORWARD = 0, DEC_EXPERTS = 1, DEC_BLOCK = 2 };  // DEC_BLOCK: the forward with RMSNorm and residual
+static constexpr int kDecModes = 3;
+static constexpr int kMaxHidden = 4096;  // widest admitted hidden size
 
 __host__ __device__ constexpr int round32(int x) { return (x + 31) / 32 * 32; }
 
@@ -64,8 +66,8 @@ struct DecodeArgs {
   const int8_t* sh2_q; const uint16_t* sh2_s;
   const uint16_t* x;
   uint16_t* out;
-  const uint16_t* gain;  // sub-block: RMSNorm gain [H] (x is the residual stream), or null
-  float eps;             // sub-block: RMSNorm epsilon
+  const uint16_t* gain;  // DEC_BLOCK: RMSNorm gain [H] (x is the residual stream)
+  float eps;             // DEC_BLOCK: RMSNorm epsilon
   int32_t* ids_out; float* w_out; float* sigma_out;  // nullable
   const int32_t* ids_in; const float* w_in;          // routing given by the caller
   uint32_t* sync;
