@@ -90,3 +90,18 @@ def test_block_token_counts(T, flags):
     h_bits, gain_bits = _inputs(case, 7200 + T)
     gpu = _run_block(case, h_bits, gain_bits, flags)
     _check(case, h_bits, gain_bits, gpu, f"block-T{T}-f{flags}")
+
+
+# other admitted widths: 512 (toy-sized rows), 4096 (the router takes two load
+# batches per row, so the norm needs its own first pass over x)
+@pytest.mark.parametrize("shape", [(512, 32, 4, 128, 256), (4096, 64, 8, 1024, 128)],
+                         ids=lambda s: "H{}E{}k{}I{}Is{}".format(*s))
+@pytest.mark.parametrize("T,flags", [(1, m.PATH_AUTO), (2, m.PATH_CHUNK), (10, m.PATH_AUTO)])
+def test_block_other_widths(shape, T, flags):
+    H, E, k, I, Is = shape
+    d = gen.Dims(H=H, E=E, k=k, I=I, Is=Is)
+    case = gen.make_case(d, T, seed=7300 + H + T)
+    _gpu.log(f"sub-block shape {shape} T={T} flags={flags}")
+    h_bits, gain_bits = _inputs(case, 7400 + H + T)
+    gpu = _run_block(case, h_bits, gain_bits, flags)
+    _check(case, h_bits, gain_bits, gpu, f"block-{shape}-T{T}-f{flags}")

@@ -119,19 +119,11 @@ __global__ __launch_bounds__(64 * kRouterWaves) void router_gemm_kernel(ChunkArg
   __shared__ float s_rn[32];
   const bool sub = a.gain != nullptr;  // uniform
   const __amdgpu_buffer_rsrc_t rg = make_rsrc(a.gain, sub ? (uint32_t)H * 2u : 0u);
-  if (sub) {
-    float ss[4] = {0.f, 0.f, 0.f, 0.f};
-    for (int gi = wave; gi < ngr; gi += kRouterWaves) {
-      u32x4 v[4];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) v[j] = __builtin_amdgcn_raw_buffer_load_b128(rx, xoff[j] + 128u * gi, 0, 0);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const h8 hv = __builtin_bit_cast(h8, v[j]);
-#pragma unroll
-        for (int i = 0; i < 8; ++i) ss[j] = fmaf((float)hv[i], (float)hv[i], ss[j]);
-      }
-    }
+  constexpr int BATCH = 4;
+  const bool one_batch = ngr <= kRouterWaves * BATCH;  // H <= 2048: the batch holds the wave's whole share
+  // reciprocal RMS of the 32 tokens from each lane's partial sums of squares
+  // of rows 8j + lane / 8 (four rows per lane)
+  auto finish_rn = [&](float ss[4]) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) {  // the 8 lanes of one row (lanes 8m .. 8m + 7)
       ss[j] += __shfl_xor(ss[j], 1, 64);
@@ -148,12 +140,35 @@ __global__ __launch_bounds__(64 * kRouterWaves) void router_gemm_kernel(ChunkArg
       s_rn[row] = 1.0f / sqrtf(t / (float)H + a.eps);
     }
     __syncthreads();
+  };
+  auto add_squares = [&](float ss[4], const u32x4 v[4]) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const h8 hv = __builtin_bit_cast(h8, v[j]);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) ss[j] = fmaf((float)hv[i], (float)hv[i], ss[j]);
+    }
+  };
+  if (sub && !one_batch) {  // wider rows: a first pass over x for the sums of squares
+    float ss[4] = {0.f, 0.f, 0.f, 0.f};
+    for (int g0 = wave; g0 < ngr; g0 += kRouterWaves * BATCH) {
+      u32x4 v[BATCH][4];
+#pragma unroll
+      for (int u = 0; u < BATCH; ++u) {
+        const int gi = g0 + kRouterWaves * u;
+        const uint32_t kx = gi < ngr ? 128u * gi : kOob;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) v[u][j] = __builtin_amdgcn_raw_buffer_load_b128(rx, xoff[j] + kx, 0, 0);
+      }
+#pragma unroll
+      for (int u = 0; u < BATCH; ++u) add_squares(ss, v[u]);
+    }
+    finish_rn(ss);
   }
   const __amdgpu_buffer_rsrc_t rxn = make_rsrc(a.xn, sub && blockIdx.y == 0 ? (uint32_t)a.T * H * 2u : 0u);
   uint4* xs = stage[wave];
   uint4* wsl = stage[wave] + 32 * kRxStride;
   f16v acc = {};
-  constexpr int BATCH = 4;
   for (int g0 = wave; g0 < ngr; g0 += kRouterWaves * BATCH) {
     u32x4 xa[BATCH][4], wb[BATCH][2], gn[BATCH];
     uint16_t sc[BATCH];
@@ -170,6 +185,12 @@ __global__ __launch_bounds__(64 * kRouterWaves) void router_gemm_kernel(ChunkArg
       gn[u] = __builtin_amdgcn_raw_buffer_load_b128(rg, ok ? 128u * gi + 16u * (lane & 7) : kOob, 0, 0);
     }
     __builtin_amdgcn_sched_barrier(0);  // the whole batch in flight before any use
+    if (sub && one_batch) {  // the batch holds the wave's share of every row
+      float ss[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int u = 0; u < BATCH; ++u) add_squares(ss, xa[u]);
+      finish_rn(ss);
+    }
 #pragma unroll
     for (int u = 0; u < BATCH; ++u) {
       if (sub) {  // binary16(x * rsqrt(mean x^2 + eps) * gain), kept for the expert GEMMs

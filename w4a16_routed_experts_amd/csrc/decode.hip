@@ -424,25 +424,33 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
   // LDS with x, wave t sums token t's squares in a fixed order (so every
   // workgroup derives the same binary16 activations), and act is normalised in
   // place.
-  __shared__ _Float16 s_gain[MODE == DEC_BLOCK ? kMaxHidden : 1];
+  __shared__ __attribute__((aligned(16))) _Float16 s_gain[MODE == DEC_BLOCK ? kMaxHidden : 8];
   __shared__ float s_rn[kDecMaxT];
   copy_halves(act, a.x, T * H);
   if (MODE == DEC_BLOCK) copy_halves(s_gain, a.gain, H);
   __syncthreads();
   if (MODE == DEC_BLOCK) {
-    if (wave < T) {
+    if (wave < T) {  // 8 halves (16 bytes) per lane and step
+      const h8* row = reinterpret_cast<const h8*>(act + (size_t)wave * H);
       float ss = 0.f;
-      for (int j = lane; j < H; j += 64) {
-        const float v = (float)act[(size_t)wave * H + j];
-        ss = fmaf(v, v, ss);
+      for (int c = lane; c < H / 8; c += 64) {
+        const h8 v = row[c];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) ss = fmaf((float)v[i], (float)v[i], ss);
       }
       ss = lane_group_sum(ss, 64);
       if (lane == 0) s_rn[wave] = 1.0f / sqrtf(ss / (float)H + a.eps);
     }
     __syncthreads();
-    for (int t = 0; t < T; ++t)
-      for (int j = tid; j < H; j += blockDim.x)
-        act[(size_t)t * H + j] = (_Float16)((float)act[(size_t)t * H + j] * s_rn[t] * (float)s_gain[j]);
+    for (int q = tid; q < T * (H / 8); q += blockDim.x) {
+      const int t = q / (H / 8), c = q - t * (H / 8);
+      h8* p = reinterpret_cast<h8*>(act + (size_t)t * H) + c;
+      const h8 gv = reinterpret_cast<const h8*>(s_gain)[c];
+      h8 v = *p;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) v[i] = (_Float16)((float)v[i] * s_rn[t] * (float)gv[i]);
+      *p = v;
+    }
     __syncthreads();
   }
 
