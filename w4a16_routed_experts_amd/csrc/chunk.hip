@@ -6,12 +6,17 @@
 //   1. router GEMM          logits[T][E+1]   (int8 rows, MFMA, per-group scales)
 //   2. top-k per token      ids, renormalised weights, sigma
 //   3. bucketing            (token, slot) pairs sorted by expert, then pair
-//                           index; 64- or 32-row tiles per expert; shared tiles
+//                           index; tiles of up to 128 rows per expert, shared
+//                           tiles (2 and 3 run in one launch for the complete
+//                           block: the last top-k workgroup sorts)
 //   4. gate/up GEMM         h[row][I] = silu(x W_gate^T) * (x W_up^T)   (fp16)
 //   5. down GEMM            y[t*k+i][H] = w * (h W_down^T)                (fp16)
 //   6. combine              out[t] = sum_i y[t*k+i] + sigma_t * s[t]
 // Each tile streams its expert's weights once; a tile's rows are the tokens
-// routed to that expert.
+// routed to that expert.  For the sub-block of a decoder layer (the same
+// notebook, sections 7 and 10) the router GEMM also applies the post-attention
+// RMSNorm and writes the normalised rows the expert GEMMs read, and the combine
+// adds the residual.
 #include "chunk.hpp"
 
 namespace moe {
