@@ -163,3 +163,26 @@ def test_workspace_reused_across_token_counts():
         assert _gpu.row_rel_l2(o, want).max() <= _gpu.ROW_TOL
     # the workspace's counters and done flags are back to zero
     assert int(ws[: 40 * 1024].view(torch.int32).abs().sum()) == 0
+
+
+def test_max_token_count_sampled():
+    """The largest admitted chunk (T = 65536 at real widths, iid routing, so
+    every expert takes thousands of rows): ids valid and distinct on every row,
+    every output finite, and sampled rows checked against the oracle computed
+    for those tokens alone (routing and experts act on each token independently)."""
+    T = 65536
+    case = gen.make_case(gen.REAL, T, seed=6553, real_experts=True)
+    _gpu.log(f"maximum chunk T={T}")
+    g = _gpu.run_forward(case)
+    d = case.dims
+    ids = g["ids"]
+    assert ids.min() >= 0 and ids.max() < d.E
+    srt = np.sort(ids, axis=1)
+    assert np.all(srt[:, 1:] != srt[:, :-1]), "an expert listed twice for one token"
+    assert np.all(np.isfinite(g["out"]))
+    rng = np.random.default_rng(65)
+    rows = np.sort(np.concatenate([[0, T - 1], rng.choice(T, 46, replace=False)]))
+    sub = Case(name="max-sample", dims=d, weights=case.weights, x=case.x[rows], meta={})
+    r = ref.forward(sub.x, sub.weights, d)
+    gs = dict(out=g["out"][rows], ids=ids[rows], w=g["w"][rows], sigma=g["sigma"][rows])
+    _gpu.check_forward(sub, r, gs, f"T{T}-sampled")

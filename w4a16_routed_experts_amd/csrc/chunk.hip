@@ -1224,8 +1224,11 @@ __device__ __forceinline__ void add8(float acc[8], uint4 v) {
 }
 
 __global__ __launch_bounds__(256) void combine_kernel(ChunkArgs a) {
-  const int t = blockIdx.y;
-  const int n = (blockIdx.x * blockDim.x + threadIdx.x) * 8;
+  // a one-dimensional grid of T x nbx blocks (a token's row is nbx blocks of
+  // 2048 outputs), so T is not bound by the limit of a grid's second dimension
+  const int nbx = (a.H / 8 + 255) / 256;
+  const int t = blockIdx.x / nbx;
+  const int n = ((blockIdx.x - t * nbx) * blockDim.x + threadIdx.x) * 8;
   if (n >= a.H) return;
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   // the token's k rows of y (row t * k + i) and its ids are loaded together;
@@ -1283,7 +1286,7 @@ static void launch_gemms(const ChunkArgs& a, hipStream_t s) {
   const int down_items = max_tiles * ((a.H + 255) / 256);
   hipLaunchKernelGGL(up_gemm_kernel, dim3((up_items + 7) & ~7), dim3(256), 0, s, a);
   hipLaunchKernelGGL(down_gemm_kernel, dim3((down_items + 7) & ~7), dim3(256), 0, s, a);
-  hipLaunchKernelGGL(combine_kernel, dim3((a.H / 8 + 255) / 256, a.T), dim3(256), 0, s, a);
+  hipLaunchKernelGGL(combine_kernel, dim3((a.H / 8 + 255) / 256 * a.T), dim3(256), 0, s, a);
 }
 
 }  // namespace moe
