@@ -186,3 +186,32 @@ def test_max_token_count_sampled():
     r = ref.forward(sub.x, sub.weights, d)
     gs = dict(out=g["out"][rows], ids=ids[rows], w=g["w"][rows], sigma=g["sigma"][rows])
     _gpu.check_forward(sub, r, gs, f"T{T}-sampled")
+
+
+@pytest.mark.parametrize("T", [1, 40])
+def test_hip_graph_replays_match_eager(T):
+    """One call captured in a HIP graph and replayed several times, with eager
+    calls on other inputs in between: every replay leaves exactly the eager
+    output (the library records no memset and leaves its counters at zero)."""
+    case = gen.make_case(gen.REAL, T, seed=6600 + T, real_experts=True)
+    other = gen.make_case(gen.REAL, T, seed=6700 + T, real_experts=True)
+    d = case.dims
+    dims = _gpu.dims_of(d)
+    W = _gpu.device_weights(_gpu.config_case(1))
+    x, x2 = _gpu.x_tensor(case), _gpu.x_tensor(other)
+    out = torch.zeros((T, d.H), dtype=torch.int16, device="cuda")
+    out2 = torch.zeros((T, d.H), dtype=torch.int16, device="cuda")
+    ws = m.workspace(dims, T)
+    m.moe_forward(dims, W.struct, x, T, out, ws=ws)
+    torch.cuda.synchronize()
+    want = out.clone()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        m.moe_forward(dims, W.struct, x, T, out, ws=ws)
+    for rep in range(4):
+        out.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, want), f"replay {rep} differs from eager"
+        m.moe_forward(dims, W.struct, x2, T, out2, ws=ws)  # eager work between replays
+        torch.cuda.synchronize()
