@@ -297,7 +297,7 @@ def main():
                     help="untimed steps plus a calibration copy, for rocprofv3 counter passes (no JSON metric line)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(json.dumps({"error": "this layer is measured on one GPU; multi-GPU runs are not part of this build",
+        print(json.dumps({"error": "this layer runs and is measured on one GPU: the library has no multi-GPU path",
                           "n_gpus": args.gpus}))
         sys.exit(2)
 
