@@ -28,7 +28,9 @@ h / sqrt(mean(h^2) + eps) * gain with the gain vector as applied, and its output
 is rounded to binary16 (the MoE input everywhere else) before the block.
 
 Every function below is pinned by the ``-m "not gpu"`` tests (hand-derived
-fixtures, brute force, closed forms and invariants).
+fixtures, brute force, closed forms and invariants), and the block and the
+RMSNorm also against transformers' Qwen3.5-MoE modules (the published
+implementation the Chimera notebook checks its reference against, section 5.2).
 """
 from __future__ import annotations
 
