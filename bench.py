@@ -3,12 +3,14 @@
 One step = one call of the whole layer (router, top-k, experts, shared
 expert, combine) on one batch of seeded synthetic input already resident in
 HBM.  The headline workload is single-token decode at real widths (T=1,
-H=2048, E=256, top-8, I=512, Is=512); the 512-token Zipf chunk is measured in
-the same run and reported beside it.
+H=2048, E=256, top-8, I=512, Is=512); the 512-token Zipf chunk and the other
+three workloads (toy layer, 32-token batched decode, 128-token prefill) are
+measured in the same run and reported beside it.
 
 Cold-cache discipline: the weights are replicated R times at distinct device
-addresses and step s uses copy s mod R, so a copy's touched bytes have been
-evicted from L2 and the 256 MB last-level cache before it is used again.
+addresses and step s (warm-up steps included) uses copy s mod R, so a copy's
+touched bytes have been evicted from L2 and the 256 MB last-level cache before
+it is used again.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
 Prints one JSON line.
@@ -134,8 +136,8 @@ def time_block(cfg, steps, warmup, R, torch, m, gen):
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record(stream)
-    for s in range(steps):
-        fn(*args[s % R])
+    for s in range(steps):  # the rotation continues past warm-up: no timed step reuses a warm copy
+        fn(*args[(warmup + s) % R])
     e1.record(stream)
     torch.cuda.synchronize()
     us = e0.elapsed_time(e1) * 1e3 / steps
@@ -172,8 +174,8 @@ def time_config(cfg, steps, warmup, R, torch, m, gen, per_launch_events):
     torch.cuda.synchronize()
     e0.record(stream)
     t0 = time.perf_counter()
-    for s in range(steps):
-        fwd(*args[s % R])
+    for s in range(steps):  # the rotation continues past warm-up: no timed step reuses a warm copy
+        fwd(*args[(warmup + s) % R])
     e1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
@@ -188,7 +190,7 @@ def time_config(cfg, steps, warmup, R, torch, m, gen, per_launch_events):
         torch.cuda.synchronize()
         for s in range(n):
             ev[s][0].record(stream)
-            fwd(*args[s % R])
+            fwd(*args[(warmup + steps + s) % R])
             ev[s][1].record(stream)
         torch.cuda.synchronize()
         durs = np.array([a.elapsed_time(b) for a, b in ev]) * 1e3
@@ -221,6 +223,30 @@ def time_config(cfg, steps, warmup, R, torch, m, gen, per_launch_events):
     del copies
     torch.cuda.empty_cache()
     return res
+
+
+def workload_summary(r, copies, description):
+    """tokens/s, HBM GB/s, MFMA % and roofline fraction of one timed workload."""
+    d, T = r["dims"], r["T"]
+    b = algorithmic_bytes(d, T, r["distinct_experts"])
+    f = algorithmic_flops(d, T)
+    t = r["us_per_step"] * 1e-6
+    return {"workload": description, "tokens_per_s": round(T / t, 1), "us_per_step": round(r["us_per_step"], 3),
+            "hbm_gbs": round(b / t / 1e9, 1), "hbm_frac": round(b / t / 1e9 / HBM_PEAK_GBS, 4),
+            "mfma_pct": round(100 * f / t / (MFMA_F16_PEAK_TFLOPS * 1e12), 3),
+            "roofline_frac": round(max(b / (HBM_PEAK_GBS * 1e9), f / (MFMA_F16_PEAK_TFLOPS * 1e12)) / t, 4),
+            "algorithmic_bytes": b, "flops": f, "distinct_experts": r["distinct_experts"],
+            "weight_copies_rotated": copies, "steps": r["steps"]}
+
+
+# configurations besides the headline: (steps, warm-up, weight copies, description)
+OTHER_WORKLOADS = {
+    0: (2000, 100, 1, "toy layer: T=1, hidden 256, 8 experts, top-2, intermediates 64 (0.1 MB of weights: "
+                      "one copy, cache-warm)"),
+    2: (300, 20, 3, "batched decode: T=32 iid tokens, real widths (about 280 MB touched per call, "
+                    "3 copies rotated)"),
+    3: (300, 20, 3, "prefill chunk: T=128, per-expert logit bias N(0, 0.5), real widths (3 copies rotated)"),
+}
 
 
 # --------------------------------------------------------------- CPU leg
@@ -291,6 +317,7 @@ def main():
     ap.add_argument("--copies", type=int, default=32, help="weight copies rotated for cold-cache timing")
     ap.add_argument("--chunk-steps", type=int, default=300, help="steps of the 512-token workload")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--no-other-workloads", action="store_true", help="time only T=1 and T=512")
     ap.add_argument("--no-sub-block", action="store_true",
                     help="skip the RMSNorm + residual sub-block timing (its launches share the block's kernel names)")
     ap.add_argument("--profile-run", choices=["decode", "chunk"], default=None,
@@ -318,6 +345,14 @@ def main():
                      per_launch_events=False)
     log(f"  {r4['us_per_step']:.3f} us/step")
 
+    others = {}
+    if not args.no_other_workloads:
+        for cfg, (steps, warm, R, desc) in OTHER_WORKLOADS.items():
+            log(f"config {cfg} ...")
+            r = time_config(cfg, steps, warm, R, torch, m, gen, per_launch_events=False)
+            others[f"config{cfg}"] = workload_summary(r, R, desc)
+            log(f"  {r['us_per_step']:.3f} us/step")
+
     sb1 = sb4 = None
     if not args.no_sub_block:
         log("sub-block (RMSNorm -> block -> residual) T=1 and T=512 ...")
@@ -335,10 +370,6 @@ def main():
     traffic = read_traffic(digest)
     value = r1["T"] * r1["steps"] / (r1["ms_total"] * 1e-3)
 
-    d4 = r4["dims"]
-    b4 = algorithmic_bytes(d4, r4["T"], r4["distinct_experts"])
-    f4 = algorithmic_flops(d4, r4["T"])
-    t4 = r4["us_per_step"] * 1e-6
     line = {
         "metric": METRIC,
         "value": round(value, 1),
@@ -364,15 +395,11 @@ def main():
                                                else r1.get("graph_error")),
                      "hip_graph_matches_eager": r1.get("graph_matches_eager"),
                      "mfma_pct": round(100 * f1 / (us_launch * 1e-6) / (MFMA_F16_PEAK_TFLOPS * 1e12), 4)},
-        "chunk_t512": {"workload": "512-token chunk, Zipf(1.1) expert popularity, same widths",
-                       "tokens_per_s": round(r4["T"] / t4, 1), "us_per_step": round(r4["us_per_step"], 3),
-                       "hbm_gbs": round(b4 / t4 / 1e9, 1), "hbm_frac": round(b4 / t4 / 1e9 / HBM_PEAK_GBS, 4),
-                       "mfma_pct": round(100 * f4 / t4 / (MFMA_F16_PEAK_TFLOPS * 1e12), 3),
-                       "algorithmic_bytes": b4, "flops": f4, "distinct_experts": r4["distinct_experts"],
-                       "roofline_frac": round(max(b4 / (HBM_PEAK_GBS * 1e9), f4 / (MFMA_F16_PEAK_TFLOPS * 1e12)) / t4,
-                                              4)},
+        "chunk_t512": workload_summary(r4, max(4, args.copies // 8),
+                                       "512-token chunk, Zipf(1.1) expert popularity, same widths"),
         "source_digest": digest,
     }
+    line.update(others)
     if sb1 is not None:
         line["sub_block"] = {"workload": "post-attention RMSNorm -> the same block -> residual add, same inputs",
                              "t1_us_per_step": round(sb1, 3), "t512_us_per_step": round(sb4, 3),
