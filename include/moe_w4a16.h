@@ -75,6 +75,7 @@ extern "C" {
 #define MOE_ERR_WORKSPACE (-4) /* ws_bytes < moe_workspace_bytes(dims, T) */
 #define MOE_ERR_LAUNCH (-5)    /* the HIP runtime refused a launch */
 #define MOE_ERR_DEVICE (-6)    /* the current device is not gfx950 or cannot be queried */
+#define MOE_ERR_SCRATCH (-7)   /* moe_forward_noalloc: the call needs more than MOE_NOALLOC_SCRATCH_BYTES */
 
 /* dims.flags: execution path (both compute the same result) */
 #define MOE_PATH_AUTO 0u   /* few tokens: persistent GEMV launch; otherwise grouped MFMA GEMMs */
@@ -150,6 +151,23 @@ MOE_API int moe_forward(const moe_dims* dims, const moe_weights* w, const uint16
 MOE_API int moe_block_forward(const moe_dims* dims, const moe_weights* w, const uint16_t* h, const uint16_t* gain,
                               float eps, int32_t T, uint16_t* out, int32_t* ids, float* weights,
                               float* shared_gate, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* moe_forward without a workspace argument and without any allocation, for
+ * callers that cannot allocate device memory: code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc.  Same arguments and
+ * result as moe_forward; the scratch memory is a static array of
+ * MOE_NOALLOC_SCRATCH_BYTES bytes inside the library, one per GPU the library
+ * runs on, held until the process ends (its address is looked up once per
+ * device, on the first call there).  A call whose moe_workspace_bytes(dims, T)
+ * exceeds that size is refused with MOE_ERR_SCRATCH before anything is
+ * enqueued (at real widths the limit admits 160 tokens and more).  Every call on
+ * one GPU shares that GPU's array: calls that may overlap on one GPU (other
+ * streams, other threads) race and must be ordered by the caller.  Each
+ * completed call leaves the array's counters zero, as the next call needs. */
+#define MOE_NOALLOC_SCRATCH_BYTES ((size_t)8 << 20)
+MOE_API int moe_forward_noalloc(const moe_dims* dims, const moe_weights* w, const uint16_t* x, int32_t T,
+                                uint16_t* out, int32_t* ids, float* weights, float* shared_gate,
+                                hipStream_t stream);
 
 /* Static description of a status code. */
 MOE_API const char* moe_status_string(int status);

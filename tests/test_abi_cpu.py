@@ -43,13 +43,13 @@ def test_every_declared_symbol_is_exported(L):
     text = open(HEADER).read()
     names = re.findall(r"MOE_API\s+[\w\s\*]+?\b(moe_\w+)\s*\(", text)
     assert set(names) == {"moe_workspace_bytes", "moe_route", "moe_experts_w4a16", "moe_forward", "moe_block_forward",
-                          "moe_status_string"}
+                          "moe_forward_noalloc", "moe_status_string"}
     for n in names:
         assert hasattr(L, n), n
 
 
 def test_status_strings(L):
-    for code in (0, -1, -2, -3, -4, -5, -6):
+    for code in (0, -1, -2, -3, -4, -5, -6, -7):
         assert m.moe_status_string(code)
     assert m.moe_status_string(99) == "unknown status"
 
@@ -143,3 +143,27 @@ def test_valid_call_without_gpu_reports_device_error(L):
     if torch.cuda.device_count() > 0:
         pytest.skip("a GPU is present: a valid call with fake pointers would reach it")
     assert _forward(L, _dims(), _weights()) == -6
+
+
+def _noalloc(L, dims, W, x=FAKE, T=1, out=FAKE, ids=None):
+    return L.moe_forward_noalloc(ctypes.byref(dims) if dims is not None else None,
+                                 ctypes.byref(W) if W is not None else None, x, T, out, ids, None, None, None)
+
+
+def test_refusals_forward_noalloc(L):
+    """The allocation-free variant refuses what moe_forward refuses, before any
+    device call, and refuses calls that need more than its static scratch."""
+    d, W = _dims(), _weights()
+    assert _noalloc(L, None, W) == -1
+    assert _noalloc(L, d, None) == -1
+    assert _noalloc(L, d, W, x=None) == -1
+    assert _noalloc(L, d, _weights(sh13_s=None)) == -1
+    assert _noalloc(L, _dims(k=9), W) == -2
+    assert _noalloc(L, _dims(flags=m.PATH_DECODE), W, T=5) == -2
+    assert _noalloc(L, d, W, x=FAKE + 2) == -3
+    assert _noalloc(L, d, W, ids=FAKE + 2) == -3
+    assert _noalloc(L, d, W, T=0) == 0
+    big = next(T for T in range(1, 4097) if m.moe_workspace_bytes(d, T) > m.NOALLOC_SCRATCH_BYTES)
+    assert big > 128
+    assert _noalloc(L, d, W, T=big) == -7
+    assert _noalloc(L, d, W, T=512) == -7

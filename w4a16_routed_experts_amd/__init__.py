@@ -19,6 +19,8 @@ from .binding import (  # noqa: F401
     moe_route,
     moe_experts_w4a16,
     moe_forward,
+    moe_forward_noalloc,
+    NOALLOC_SCRATCH_BYTES,
     moe_block_forward,
     DeviceWeights,
     make_dims,

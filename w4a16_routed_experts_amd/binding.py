@@ -15,7 +15,10 @@ from .build import LIB_PATH
 PATH_AUTO, PATH_DECODE, PATH_CHUNK = 0, 1, 2
 
 _STATUS = {0: "MOE_OK", -1: "MOE_ERR_NULL", -2: "MOE_ERR_SHAPE", -3: "MOE_ERR_ALIGN",
-           -4: "MOE_ERR_WORKSPACE", -5: "MOE_ERR_LAUNCH", -6: "MOE_ERR_DEVICE"}
+           -4: "MOE_ERR_WORKSPACE", -5: "MOE_ERR_LAUNCH", -6: "MOE_ERR_DEVICE", -7: "MOE_ERR_SCRATCH"}
+
+# size of the static scratch array behind moe_forward_noalloc (MOE_NOALLOC_SCRATCH_BYTES)
+NOALLOC_SCRATCH_BYTES = 8 << 20
 
 WEIGHT_FIELDS = ("router_q", "router_s", "w13_q", "w13_s", "w2_q", "w2_s",
                  "sh13_q", "sh13_s", "sh2_q", "sh2_s")
@@ -64,6 +67,9 @@ def lib() -> ctypes.CDLL:
         L.moe_experts_w4a16.restype = ctypes.c_int
         L.moe_forward.argtypes = [dims_p, w_p, vp, i32, vp, vp, vp, vp, vp, sz, vp]
         L.moe_forward.restype = ctypes.c_int
+        if hasattr(L, "moe_forward_noalloc"):
+            L.moe_forward_noalloc.argtypes = [dims_p, w_p, vp, i32, vp, vp, vp, vp, vp]
+            L.moe_forward_noalloc.restype = ctypes.c_int
         if hasattr(L, "moe_block_forward"):  # a library without it raises when it is called
             L.moe_block_forward.argtypes = [dims_p, w_p, vp, vp, ctypes.c_float, i32, vp, vp, vp, vp, vp, sz, vp]
             L.moe_block_forward.restype = ctypes.c_int
@@ -140,6 +146,13 @@ def moe_forward(dims, weights, x, T, out, ids=None, w=None, shared_gate=None, ws
     st = lib().moe_forward(ctypes.byref(dims), ctypes.byref(weights), _ptr(x), T, _ptr(out), _ptr(ids), _ptr(w),
                            _ptr(shared_gate), _ptr(ws), _nbytes(ws), _stream(stream))
     return _check(st, "moe_forward", raise_on_error)
+
+
+def moe_forward_noalloc(dims, weights, x, T, out, ids=None, w=None, shared_gate=None, stream=None,
+                        raise_on_error=True) -> int:
+    st = lib().moe_forward_noalloc(ctypes.byref(dims), ctypes.byref(weights), _ptr(x), T, _ptr(out), _ptr(ids),
+                                   _ptr(w), _ptr(shared_gate), _stream(stream))
+    return _check(st, "moe_forward_noalloc", raise_on_error)
 
 
 def moe_block_forward(dims, weights, h, gain, eps, T, out, ids=None, w=None, shared_gate=None, ws=None, stream=None,

@@ -11,6 +11,13 @@
 #include "decode.hpp"
 #include "moe_w4a16.h"
 
+// Scratch of moe_forward_noalloc.  In host code `scratch` names a host-side
+// stand-in, not device memory: its device address comes from
+// hipGetSymbolAddress, once per device with that device current, and only
+// that address is ever passed to kernels.  Static storage is zero-filled when
+// the code object is loaded, so the counters start at zero.
+static __device__ __attribute__((aligned(256))) unsigned char scratch[MOE_NOALLOC_SCRATCH_BYTES];
+
 namespace {
 
 using namespace moe;
@@ -140,6 +147,7 @@ struct DeviceInfo {
   bool checked = false;
   bool ok = false;
   int cus = 0;
+  void* scratch = nullptr;  // this device's address of the static scratch array
   int occ[kDecModes][2][17] = {};  // blocks per CU by mode, width specialisation and LDS (4 KiB steps)
 };
 
@@ -164,6 +172,25 @@ int device_info(DeviceInfo** out) {
   }
   if (!di.ok) return MOE_ERR_DEVICE;
   *out = &di;
+  return MOE_OK;
+}
+
+// --------------------------------------------------------------- static scratch
+
+int scratch_of_current_device(void** out) {
+  DeviceInfo* di = nullptr;
+  int st = device_info(&di);
+  if (st != MOE_OK) return st;
+  std::lock_guard<std::mutex> lk(g_dev_mu);
+  if (!di->scratch) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) {
+      (void)hipGetLastError();  // leave no sticky error for the caller's next HIP call
+      return MOE_ERR_DEVICE;
+    }
+    di->scratch = p;
+  }
+  *out = di->scratch;
   return MOE_OK;
 }
 
@@ -242,6 +269,12 @@ bool any_null(std::initializer_list<const void*> ps) {
   return false;
 }
 
+int validate_forward(const moe_dims* dims, const moe_weights* w, const uint16_t* x, int32_t T, const uint16_t* out,
+                     const int32_t* ids, const float* weights, const float* shared_gate, const void* ws,
+                     size_t ws_bytes);
+int launch_forward(const moe_dims* dims, const moe_weights* w, const uint16_t* x, int32_t T, uint16_t* out,
+                   int32_t* ids, float* weights, float* shared_gate, void* ws, hipStream_t stream);
+
 }  // namespace
 
 extern "C" {
@@ -260,6 +293,7 @@ MOE_API const char* moe_status_string(int status) {
     case MOE_ERR_WORKSPACE: return "workspace smaller than moe_workspace_bytes()";
     case MOE_ERR_LAUNCH: return "the HIP runtime refused a kernel launch";
     case MOE_ERR_DEVICE: return "the current device is not gfx950 or cannot be queried";
+    case MOE_ERR_SCRATCH: return "the call needs more scratch than moe_forward_noalloc's static array holds";
     default: return "unknown status";
   }
 }
@@ -306,7 +340,35 @@ MOE_API int moe_experts_w4a16(const moe_dims* dims, const moe_weights* w, const 
 MOE_API int moe_forward(const moe_dims* dims, const moe_weights* w, const uint16_t* x, int32_t T, uint16_t* out,
                         int32_t* ids, float* weights, float* shared_gate, void* ws, size_t ws_bytes,
                         hipStream_t stream) {
-  int st = check_common(dims, x, T, ws, ws_bytes);
+  int st = validate_forward(dims, w, x, T, out, ids, weights, shared_gate, ws, ws_bytes);
+  if (st != MOE_OK || T == 0) return st;
+  return launch_forward(dims, w, x, T, out, ids, weights, shared_gate, ws, stream);
+}
+
+MOE_API int moe_forward_noalloc(const moe_dims* dims, const moe_weights* w, const uint16_t* x, int32_t T,
+                                uint16_t* out, int32_t* ids, float* weights, float* shared_gate,
+                                hipStream_t stream) {
+  int st = check_dims(dims, T);
+  if (st != MOE_OK || T == 0) return st;
+  if (workspace_bytes(dims, T) > MOE_NOALLOC_SCRATCH_BYTES) return MOE_ERR_SCRATCH;
+  // every other check of moe_forward, against an aligned stand-in address for
+  // the scratch (validation never dereferences the workspace)
+  st = validate_forward(dims, w, x, T, out, ids, weights, shared_gate, reinterpret_cast<void*>(uintptr_t{256}),
+                        MOE_NOALLOC_SCRATCH_BYTES);
+  if (st != MOE_OK) return st;
+  void* ws = nullptr;
+  if ((st = scratch_of_current_device(&ws)) != MOE_OK) return st;
+  return launch_forward(dims, w, x, T, out, ids, weights, shared_gate, ws, stream);
+}
+
+}  // extern "C"
+
+namespace {
+
+int validate_forward(const moe_dims* dims, const moe_weights* w, const uint16_t* x, int32_t T, const uint16_t* out,
+                     const int32_t* ids, const float* weights, const float* shared_gate, const void* ws,
+                     size_t ws_bytes) {
+  int st = check_common(dims, x, T, const_cast<void*>(ws), ws_bytes);
   if (st != MOE_OK || T == 0) return st;
   if (!w) return MOE_ERR_NULL;
   if (any_null({w->router_q, w->router_s, w->w13_q, w->w13_s, w->w2_q, w->w2_s, w->sh13_q, w->sh13_s, w->sh2_q,
@@ -316,10 +378,17 @@ MOE_API int moe_forward(const moe_dims* dims, const moe_weights* w, const uint16
               w->sh2_s, out}) ||
       !all4({ids, weights, shared_gate}))
     return MOE_ERR_ALIGN;
+  return MOE_OK;
+}
+
+// the complete block on validated arguments
+int launch_forward(const moe_dims* dims, const moe_weights* w, const uint16_t* x, int32_t T, uint16_t* out,
+                   int32_t* ids, float* weights, float* shared_gate, void* ws, hipStream_t stream) {
   if (use_decode(dims, T))
     return run_decode(dims, w, x, T, out, DEC_FORWARD, ids, weights, shared_gate, nullptr, nullptr, ws, stream);
   DeviceInfo* di = nullptr;
-  if ((st = device_info(&di)) != MOE_OK) return st;
+  int st = device_info(&di);
+  if (st != MOE_OK) return st;
   ChunkArgs a = chunk_args(dims, w, x, T, out, ws);
   if (ids) a.ids = ids;
   if (weights) a.wts = weights;
@@ -328,6 +397,10 @@ MOE_API int moe_forward(const moe_dims* dims, const moe_weights* w, const uint16
   a.cus = di->cus;
   return launch_forward_chunk(a, stream);
 }
+
+}  // namespace
+
+extern "C" {
 
 MOE_API int moe_block_forward(const moe_dims* dims, const moe_weights* w, const uint16_t* h, const uint16_t* gain,
                               float eps, int32_t T, uint16_t* out, int32_t* ids, float* weights,
