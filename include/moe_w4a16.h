@@ -43,10 +43,21 @@
  *   - Shape admission: G = 64; 1 <= k <= E <= 256 and k <= 8; each of H, I and
  *     Is is 64 * 2^m or a multiple of 2048, and at most 4096; 0 <= T <= 65536.
  *   - The workspace (`ws`, `ws_bytes` >= moe_workspace_bytes(dims, T)) is
- *     scratch owned by the caller.  Its first 40 KiB hold counters and flags
- *     that must be zero before the first call that uses the workspace
- *     (allocate it zero-filled); every completed call leaves them zero.  Calls
- *     that share a workspace must be ordered (same stream, or synchronised).
+ *     scratch owned by the caller.  Its first 40 KiB hold counters that must
+ *     be zero before the first call that uses the workspace (allocate it
+ *     zero-filled); every call keeps them consistent for the next one (arrival
+ *     counters return to zero, call counters advance by a fixed amount).  The
+ *     32-bit word at byte offset 1024 counts the workgroups whose bounded wait
+ *     gave up (see below); it is never reset by the library.  Calls that share
+ *     a workspace must be ordered (same stream, or synchronised).
+ *   - The few-token path (T <= 4) is one launch whose workgroups wait for each
+ *     other with bounded waits (about a second each), so it needs the whole
+ *     grid resident at once: nothing else may hold the device's compute units
+ *     for that long while it runs.  If a wait gives up, the call writes NaN to
+ *     the outputs that depend on the missing values (in practice all of out),
+ *     counts the give-up in the workspace word above, and leaves the workspace
+ *     usable: the next call is unaffected.  MOE_DEBUG_WAIT_GIVE_UP forces this
+ *     path for testing.
  *   - Device-side routing ids outside [0, E) passed to moe_experts_w4a16
  *     contribute nothing (they are never dereferenced).
  */
@@ -81,6 +92,11 @@ extern "C" {
 #define MOE_PATH_AUTO 0u   /* few tokens: persistent GEMV launch; otherwise grouped MFMA GEMMs */
 #define MOE_PATH_DECODE 1u /* force the few-token path (T <= 4) */
 #define MOE_PATH_CHUNK 2u  /* force the grouped-GEMM path */
+/* dims.flags bit (test hook): every bounded wait of the few-token path gives
+ * up at once, as it would if the launch's workgroups could not all run at the
+ * same time.  The call then writes NaN to out (see the few-token path's
+ * failure contract below) and the workspace stays usable. */
+#define MOE_DEBUG_WAIT_GIVE_UP 0x100u
 
 typedef struct {
   int32_t hidden;       /* H */
@@ -89,7 +105,7 @@ typedef struct {
   int32_t expert_inter; /* I: routed-expert intermediate width */
   int32_t shared_inter; /* Is: shared-expert intermediate width */
   int32_t group;        /* G: quantisation group along K, must be 64 */
-  uint32_t flags;       /* MOE_PATH_* */
+  uint32_t flags;       /* MOE_PATH_*, optionally | MOE_DEBUG_WAIT_GIVE_UP */
 } moe_dims;
 
 typedef struct {

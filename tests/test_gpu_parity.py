@@ -161,8 +161,17 @@ def test_workspace_reused_across_token_counts():
     for case, o in zip(seq, res):
         want = ref.forward(case.x, W_host, d)["out"]
         assert _gpu.row_rel_l2(o, want).max() <= _gpu.ROW_TOL
-    # the workspace's counters and done flags are back to zero
-    assert int(ws[: 40 * 1024].view(torch.int32).abs().sum()) == 0
+    # The workspace's sync area: each of the 8 per-group call counters (64-bit,
+    # one 128-byte line each) advanced by exactly 2^16 per few-token call (4 of
+    # the 5 calls), the give-up word is zero, and every other word (arrival
+    # counters, the multi-token path's counter) is back to zero.
+    sync = ws[: 40 * 1024].cpu().numpy().view(np.uint32).copy()
+    calls = sum(1 for c in seq if c.T <= 4)
+    for g in range(8):
+        lo, hi = sync[32 * g], sync[32 * g + 1]
+        assert (int(hi) << 32 | int(lo)) == calls << 16, f"group {g} call counter"
+        sync[32 * g] = sync[32 * g + 1] = 0
+    assert int(sync.astype(np.int64).sum()) == 0
 
 
 def test_max_token_count_sampled():
@@ -215,3 +224,43 @@ def test_hip_graph_replays_match_eager(T):
         assert torch.equal(out, want), f"replay {rep} differs from eager"
         m.moe_forward(dims, W.struct, x2, T, out2, ws=ws)  # eager work between replays
         torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("cfg", [0, 1])
+def test_few_token_give_up_is_loud_and_recoverable(cfg):
+    """A few-token call whose bounded waits give up (forced from the host with
+    the MOE_DEBUG_WAIT_GIVE_UP flag, so every kernel still exits normally)
+    writes NaN to every output and counts the give-ups in the workspace; the
+    next call on the same workspace is correct again."""
+    case = _gpu.config_case(cfg)
+    d, T = case.dims, case.T
+    W = _gpu.device_weights(case)
+    x = _gpu.x_tensor(case)
+    ws = m.workspace(_gpu.dims_of(d), T)
+    word = m.GIVE_UP_WORD_OFFSET // 4
+    before = int(ws.view(torch.int32)[word].item())
+    for mode in ("forward", "experts"):
+        out = torch.zeros((T, d.H), dtype=torch.int16, device="cuda")
+        dims = _gpu.dims_of(d, m.PATH_DECODE | m.DEBUG_WAIT_GIVE_UP)
+        if mode == "forward":
+            m.moe_forward(dims, W.struct, x, T, out, ws=ws)
+        else:
+            ids = torch.zeros((T, d.k), dtype=torch.int32, device="cuda")
+            w = torch.full((T, d.k), 0.5, dtype=torch.float32, device="cuda")
+            m.moe_experts_w4a16(dims, W.struct, x, T, ids, w, out, ws=ws)
+        torch.cuda.synchronize()
+        got = _gpu.half_to_f64(out)
+        assert np.isnan(got).all(), f"{mode}: {np.isfinite(got).sum()} finite outputs after a give-up"
+    after = int(ws.view(torch.int32)[word].item())
+    assert after - before >= 2 * 8, "the give-ups were not counted"
+    _gpu.log(f"give-up word {before} -> {after}")
+    # the workspace is consistent: a normal call right after is correct
+    out = torch.full((T, d.H), 0x7E00, dtype=torch.int16, device="cuda")
+    ids = torch.full((T, d.k), -7, dtype=torch.int32, device="cuda")
+    w = torch.full((T, d.k), -1.0, dtype=torch.float32, device="cuda")
+    sig = torch.full((T,), -1.0, dtype=torch.float32, device="cuda")
+    m.moe_forward(_gpu.dims_of(d, m.PATH_DECODE), W.struct, x, T, out, ids, w, sig, ws)
+    torch.cuda.synchronize()
+    g = dict(out=_gpu.half_to_f64(out), ids=ids.cpu().numpy(), w=w.cpu().numpy().astype(np.float64),
+             sigma=sig.cpu().numpy().astype(np.float64))
+    _gpu.check_forward(case, _gpu.config_oracle(cfg), g, f"cfg{cfg} after give-up")

@@ -12,6 +12,8 @@ from .binding import (  # noqa: F401
     PATH_AUTO,
     PATH_DECODE,
     PATH_CHUNK,
+    DEBUG_WAIT_GIVE_UP,
+    GIVE_UP_WORD_OFFSET,
     lib,
     library_path,
     moe_workspace_bytes,

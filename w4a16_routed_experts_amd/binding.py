@@ -13,6 +13,8 @@ from typing import Optional
 from .build import LIB_PATH
 
 PATH_AUTO, PATH_DECODE, PATH_CHUNK = 0, 1, 2
+DEBUG_WAIT_GIVE_UP = 0x100  # dims.flags test hook: the few-token path's bounded waits give up at once
+GIVE_UP_WORD_OFFSET = 1024  # byte offset in the workspace of the give-up counter
 
 _STATUS = {0: "MOE_OK", -1: "MOE_ERR_NULL", -2: "MOE_ERR_SHAPE", -3: "MOE_ERR_ALIGN",
            -4: "MOE_ERR_WORKSPACE", -5: "MOE_ERR_LAUNCH", -6: "MOE_ERR_DEVICE", -7: "MOE_ERR_SCRATCH"}

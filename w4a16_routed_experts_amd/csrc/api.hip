@@ -25,6 +25,7 @@ using namespace moe;
 constexpr int kMaxT = 65536;
 constexpr int kMaxWidth = 4096;
 constexpr size_t kDecodeMaxLds = 64 * 1024;
+constexpr uint32_t kPathMask = 0xFFu;
 
 size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
@@ -42,24 +43,25 @@ int check_dims(const moe_dims* d, int32_t T) {
   if (d->num_experts < 1 || d->num_experts > kMaxExperts) return MOE_ERR_SHAPE;
   if (d->top_k < 1 || d->top_k > kMaxTopK || d->top_k > d->num_experts) return MOE_ERR_SHAPE;
   if (!width_ok(d->hidden) || !width_ok(d->expert_inter) || !width_ok(d->shared_inter)) return MOE_ERR_SHAPE;
-  if (d->flags > MOE_PATH_CHUNK) return MOE_ERR_SHAPE;
+  if ((d->flags & kPathMask) > MOE_PATH_CHUNK || (d->flags & ~(kPathMask | MOE_DEBUG_WAIT_GIVE_UP))) return MOE_ERR_SHAPE;
   if (T < 0 || T > kMaxT) return MOE_ERR_SHAPE;
   return MOE_OK;
 }
 
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
-size_t decode_lds_bytes(const moe_dims* d, int T) {
-  const size_t act = (size_t)std::max(T * d->hidden, T * d->top_k * d->expert_inter);
-  return (act + (size_t)T * d->shared_inter) * 2;
+// the few-token path's plan for a grid of nb workgroups (the workspace and
+// LDS sizes do not depend on nb)
+DecodePlan plan_of(const moe_dims* d, int T, int nb = kGroups * kMaxGroupWgs) {
+  return decode_plan(d->hidden, d->num_experts, d->top_k, d->expert_inter, d->shared_inter, T, nb);
 }
 
 bool decode_admissible(const moe_dims* d, int T) {
-  return T >= 1 && T <= kDecMaxT && decode_lds_bytes(d, T) <= kDecodeMaxLds;
+  return T >= 1 && T <= kDecMaxT && decode_lds_bytes(plan_of(d, T)) <= kDecodeMaxLds;
 }
 
 bool use_decode(const moe_dims* d, int T) {
-  if (d->flags == MOE_PATH_CHUNK) return false;
+  if ((d->flags & kPathMask) == MOE_PATH_CHUNK) return false;
   return decode_admissible(d, T);  // AUTO and DECODE both take it when it fits
 }
 
@@ -84,25 +86,14 @@ struct Carve {
 
 struct DecodeWs {
   uint32_t* sync;
-  float* logits;
-  float* h_s;
-  float* h_e;
-  float* s_sh;
+  uint64_t* tagged;
 };
 
-DecodePlan plan_of(const moe_dims* d, int T, bool routed_only) {
-  return decode_plan(d->hidden, d->num_experts, d->top_k, d->expert_inter, d->shared_inter, T, routed_only);
-}
-
 DecodeWs carve_decode(const moe_dims* d, int T, Carve& c) {
-  // sized for the complete block; the routed half alone uses a subset
-  const DecodePlan p = plan_of(d, T, false);
+  const DecodePlan p = plan_of(d, T);
   DecodeWs w;
   w.sync = c.take<uint32_t>(kSyncBytes);
-  w.logits = c.take<float>(decode_region_floats(p, T, 0) * 4);
-  w.h_s = c.take<float>(decode_region_floats(p, T, 1) * 4);
-  w.h_e = c.take<float>(decode_region_floats(p, T, 2) * 4);
-  w.s_sh = c.take<float>(decode_region_floats(p, T, 3) * 4);
+  w.tagged = c.take<uint64_t>(p.z_words * 8);
   return w;
 }
 
@@ -210,24 +201,27 @@ int run_decode(const moe_dims* d, const moe_weights* w, const uint16_t* x, int T
   int st = device_info(&di);
   if (st != MOE_OK) return st;
   DecodeArgs a{};
-  a.H = d->hidden; a.E = d->num_experts; a.k = d->top_k; a.I = d->expert_inter; a.Is = d->shared_inter; a.T = T;
   fill_weights(w, &a.router_q, &a.router_s, &a.w13_q, &a.w13_s, &a.w2_q, &a.w2_s, &a.sh13_q, &a.sh13_s, &a.sh2_q,
                &a.sh2_s);
   a.x = x; a.out = out;
   a.gain = gain; a.eps = eps;
   a.ids_out = ids_out; a.w_out = w_out; a.sigma_out = sig_out;
   a.ids_in = ids_in; a.w_in = w_in;
+  a.give_up = (d->flags & MOE_DEBUG_WAIT_GIVE_UP) ? 1 : 0;
   Carve c{static_cast<char*>(ws)};
   DecodeWs dw = carve_decode(d, T, c);
-  a.sync = dw.sync; a.logits = dw.logits; a.h_s = dw.h_s; a.h_e = dw.h_e; a.s_sh = dw.s_sh;
-  a.p = plan_of(d, T, mode == DEC_EXPERTS);
-  const size_t lds = decode_lds_bytes(d, T);
-  const bool real = decode_real_widths(a.H, a.I, a.Is);
+  a.sync = dw.sync; a.tagged = dw.tagged;
+  const size_t lds = decode_lds_bytes(plan_of(d, T));
+  const bool real = decode_real_widths(d->hidden, d->expert_inter, d->shared_inter);
   const int per_cu = di->occ[mode][real ? 1 : 0][(lds + 4095) / 4096];
-  if (per_cu < 1) return MOE_ERR_LAUNCH;
-  const int want = std::max(std::max(a.p.n_router + a.p.n_shup, a.p.n_up + a.p.n_sd), a.p.n_down);
-  const int grid = std::max(1, std::min(want, per_cu * di->cus));
-  return launch_decode(a, mode, grid, lds, s);
+  // Every workgroup must be resident at once (they wait for each other, with
+  // bounded waits): the grid is what an idle device holds, in whole groups of
+  // 8, at most 8 x kMaxGroupWgs; a group needs at least H / 64 members (its
+  // members' output rows fit the per-block row buffer).
+  const int nj = std::min(kMaxGroupWgs, per_cu * di->cus / kGroups);
+  if (nj < 1 || nj * kMaxGroupWgs < d->hidden) return MOE_ERR_LAUNCH;
+  a.p = plan_of(d, T, kGroups * nj);
+  return launch_decode(a, mode, lds, s);
 }
 
 ChunkArgs chunk_args(const moe_dims* d, const moe_weights* w, const uint16_t* x, int T, uint16_t* out, void* ws) {
@@ -249,7 +243,7 @@ int check_common(const moe_dims* d, const void* x, int32_t T, void* ws, size_t w
   if (!x || !ws) return MOE_ERR_NULL;
   if (!aligned(x, 16) || !aligned(ws, 256)) return MOE_ERR_ALIGN;
   if (ws_bytes < workspace_bytes(d, T)) return MOE_ERR_WORKSPACE;
-  if (d->flags == MOE_PATH_DECODE && !decode_admissible(d, T)) return MOE_ERR_SHAPE;
+  if ((d->flags & kPathMask) == MOE_PATH_DECODE && !decode_admissible(d, T)) return MOE_ERR_SHAPE;
   return MOE_OK;
 }
 

@@ -1,64 +1,76 @@
-// Arguments and launcher of the few-token (persistent GEMV) path.
+// Arguments and launcher of the few-token path (T <= 4): one persistent launch.
 #pragma once
 #include "common.hpp"
 
 namespace moe {
 
 static constexpr int kDecMaxT = 4;        // tokens per call on this path
+static constexpr int kGroups = 8;         // workgroup groups (block b is in group b % 8, one per XCD)
+static constexpr int kMaxGroupWgs = 64;   // workgroups per group at most (grid <= 512)
 static constexpr int kSyncStride = 32;    // counters 128 bytes apart (in 32-bit words)
-static constexpr int kXcds = 8;           // XCDs of an MI355X
-static constexpr int kFlagPage = 1024;    // per-XCD flag pages 4 KiB apart (in words)
-static constexpr int kCounterPages = 2;   // 64 counter slots
-static constexpr int kSubCounters = 8;    // items of a stage count on 8 sub-counters, then one top counter
-static constexpr int kSyncBytes = (kCounterPages + kXcds) * kFlagPage * 4;  // counters, then one flag page per XCD
-enum { SYNC_ROUTER = 0, SYNC_SHUP = 1, SYNC_UP = 2, SYNC_SD = 3, SYNC_EXIT = 4, SYNC_ERR = 5, SYNC_COUNT = 6 };
+static constexpr int kCounterPages = 2;   // words [0, 2048) of the sync area: path counters
+static constexpr int kFlagPage = 1024;    // words per page
+static constexpr int kSyncBytes = (kCounterPages + 8) * kFlagPage * 4;  // 40 KiB, zero between calls
+static constexpr int kMaxHidden = 4096;   // widest admitted hidden size
 enum { DEC_FORWARD = 0, DEC_EXPERTS = 1, DEC_BLOCK = 2 };  // DEC_BLOCK: the forward with RMSNorm and residual
 static constexpr int kDecModes = 3;
-static constexpr int kMaxHidden = 4096;  // widest admitted hidden size
 
-__host__ __device__ constexpr int round32(int x) { return (x + 31) / 32 * 32; }
+// Sync-area words used by the few-token path (the grouped-GEMM path uses the
+// word at kCounterPages * kFlagPage - kSyncStride).
+static constexpr int kJoinWord = 0;                       // 8 call counters (64-bit), one line each
+static constexpr int kGiveUpWord = 8 * kSyncStride;       // count of workgroups whose bounded wait gave up
+static constexpr uint64_t kJoinQuantum = 1u << 16;        // each call adds exactly this to every call counter
 
-// rows of a K-wide row that one 64-lane load covers (16-byte chunks per lane)
-__host__ __device__ constexpr int rows_per_load(int K, int bits) {
-  return 64 / ((K * bits / 128) < 64 ? (K * bits / 128) : 64);
-}
-
-// Work decomposition of the few-token path; the host and the kernel both use
-// these numbers.  Every item writes its results to its own 128-byte-aligned
-// region of the workspace (floats), so no cache line is shared by producers.
+// Work decomposition; the host and the kernel both use these numbers.
 struct DecodePlan {
-  int n_router, n_shup, n_up, n_sd, n_down;
-  int up_jblocks;           // j-blocks per (token, slot)
-  int lg_rows, lg_stride;   // router rows per item; floats per (item, token)
-  int hs_cols, hs_stride;   // shared gate/up columns per item; floats per (item, token)
-  int he_cols, he_stride;   // expert gate/up columns per item; floats (4-byte units) per item
-  int ss_rows, ss_stride;   // shared down rows per item; floats per (item, token)
-  int down_rows;            // output rows per down item
+  int T, H, E, k, I, Is;
+  int nb, nj;     // grid, workgroups per group (nb / 8)
+  int S;          // shared-expert slices: 8 (one per group) or 1 (group 0 takes it all)
+  int sw;         // shared intermediate columns per slice (Is / S)
+  int npg;        // routed (token, slot) pairs per group at most: ceil(T k / 8)
+  int cw;         // routed intermediate columns per workgroup and pair: ceil(I / nj)
+  int rw;         // output rows per workgroup: ceil(H / nj)
+  int scw;        // shared columns per workgroup: ceil(sw / nj)
+  // tagged zones (64-bit words: call tag << 32 | value bits)
+  size_t z_logits;  // [T][E + 1]
+  size_t z_route;   // [8][16]: per group, pair experts (4), pair weights (4), sigma per token (4)
+  size_t z_hs;      // [8][T][sw] shared SwiGLU activations of each slice
+  size_t z_h;       // [8][npg][I] routed SwiGLU activations of each group's pairs
+  size_t z_part;    // [8][T][H] each group's partial output rows
+  size_t z_words;   // total tagged words
 };
 
-__host__ __device__ inline DecodePlan decode_plan(int H, int E, int k, int I, int Is, int T, bool routed_only) {
+__host__ __device__ inline DecodePlan decode_plan(int H, int E, int k, int I, int Is, int T, int nb) {
   DecodePlan p;
-  const int r8h = rows_per_load(H, 8), r4h = rows_per_load(H, 4), r8s = rows_per_load(Is, 8);
-  p.lg_rows = 4 * r8h;
-  p.hs_cols = 8 * r8h;
-  p.he_cols = 16 * r4h;
-  p.ss_rows = 16 * r8s;
-  p.lg_stride = round32(p.lg_rows);
-  p.hs_stride = round32(p.hs_cols);
-  p.he_stride = round32(p.he_cols);
-  p.ss_stride = round32(p.ss_rows);
-  p.n_router = routed_only ? 0 : (E + 1 + p.lg_rows - 1) / p.lg_rows;
-  p.n_shup = routed_only ? 0 : (Is + p.hs_cols - 1) / p.hs_cols;
-  p.up_jblocks = (I + p.he_cols - 1) / p.he_cols;
-  p.n_up = T * k * p.up_jblocks;
-  p.n_sd = routed_only ? 0 : (H + p.ss_rows - 1) / p.ss_rows;
-  p.down_rows = rows_per_load(I, 4);
-  p.n_down = T * (H / p.down_rows);
+  p.T = T; p.H = H; p.E = E; p.k = k; p.I = I; p.Is = Is;
+  p.nb = nb;
+  p.nj = nb / kGroups;
+  p.S = (Is / kGroups) % 16 == 0 ? kGroups : 1;
+  p.sw = Is / p.S;
+  p.npg = (T * k + kGroups - 1) / kGroups;
+  p.cw = (I + p.nj - 1) / p.nj;
+  p.rw = (H + p.nj - 1) / p.nj;
+  p.scw = (p.sw + p.nj - 1) / p.nj;
+  size_t o = 0;
+  p.z_logits = o; o += (size_t)T * (E + 1);
+  o = (o + 15) / 16 * 16;
+  p.z_route = o; o += (size_t)kGroups * 16;
+  p.z_hs = o; o += (size_t)kGroups * T * p.sw;
+  o = (o + 15) / 16 * 16;
+  p.z_h = o; o += (size_t)kGroups * p.npg * I;
+  o = (o + 15) / 16 * 16;
+  p.z_part = o; o += (size_t)kGroups * T * H;
+  p.z_words = (o + 15) / 16 * 16;
   return p;
 }
 
+// dynamic LDS of one workgroup: activations [T][H], the group's routed h
+// [npg][I] and its shared slice [T][sw], all binary16
+__host__ __device__ inline size_t decode_lds_bytes(const DecodePlan& p) {
+  return ((size_t)p.T * p.H + (size_t)p.npg * p.I + (size_t)p.T * p.sw) * 2;
+}
+
 struct DecodeArgs {
-  int H, E, k, I, Is, T;
   const int8_t* router_q; const uint16_t* router_s;
   const uint8_t* w13_q; const uint16_t* w13_s;
   const uint8_t* w2_q; const uint16_t* w2_s;
@@ -70,26 +82,15 @@ struct DecodeArgs {
   float eps;             // DEC_BLOCK: RMSNorm epsilon
   int32_t* ids_out; float* w_out; float* sigma_out;  // nullable
   const int32_t* ids_in; const float* w_in;          // routing given by the caller
-  uint32_t* sync;
-  float* logits;   // router hand-off:      [n_router][T][lg_stride]
-  float* h_s;      // shared gate/up:       [n_shup][T][hs_stride]
-  float* h_e;      // expert gate/up:       [n_up][he_stride], he_cols binary16 values each
-  float* s_sh;     // shared down:          [n_sd][T][ss_stride]
+  uint32_t* sync;        // the workspace's sync area (kSyncBytes)
+  uint64_t* tagged;      // tagged zones (plan.z_words words)
+  int give_up;           // nonzero: every bounded wait gives up at once (exercises the failure path)
   DecodePlan p;
 };
 
-// floats of each hand-off region
-inline size_t decode_region_floats(const DecodePlan& p, int T, int which) {
-  switch (which) {
-    case 0: return (size_t)p.n_router * T * p.lg_stride;
-    case 1: return (size_t)p.n_shup * T * p.hs_stride;
-    case 2: return (size_t)p.n_up * p.he_stride;
-    default: return (size_t)p.n_sd * T * p.ss_stride;
-  }
-}
 
 int decode_blocks_per_cu(int mode, bool real_widths, size_t lds_bytes);
-int launch_decode(const DecodeArgs& a, int mode, int grid, size_t lds_bytes, hipStream_t s);
+int launch_decode(const DecodeArgs& a, int mode, size_t lds_bytes, hipStream_t s);
 bool decode_real_widths(int H, int I, int Is);
 
 }  // namespace moe

@@ -85,61 +85,91 @@ __device__ __forceinline__ float chunk_dot8(uint4 wq, const h2 xp[8]) {
 template <int BITS>
 __device__ __forceinline__ int chunk_group(int c) { return BITS == 4 ? (c >> 1) : (c >> 2); }
 
-// This lane's partial dot products for `nb` row-batches (one wave-load of
-// g.rpb rows each; rows[b] is this lane's row in batch b, or -1 when masked)
-// against TT activation vectors act + t*act_stride, scaled per group.  All
-// weight loads are issued before any arithmetic.  A lane's chunk index does
-// not depend on the batch, so each activation chunk is converted once.
-template <int BITS, int MAXB, int MAXCPL, int TT>
-__device__ __forceinline__ void lane_rows_dot(const uint8_t* __restrict__ W, const uint16_t* __restrict__ S, int K,
-                                              const int rows[MAXB], int nb, const RowGeom& g,
-                                              const _Float16* act, int act_stride, int T, float acc[MAXB][TT]) {
-  const int lane = threadIdx.x & 63;
-  const size_t row_bytes = (size_t)K * BITS / 8;
-  const int ngroups = K / kGroup;
-  constexpr int EPC = BITS == 4 ? 32 : 16;  // codes per 16-byte chunk
-  uint4 wq[MAXB][MAXCPL];
-  float sc[MAXB][MAXCPL];
+// per-lane 16-byte chunks of up to NB row-batches
+template <int BITS, int NB, int MAXCPL>
+struct Frag {
+  uint4 q[NB][MAXCPL];
+  uint16_t s[NB][MAXCPL];  // binary16 scale bits (converted where they are used)
+
+  // rows[b]: this lane's row pointer in batch b (nullptr = masked); srow: its
+  // scales (always a valid row).  A masked lane reads `safe` (a valid row)
+  // instead: its products land in its own row's accumulator, which the caller
+  // discards.  Only pointers are selected, never loaded values, so every load
+  // of the batch is in flight before the first one is waited for.
+  __device__ __forceinline__ void load(const uint8_t* const rows[NB], const uint16_t* const srow[NB],
+                                       const RowGeom& g, const uint8_t* safe) {
+    const int lane = threadIdx.x & 63;
 #pragma unroll
-  for (int b = 0; b < MAXB; ++b) {
+    for (int b = 0; b < NB; ++b)
+#pragma unroll
+      for (int m = 0; m < MAXCPL; ++m) {
+        const int c = (lane % g.lpr) + g.lpr * (m < g.cpl ? m : 0);
+        const uint8_t* src = rows[b] != nullptr ? rows[b] : safe;
+        q[b][m] = *reinterpret_cast<const uint4*>(src + 16 * (size_t)c);
+        s[b][m] = srow[b][chunk_group<BITS>(c)];
+      }
+  }
+
+  // acc[b][t] = this lane's share of row_b . act_t (same activations for every batch)
+  template <int TT>
+  __device__ __forceinline__ void dot_shared(const RowGeom& g, const _Float16* act, int stride, int T,
+                                             float acc[NB][TT]) const {
+    const int lane = threadIdx.x & 63;
+    constexpr int EPC = BITS == 4 ? 32 : 16;
+#pragma unroll
+    for (int b = 0; b < NB; ++b)
+#pragma unroll
+      for (int t = 0; t < TT; ++t) acc[b][t] = 0.f;
 #pragma unroll
     for (int m = 0; m < MAXCPL; ++m) {
-      wq[b][m] = make_uint4(0, 0, 0, 0);
-      sc[b][m] = 0.f;
-      if (b < nb && m < g.cpl && rows[b] >= 0) {
+      if (m < g.cpl) {
         const int c = (lane % g.lpr) + g.lpr * m;
-        wq[b][m] = *reinterpret_cast<const uint4*>(W + (size_t)rows[b] * row_bytes + 16 * (size_t)c);
-        sc[b][m] = half_bits_to_float(S[(size_t)rows[b] * ngroups + chunk_group<BITS>(c)]);
+#pragma unroll
+        for (int t = 0; t < TT; ++t) {
+          if (t < T) {
+            const _Float16* a = act + (size_t)t * stride + EPC * c;
+            if (BITS == 4) {
+              h2 xp[16];
+              act32(a, xp);
+#pragma unroll
+              for (int b = 0; b < NB; ++b) acc[b][t] = fmaf(chunk_dot4(q[b][m], xp), half_bits_to_float(s[b][m]), acc[b][t]);
+            } else {
+              h2 xp[8];
+              act16(a, xp);
+#pragma unroll
+              for (int b = 0; b < NB; ++b) acc[b][t] = fmaf(chunk_dot8(q[b][m], xp), half_bits_to_float(s[b][m]), acc[b][t]);
+            }
+          }
+        }
       }
     }
   }
+
+  // acc[b] = this lane's share of row_b . act_b (one activation vector per batch)
+  __device__ __forceinline__ void dot_per_batch(const RowGeom& g, const _Float16* const act[NB], float acc[NB]) const {
+    const int lane = threadIdx.x & 63;
+    constexpr int EPC = BITS == 4 ? 32 : 16;
 #pragma unroll
-  for (int b = 0; b < MAXB; ++b)
+    for (int b = 0; b < NB; ++b) {
+      acc[b] = 0.f;
+      if (act[b] == nullptr) continue;
 #pragma unroll
-    for (int t = 0; t < TT; ++t) acc[b][t] = 0.f;
-#pragma unroll
-  for (int m = 0; m < MAXCPL; ++m) {
-    if (m >= g.cpl) break;
-    const int c = (lane % g.lpr) + g.lpr * m;
-#pragma unroll
-    for (int t = 0; t < TT; ++t) {
-      if (t >= T) break;
-      const _Float16* a = act + (size_t)t * act_stride + EPC * c;
-      if (BITS == 4) {
-        h2 xp[16];
-        act32(a, xp);
-#pragma unroll
-        for (int b = 0; b < MAXB; ++b)
-          if (b < nb) acc[b][t] = fmaf(chunk_dot4(wq[b][m], xp), sc[b][m], acc[b][t]);
-      } else {
-        h2 xp[8];
-        act16(a, xp);
-#pragma unroll
-        for (int b = 0; b < MAXB; ++b)
-          if (b < nb) acc[b][t] = fmaf(chunk_dot8(wq[b][m], xp), sc[b][m], acc[b][t]);
+      for (int m = 0; m < MAXCPL; ++m) {
+        if (m < g.cpl) {
+          const int c = (lane % g.lpr) + g.lpr * m;
+          if (BITS == 4) {
+            h2 xp[16];
+            act32(act[b] + EPC * c, xp);
+            acc[b] = fmaf(chunk_dot4(q[b][m], xp), half_bits_to_float(s[b][m]), acc[b]);
+          } else {
+            h2 xp[8];
+            act16(act[b] + EPC * c, xp);
+            acc[b] = fmaf(chunk_dot8(q[b][m], xp), half_bits_to_float(s[b][m]), acc[b]);
+          }
+        }
       }
     }
   }
-}
+};
 
 }  // namespace moe
