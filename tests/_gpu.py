@@ -23,6 +23,11 @@ from workloads import gen
 GAP_EXEMPT = 1e-3
 ROW_TOL = 2e-3
 W_TOL = 2e-5
+# Element guard beside the per-row bar: a mistake confined to one output
+# element (one mis-scaled group or row of a down projection) moves a row's
+# relative L2 error by less than 2e-3, but that element by far more than the
+# few 1e-3 of the row's RMS that binary16 rounding leaves.
+ELEM_TOL = 2e-2
 
 
 def log(*a):
@@ -157,7 +162,16 @@ def check_forward(case, r, gpu, label=""):
             routed = ref.experts(case.x[t : t + 1], ids_g, w_g, case.weights, d)
             want[t] = routed[0] + r["sigma"][t] * r["shared"][t]
     err = row_rel_l2(gpu["out"], want)
-    log(f"{label}: per-row rel L2 max {err.max():.3e} median {np.median(err):.3e}")
+    elem = elem_err(gpu["out"], want)
+    log(f"{label}: per-row rel L2 max {err.max():.3e} median {np.median(err):.3e}; "
+        f"largest element error {elem.max():.3e} of the row RMS")
     assert np.all(np.isfinite(gpu["out"])), f"{label}: non-finite output"
     assert err.max() <= ROW_TOL, f"{label}: row {int(err.argmax())} rel L2 {err.max():.3e}"
+    assert elem.max() <= ELEM_TOL, f"{label}: row {int(elem.argmax())} element error {elem.max():.3e} of its RMS"
     return err
+
+
+def elem_err(a, b):
+    """Per row, the largest |a - b| over the row's RMS of b."""
+    rms = np.sqrt((b ** 2).mean(axis=1))
+    return np.abs(a - b).max(axis=1) / np.maximum(rms, 1e-30)

@@ -105,10 +105,13 @@ __device__ __forceinline__ bool wave_poll(const uint64_t* w, int n, uint32_t tag
 
 // ------------------------------------------------------------------ kernel
 
-// HC, IC, ISC: compile-time H, I, Is (0: taken from the plan).  CB: column
-// batches of the gate/up rows in flight per wave; DB: row batches of the down
-// rows prefetched per wave.
-template <int MODE, int HC, int IC, int ISC>
+// HC, IC, ISC: compile-time H, I, Is (0: taken from the plan); TT: most tokens
+// the instance handles (1, or kDecMaxT).  Every phase of a launch runs once, so
+// code is kept short: the per-token loops are unrolled for TT tokens only, and
+// the loops that cover more rows than one wave-load holds (small grids) exist
+// only in the generic instances.  CB: column batches of the gate/up rows in
+// flight per wave; DB: row batches of the down rows prefetched per wave.
+template <int MODE, int HC, int IC, int ISC, int TT>
 __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
   extern __shared__ uint4 smem_raw[];
   const DecodePlan& p = a.p;
@@ -214,20 +217,20 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
   // ---------------- stage A: publish logits and the shared slice's activations
   if (MODE != DEC_EXPERTS) {
     if (wave == 0 && r_first <= E) {
-      float acc[1][kDecMaxT];
-      fr.template dot_shared<kDecMaxT>(g8h, act, H, T, acc);
+      float acc[1][TT];
+      fr.template dot_shared<TT>(g8h, act, H, T, acc);
 #pragma unroll
-      for (int t = 0; t < kDecMaxT; ++t)
+      for (int t = 0; t < TT; ++t)
         if (t < T) {
           const float v = lane_group_sum(acc[0][t], g8h.lpr);
           if (r_row >= 0 && (lane % g8h.lpr) == 0) put_tagged_f(zl + (size_t)t * (E + 1) + r_row, tag, v);
         }
     }
     if (wave == 1 && g < S && j < sw) {
-      float acc[2][kDecMaxT];
-      fs.template dot_shared<kDecMaxT>(g8h, act, H, T, acc);
+      float acc[2][TT];
+      fs.template dot_shared<TT>(g8h, act, H, T, acc);
 #pragma unroll
-      for (int t = 0; t < kDecMaxT; ++t)
+      for (int t = 0; t < TT; ++t)
         if (t < T) {
           const float gt = lane_group_sum(acc[0][t], g8h.lpr);
           const float up = lane_group_sum(acc[1][t], g8h.lpr);
@@ -236,23 +239,23 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
         }
     }
     // more router rows or shared columns than one wave-load holds (small grids)
-    for (int r0 = r_first + nb * g8h.rpb; r0 <= E; r0 += nb * g8h.rpb) {
+    for (int r0 = r_first + nb * g8h.rpb; HC == 0 && r0 <= E; r0 += nb * g8h.rpb) {
       if (wave != 0) break;
       const int r = r0 + nb * (lane / g8h.lpr);
       const uint8_t* rows[1] = {r <= E ? reinterpret_cast<const uint8_t*>(a.router_q) + (size_t)r * H : nullptr};
       const uint16_t* srow[1] = {a.router_s + (size_t)(r <= E ? r : 0) * (H / kGroup)};
       Frag<8, 1, CPL8H> f;
       f.load(rows, srow, g8h, reinterpret_cast<const uint8_t*>(a.router_q));
-      float acc[1][kDecMaxT];
-      f.template dot_shared<kDecMaxT>(g8h, act, H, T, acc);
+      float acc[1][TT];
+      f.template dot_shared<TT>(g8h, act, H, T, acc);
 #pragma unroll
-      for (int t = 0; t < kDecMaxT; ++t)
+      for (int t = 0; t < TT; ++t)
         if (t < T) {
           const float v = lane_group_sum(acc[0][t], g8h.lpr);
           if (r <= E && (lane % g8h.lpr) == 0) put_tagged_f(zl + (size_t)t * (E + 1) + r, tag, v);
         }
     }
-    for (int c0 = j + nj * g8h.rpb; g < S && c0 < sw; c0 += nj * g8h.rpb) {
+    for (int c0 = j + nj * g8h.rpb; HC == 0 && g < S && c0 < sw; c0 += nj * g8h.rpb) {
       if (wave != 1) break;
       const int c = c0 + nj * (lane / g8h.lpr);
       const int cg = g * sw + (c < sw ? c : 0);
@@ -261,10 +264,10 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
       const uint16_t* srow[2] = {a.sh13_s + (size_t)cg * (H / kGroup), a.sh13_s + (size_t)(Is + cg) * (H / kGroup)};
       Frag<8, 2, CPL8H> f;
       f.load(rows, srow, g8h, base);
-      float acc[2][kDecMaxT];
-      f.template dot_shared<kDecMaxT>(g8h, act, H, T, acc);
+      float acc[2][TT];
+      f.template dot_shared<TT>(g8h, act, H, T, acc);
 #pragma unroll
-      for (int t = 0; t < kDecMaxT; ++t)
+      for (int t = 0; t < TT; ++t)
         if (t < T) {
           const float gt = lane_group_sum(acc[0][t], g8h.lpr);
           const float up = lane_group_sum(acc[1][t], g8h.lpr);
@@ -458,10 +461,10 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
         const uint16_t* srow[1] = {a.sh2_s + (size_t)(ok ? n : 0) * (Is / kGroup) + (size_t)g * sw / kGroup};
         f.load(rows, srow, g8s, base);
       }
-      float acc[1][kDecMaxT];
-      f.template dot_shared<kDecMaxT>(g8s, hs, sw, T, acc);
+      float acc[1][TT];
+      f.template dot_shared<TT>(g8s, hs, sw, T, acc);
 #pragma unroll
-      for (int t = 0; t < kDecMaxT; ++t)
+      for (int t = 0; t < TT; ++t)
         if (t < T) {
           const float v = lane_group_sum(acc[0][t], g8s.lpr);
           if (ok && (lane % g8s.lpr) == 0) s_part[t][r] = s_sig[t] * v;
@@ -559,8 +562,9 @@ bool decode_real_widths(int H, int I, int Is) { return H == 2048 && I == 512 && 
 template <int MODE>
 static int occupancy(bool real, size_t lds) {
   int n = 0;
-  hipError_t err = real ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_kernel<MODE, 2048, 512, 512>, 256, lds)
-                        : hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_kernel<MODE, 0, 0, 0>, 256, lds);
+  hipError_t err = real ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_kernel<MODE, 2048, 512, 512, kDecMaxT>,
+                                                                       256, lds)
+                        : hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_kernel<MODE, 0, 0, 0, kDecMaxT>, 256, lds);
   return err == hipSuccess ? n : 0;
 }
 
@@ -569,18 +573,24 @@ int decode_blocks_per_cu(int mode, bool real, size_t lds_bytes) {
   return mode == DEC_FORWARD ? occupancy<DEC_FORWARD>(real, lds_bytes) : occupancy<DEC_EXPERTS>(real, lds_bytes);
 }
 
+template <int MODE, int HC, int IC, int ISC>
+static void launch_mode(const DecodeArgs& a, size_t lds_bytes, hipStream_t s) {
+  const dim3 grid(a.p.nb), block(256);
+  if (a.p.T == 1) hipLaunchKernelGGL((decode_kernel<MODE, HC, IC, ISC, 1>), grid, block, lds_bytes, s, a);
+  else hipLaunchKernelGGL((decode_kernel<MODE, HC, IC, ISC, kDecMaxT>), grid, block, lds_bytes, s, a);
+}
+
 int launch_decode(const DecodeArgs& a, int mode, size_t lds_bytes, hipStream_t s) {
   const bool real = decode_real_widths(a.p.H, a.p.I, a.p.Is);
-  const dim3 grid(a.p.nb), block(256);
   if (mode == DEC_FORWARD) {
-    if (real) hipLaunchKernelGGL((decode_kernel<DEC_FORWARD, 2048, 512, 512>), grid, block, lds_bytes, s, a);
-    else hipLaunchKernelGGL((decode_kernel<DEC_FORWARD, 0, 0, 0>), grid, block, lds_bytes, s, a);
+    if (real) launch_mode<DEC_FORWARD, 2048, 512, 512>(a, lds_bytes, s);
+    else launch_mode<DEC_FORWARD, 0, 0, 0>(a, lds_bytes, s);
   } else if (mode == DEC_BLOCK) {
-    if (real) hipLaunchKernelGGL((decode_kernel<DEC_BLOCK, 2048, 512, 512>), grid, block, lds_bytes, s, a);
-    else hipLaunchKernelGGL((decode_kernel<DEC_BLOCK, 0, 0, 0>), grid, block, lds_bytes, s, a);
+    if (real) launch_mode<DEC_BLOCK, 2048, 512, 512>(a, lds_bytes, s);
+    else launch_mode<DEC_BLOCK, 0, 0, 0>(a, lds_bytes, s);
   } else {
-    if (real) hipLaunchKernelGGL((decode_kernel<DEC_EXPERTS, 2048, 512, 512>), grid, block, lds_bytes, s, a);
-    else hipLaunchKernelGGL((decode_kernel<DEC_EXPERTS, 0, 0, 0>), grid, block, lds_bytes, s, a);
+    if (real) launch_mode<DEC_EXPERTS, 2048, 512, 512>(a, lds_bytes, s);
+    else launch_mode<DEC_EXPERTS, 0, 0, 0>(a, lds_bytes, s);
   }
   return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_LAUNCH;
 }
