@@ -97,6 +97,13 @@ extern "C" {
  * same time.  The call then writes NaN to out (see the few-token path's
  * failure contract below) and the workspace stays usable. */
 #define MOE_DEBUG_WAIT_GIVE_UP 0x100u
+/* dims.flags bit: the routed experts are affine int4 (the form of a 4-bit
+ * affine checkpoint such as the one the TensorFold PR runs, "Receipts"):
+ * codes are UNSIGNED nibbles q in [0, 15] (same packing: element 2j in the
+ * low nibble of byte j) and each group of 64 along K has a binary16 scale s
+ * (w13_s, w2_s) and a binary16 offset b (w13_b, w2_b):  w = q * s + b.
+ * The router and the shared expert keep their symmetric int8 form. */
+#define MOE_FMT_AFFINE4 0x200u
 
 typedef struct {
   int32_t hidden;       /* H */
@@ -105,7 +112,7 @@ typedef struct {
   int32_t expert_inter; /* I: routed-expert intermediate width */
   int32_t shared_inter; /* Is: shared-expert intermediate width */
   int32_t group;        /* G: quantisation group along K, must be 64 */
-  uint32_t flags;       /* MOE_PATH_*, optionally | MOE_DEBUG_WAIT_GIVE_UP */
+  uint32_t flags;       /* MOE_PATH_*, optionally | MOE_FMT_AFFINE4 | MOE_DEBUG_WAIT_GIVE_UP */
 } moe_dims;
 
 typedef struct {
@@ -119,6 +126,8 @@ typedef struct {
   const uint16_t* sh13_s;   /* [2Is][H/G] */
   const int8_t* sh2_q;      /* [H][Is] int8 */
   const uint16_t* sh2_s;    /* [H][Is/G] */
+  const uint16_t* w13_b;    /* MOE_FMT_AFFINE4 only: [E][2I][H/G] binary16 offsets (else NULL, not read) */
+  const uint16_t* w2_b;     /* MOE_FMT_AFFINE4 only: [E][H][I/G] binary16 offsets (else NULL, not read) */
 } moe_weights;
 
 /* Bytes of workspace a call with these dims and T tokens needs (any entry

@@ -55,6 +55,16 @@ def unpack_int4(packed: np.ndarray) -> np.ndarray:
     return out
 
 
+def unpack_uint4(packed: np.ndarray) -> np.ndarray:
+    """Bytes [..., K/2] -> unsigned 4-bit codes [..., K] in [0, 15] (the affine
+    int4 form): element 2j is the low nibble of byte j, element 2j+1 the high."""
+    b = np.asarray(packed, dtype=np.uint8).astype(np.int16)
+    out = np.empty(b.shape[:-1] + (2 * b.shape[-1],), dtype=np.int16)
+    out[..., 0::2] = b % 16
+    out[..., 1::2] = b // 16
+    return out
+
+
 def half_bits_to_f64(bits: np.ndarray) -> np.ndarray:
     """binary16 bit patterns -> float64 (exact)."""
     return np.asarray(bits, dtype=np.uint16).view(np.float16).astype(np.float64)
@@ -67,6 +77,20 @@ def dequant(codes: np.ndarray, scale_bits: np.ndarray, G: int) -> np.ndarray:
     if q.shape[-1] != s.shape[-1] * G:
         raise ValueError("scale count does not match K / G")
     return q * np.repeat(s, G, axis=-1)
+
+
+def dequant_affine(codes: np.ndarray, scale_bits: np.ndarray, offset_bits: np.ndarray, G: int) -> np.ndarray:
+    """Affine 4-bit dequantisation, per run of G consecutive elements of a row:
+    w = q * s + b with an unsigned code q, the group's scale s and offset b.
+    (The TensorFold PR runs a 4-bit affine checkpoint; the pages give no layout,
+    so this reading keeps the symmetric form's layout and adds one binary16
+    offset per group.)  Exact in float64."""
+    q = np.asarray(codes).astype(np.float64)
+    s = half_bits_to_f64(scale_bits)
+    b = half_bits_to_f64(offset_bits)
+    if q.shape[-1] != s.shape[-1] * G or s.shape != b.shape:
+        raise ValueError("scale or offset count does not match K / G")
+    return q * np.repeat(s, G, axis=-1) + np.repeat(b, G, axis=-1)
 
 
 # ---------------------------------------------------------------------------
@@ -142,7 +166,13 @@ def route(x_bits, W, dims):
 
 
 def routed_expert_weights(W, dims, e: int):
-    """Dequantised (W13_e [2I][H], W2_e [H][I]) of routed expert e."""
+    """Dequantised (W13_e [2I][H], W2_e [H][I]) of routed expert e: symmetric
+    int4 (code x scale), or affine int4 (code x scale + offset) when the
+    weights carry offsets."""
+    if getattr(W, "w13_b", None) is not None:
+        w13 = dequant_affine(unpack_uint4(W.w13_q[e]), W.w13_s[e], W.w13_b[e], dims.G)
+        w2 = dequant_affine(unpack_uint4(W.w2_q[e]), W.w2_s[e], W.w2_b[e], dims.G)
+        return w13, w2
     w13 = dequant(unpack_int4(W.w13_q[e]), W.w13_s[e], dims.G)
     w2 = dequant(unpack_int4(W.w2_q[e]), W.w2_s[e], dims.G)
     return w13, w2

@@ -87,7 +87,7 @@ def test_refusals_forward(L):
     assert _forward(L, _dims(E=4, k=8), W) == -2
     assert _forward(L, _dims(I=96), W) == -2
     assert _forward(L, _dims(flags=7), W) == -2
-    assert _forward(L, _dims(flags=0x200), W) == -2                 # an unknown flag bit
+    assert _forward(L, _dims(flags=0x400), W) == -2                 # an unknown flag bit
     assert _forward(L, _dims(flags=0x103), W) == -2                 # an unknown path with the debug bit
     assert _forward(L, d, W, T=-1) == -2
     assert _forward(L, _dims(flags=m.PATH_DECODE), W, T=5) == -2  # few-token path holds at most 4 tokens
@@ -96,6 +96,18 @@ def test_refusals_forward(L):
     assert _forward(L, d, W, ws=FAKE + 128) == -3
     need = m.moe_workspace_bytes(d, 7)
     assert _forward(L, d, W, T=7, ws_bytes=need - 1) == -4
+
+
+def test_refusals_affine(L):
+    aff = m.FMT_AFFINE4
+    W = _weights()
+    assert _forward(L, _dims(flags=aff), _weights(w13_b=None)) == -1  # offsets required with the flag
+    assert _forward(L, _dims(flags=aff), _weights(w2_b=None)) == -1
+    assert _forward(L, _dims(flags=aff), _weights(w2_b=FAKE + 4096 * 11 + 2)) == -3
+    assert _forward(L, _dims(flags=aff | m.PATH_DECODE), W, T=5) == -2
+    r = L.moe_experts_w4a16(ctypes.byref(_dims(flags=aff)), ctypes.byref(_weights(w13_b=None)), FAKE, 1, FAKE, FAKE,
+                            FAKE, FAKE, 1 << 30, None)
+    assert r == -1
 
 
 def test_refusals_route_and_experts(L):

@@ -101,6 +101,14 @@ def test_block_matches_transformers_skewed_router():
     _compare(case)
 
 
+def test_affine_block_matches_transformers():
+    """The affine int4 experts (w = q s + b), dequantised by the oracle and
+    loaded into transformers' block, agree with the oracle's forward."""
+    case = gen.make_affine_case(gen.TOY, 16, seed=7103)
+    assert case.weights.affine
+    _compare(case)
+
+
 @pytest.mark.parametrize("H", [256, 2048])
 def test_rmsnorm_matches_transformers(H):
     """Qwen3_5MoeRMSNorm multiplies by (1 + w) in float32 and rounds once to

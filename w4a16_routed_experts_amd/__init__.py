@@ -13,6 +13,7 @@ from .binding import (  # noqa: F401
     PATH_DECODE,
     PATH_CHUNK,
     DEBUG_WAIT_GIVE_UP,
+    FMT_AFFINE4,
     GIVE_UP_WORD_OFFSET,
     lib,
     library_path,

@@ -23,7 +23,8 @@ _STATUS = {0: "MOE_OK", -1: "MOE_ERR_NULL", -2: "MOE_ERR_SHAPE", -3: "MOE_ERR_AL
 NOALLOC_SCRATCH_BYTES = 8 << 20
 
 WEIGHT_FIELDS = ("router_q", "router_s", "w13_q", "w13_s", "w2_q", "w2_s",
-                 "sh13_q", "sh13_s", "sh2_q", "sh2_s")
+                 "sh13_q", "sh13_s", "sh2_q", "sh2_s", "w13_b", "w2_b")
+FMT_AFFINE4 = 0x200  # dims.flags: affine int4 routed experts (unsigned codes, per-group scale and offset)
 
 
 class MoeDims(ctypes.Structure):
@@ -173,8 +174,9 @@ class DeviceWeights:
         if tensors is None:
             tensors = {}
             for f in WEIGHT_FIELDS:
-                a = getattr(host_weights, f)
-                tensors[f] = torch.from_numpy(a.view(_TORCH_VIEW[a.dtype.str])).to(device)
+                a = getattr(host_weights, f, None)
+                if a is not None:
+                    tensors[f] = torch.from_numpy(a.view(_TORCH_VIEW[a.dtype.str])).to(device)
         self.tensors = tensors
         self.struct = MoeWeights(*[tensors[f].data_ptr() if tensors.get(f) is not None else None
                                    for f in WEIGHT_FIELDS])

@@ -43,7 +43,9 @@ int check_dims(const moe_dims* d, int32_t T) {
   if (d->num_experts < 1 || d->num_experts > kMaxExperts) return MOE_ERR_SHAPE;
   if (d->top_k < 1 || d->top_k > kMaxTopK || d->top_k > d->num_experts) return MOE_ERR_SHAPE;
   if (!width_ok(d->hidden) || !width_ok(d->expert_inter) || !width_ok(d->shared_inter)) return MOE_ERR_SHAPE;
-  if ((d->flags & kPathMask) > MOE_PATH_CHUNK || (d->flags & ~(kPathMask | MOE_DEBUG_WAIT_GIVE_UP))) return MOE_ERR_SHAPE;
+  if ((d->flags & kPathMask) > MOE_PATH_CHUNK ||
+      (d->flags & ~(kPathMask | MOE_DEBUG_WAIT_GIVE_UP | MOE_FMT_AFFINE4)))
+    return MOE_ERR_SHAPE;
   if (T < 0 || T > kMaxT) return MOE_ERR_SHAPE;
   return MOE_OK;
 }
@@ -139,7 +141,8 @@ struct DeviceInfo {
   bool ok = false;
   int cus = 0;
   void* scratch = nullptr;  // this device's address of the static scratch array
-  int occ[kDecModes][2][17] = {};  // blocks per CU by mode, width specialisation and LDS (4 KiB steps)
+  int occ[kDecModes][2][kDecVariants][17] = {};  // blocks per CU by mode, width specialisation, instance
+                                                 // and LDS (4 KiB steps)
 };
 
 std::mutex g_dev_mu;
@@ -158,7 +161,8 @@ int device_info(DeviceInfo** out) {
       di.cus = prop.multiProcessorCount;
       for (int m = 0; m < kDecModes; ++m)
         for (int r = 0; r < 2; ++r)
-          for (int s = 0; s <= 16; ++s) di.occ[m][r][s] = decode_blocks_per_cu(m, r == 1, (size_t)s * 4096);
+          for (int v = 0; v < kDecVariants; ++v)
+            for (int s = 0; s <= 16; ++s) di.occ[m][r][v][s] = decode_blocks_per_cu(m, r == 1, v, (size_t)s * 4096);
     }
   }
   if (!di.ok) return MOE_ERR_DEVICE;
@@ -208,12 +212,14 @@ int run_decode(const moe_dims* d, const moe_weights* w, const uint16_t* x, int T
   a.ids_out = ids_out; a.w_out = w_out; a.sigma_out = sig_out;
   a.ids_in = ids_in; a.w_in = w_in;
   a.give_up = (d->flags & MOE_DEBUG_WAIT_GIVE_UP) ? 1 : 0;
+  a.affine = (d->flags & MOE_FMT_AFFINE4) ? 1 : 0;
+  a.w13_b = w->w13_b; a.w2_b = w->w2_b;
   Carve c{static_cast<char*>(ws)};
   DecodeWs dw = carve_decode(d, T, c);
   a.sync = dw.sync; a.tagged = dw.tagged;
   const size_t lds = decode_lds_bytes(plan_of(d, T));
   const bool real = decode_real_widths(d->hidden, d->expert_inter, d->shared_inter);
-  const int per_cu = di->occ[mode][real ? 1 : 0][(lds + 4095) / 4096];
+  const int per_cu = di->occ[mode][real ? 1 : 0][decode_variant(T, a.affine != 0)][(lds + 4095) / 4096];
   // Every workgroup must be resident at once (they wait for each other, with
   // bounded waits): the grid is what an idle device holds, in whole groups of
   // 8, at most 8 x kMaxGroupWgs; a group needs at least H / 64 members (its
@@ -230,6 +236,8 @@ ChunkArgs chunk_args(const moe_dims* d, const moe_weights* w, const uint16_t* x,
   fill_weights(w, &a.router_q, &a.router_s, &a.w13_q, &a.w13_s, &a.w2_q, &a.w2_s, &a.sh13_q, &a.sh13_s, &a.sh2_q,
                &a.sh2_s);
   a.x = x; a.xa = x; a.out = out;
+  a.affine = (d->flags & MOE_FMT_AFFINE4) ? 1 : 0;
+  a.w13_b = w->w13_b; a.w2_b = w->w2_b;
   Carve c{static_cast<char*>(ws)};
   carve_chunk(d, T, c, a);
   a.max_route_tiles = max_route_tiles(d, T);
@@ -244,6 +252,14 @@ int check_common(const moe_dims* d, const void* x, int32_t T, void* ws, size_t w
   if (!aligned(x, 16) || !aligned(ws, 256)) return MOE_ERR_ALIGN;
   if (ws_bytes < workspace_bytes(d, T)) return MOE_ERR_WORKSPACE;
   if ((d->flags & kPathMask) == MOE_PATH_DECODE && !decode_admissible(d, T)) return MOE_ERR_SHAPE;
+  return MOE_OK;
+}
+
+// MOE_FMT_AFFINE4: the routed experts' offset arrays are required and aligned
+int check_affine(const moe_dims* d, const moe_weights* w) {
+  if (!(d->flags & MOE_FMT_AFFINE4)) return MOE_OK;
+  if (!w->w13_b || !w->w2_b) return MOE_ERR_NULL;
+  if (!aligned(w->w13_b, 16) || !aligned(w->w2_b, 16)) return MOE_ERR_ALIGN;
   return MOE_OK;
 }
 
@@ -318,6 +334,7 @@ MOE_API int moe_experts_w4a16(const moe_dims* dims, const moe_weights* w, const 
   if (!w) return MOE_ERR_NULL;
   if (any_null({w->w13_q, w->w13_s, w->w2_q, w->w2_s, ids, weights, out})) return MOE_ERR_NULL;
   if (!all16({w->w13_q, w->w13_s, w->w2_q, w->w2_s, out}) || !all4({ids, weights})) return MOE_ERR_ALIGN;
+  if ((st = check_affine(dims, w)) != MOE_OK) return st;
   if (use_decode(dims, T))
     return run_decode(dims, w, x, T, out, DEC_EXPERTS, nullptr, nullptr, nullptr, ids, weights, ws, stream);
   DeviceInfo* di = nullptr;
@@ -372,7 +389,7 @@ int validate_forward(const moe_dims* dims, const moe_weights* w, const uint16_t*
               w->sh2_s, out}) ||
       !all4({ids, weights, shared_gate}))
     return MOE_ERR_ALIGN;
-  return MOE_OK;
+  return check_affine(dims, w);
 }
 
 // the complete block on validated arguments
@@ -409,6 +426,7 @@ MOE_API int moe_block_forward(const moe_dims* dims, const moe_weights* w, const 
               w->sh2_s, out, gain}) ||
       !all4({ids, weights, shared_gate}))
     return MOE_ERR_ALIGN;
+  if ((st = check_affine(dims, w)) != MOE_OK) return st;
   if (!(eps >= 0.f && eps <= 3.0e38f)) return MOE_ERR_SHAPE;  // also refuses NaN and infinity
   {
     const uintptr_t hb = reinterpret_cast<uintptr_t>(h), ob = reinterpret_cast<uintptr_t>(out);

@@ -581,7 +581,7 @@ struct AStage {
   }
 };
 
-template <int BITS, int NF>
+template <int BITS, int NF, bool AFF = false>
 struct BStage {
   static constexpr int Q = BITS == 4 ? 1 : 2;  // 16-byte loads per lane per group
   u32x4 q[2][NF][Q];
@@ -599,15 +599,24 @@ struct BStage {
           q[gi][f][j] = __builtin_amdgcn_raw_buffer_load_b128(rq, qoff[f] + qk + (uint32_t)(kGroup * gi * BITS / 8 + 16 * j), 0, 0);
   }
   // MFMA operand for step st of group gi, fragment f; sw holds the binary16
-  // scales of the stage's two groups (group gi in half gi)
-  __device__ __forceinline__ h8 operand(int gi, int f, int st, uint32_t sw) const {
+  // scales of the stage's two groups (group gi in half gi), ow their offsets
+  // (AFF: unsigned codes, w = q s + b)
+  __device__ __forceinline__ h8 operand(int gi, int f, int st, uint32_t sw, uint32_t ow) const {
     h2 w[4];
+    const uint32_t sel = gi ? 0x07060706u : 0x05040504u;
+    const h2 sc = as_h2(__builtin_amdgcn_perm(sw, sw, sel));
+    if (AFF) {
+      uint4x8_to_h2x4(q[gi][f][0][st], w);
+      const h2 bo = as_h2(__builtin_amdgcn_perm(ow, ow, sel));
+#pragma unroll
+      for (int i = 0; i < 4; ++i) w[i] = __builtin_elementwise_fma(w[i], sc, bo);
+      return pack8(w);
+    }
     if (BITS == 4) {
       int4x8_to_h2x4(q[gi][f][0][st], w);
     } else {
       int8x8_to_h2x4(q[gi][f][st >> 1][2 * (st & 1)], q[gi][f][st >> 1][2 * (st & 1) + 1], w);
     }
-    const h2 sc = as_h2(__builtin_amdgcn_perm(sw, sw, gi ? 0x07060706u : 0x05040504u));
 #pragma unroll
     for (int i = 0; i < 4; ++i) w[i] *= sc;
     return pack8(w);
@@ -649,17 +658,18 @@ struct ScaleBlock {
 };
 
 // Operands of one tile: A rows through `ra` at byte offsets aoff (one per
-// 16-byte chunk this thread stages), weight fragments through rq/rs.
+// 16-byte chunk this thread stages), weight fragments through rq/rs (and the
+// offsets of affine weights through rb, laid out like the scales).
 template <int BITS, int NF, int MT>
 struct GemmOperands {
-  __amdgpu_buffer_rsrc_t ra, rq, rs;
+  __amdgpu_buffer_rsrc_t ra, rq, rs, rb;
   uint32_t aoff[AStage<MT>::N];
   uint32_t qoff[NF], soff[NF];
 };
 
-template <int BITS, int NF, int MT>
-__device__ __forceinline__ void stage_mfma(const _Float16* L, const BStage<BITS, NF>& b, const uint32_t sw[NF], int kb,
-                                           int K, f16v acc[MT][NF]) {
+template <int BITS, int NF, int MT, bool AFF>
+__device__ __forceinline__ void stage_mfma(const _Float16* L, const BStage<BITS, NF, AFF>& b, const uint32_t sw[NF],
+                                           const uint32_t ow[NF], int kb, int K, f16v acc[MT][NF]) {
   const int lane = threadIdx.x & 63;
   const int m = lane & 31, g = lane >> 5;
 #pragma unroll
@@ -673,7 +683,7 @@ __device__ __forceinline__ void stage_mfma(const _Float16* L, const BStage<BITS,
           av[mt] = *reinterpret_cast<const h8*>(L + (32 * mt + m) * kAStride + kGroup * gi + 32 * g + 8 * s);
 #pragma unroll
         for (int f = 0; f < NF; ++f) {
-          const h8 bv = b.operand(gi, f, s, sw[f]);
+          const h8 bv = b.operand(gi, f, s, sw[f], ow[f]);
 #pragma unroll
           for (int mt = 0; mt < MT; ++mt)
             acc[mt][f] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av[mt], bv, acc[mt][f], 0, 0, 0);
@@ -683,7 +693,7 @@ __device__ __forceinline__ void stage_mfma(const _Float16* L, const BStage<BITS,
   }
 }
 
-template <int BITS, int NF, int MT>
+template <int BITS, int NF, int MT, bool AFF = false>
 __device__ __forceinline__ void tile_gemm(_Float16* lds, const GemmOperands<BITS, NF, MT>& op, int K,
                                           f16v acc[MT][NF]) {
   constexpr int BUF = 32 * MT * kAStride;
@@ -691,12 +701,13 @@ __device__ __forceinline__ void tile_gemm(_Float16* lds, const GemmOperands<BITS
   static_assert(PF >= 1 && PF <= 3, "the stage ring holds four stages");
   const int nst = (K + kKS - 1) / kKS;
   AStage<MT> as;
-  BStage<BITS, NF> b[4];
-  ScaleBlock<NF> sc, scn;
+  BStage<BITS, NF, AFF> b[4];
+  ScaleBlock<NF> sc, scn, oc, ocn;  // scales, offsets (AFF)
   as.load(op.ra, op.aoff, 0);
 #pragma unroll
   for (int i = 0; i < PF; ++i) b[i].load(op.rq, op.qoff, i * kKS, i < nst);
   sc.load_first(op.rs, op.soff, K / kGroup);
+  if (AFF) oc.load_first(op.rb, op.soff, K / kGroup);
   as.store(lds);
   __syncthreads();
   // Four stages per iteration: stage s multiplies ring slot s % 4 and loads
@@ -712,11 +723,15 @@ __device__ __forceinline__ void tile_gemm(_Float16* lds, const GemmOperands<BITS
     as.load(op.ra, op.aoff, more ? 2u * (kb + kKS) : kOob);                    \
     b[(J + PF) & 3].load(op.rq, op.qoff, kb + PF * kKS, st + J + PF < nst);   \
     if (J == 3) scn.load(op.rs, op.soff, st / 4 + 1, st + 4 < nst);            \
+    if (AFF && J == 3) ocn.load(op.rb, op.soff, st / 4 + 1, st + 4 < nst);     \
     /* keep the next stage's loads ahead of this stage's arithmetic */         \
     __builtin_amdgcn_sched_barrier(0);                                         \
-    uint32_t sw[NF];                                                           \
-    _Pragma("unroll") for (int f = 0; f < NF; ++f) sw[f] = sc.v[f][J];         \
-    stage_mfma<BITS, NF, MT>(LC, b[J], sw, kb, K, acc);                        \
+    uint32_t sw[NF], ow[NF];                                                   \
+    _Pragma("unroll") for (int f = 0; f < NF; ++f) {                           \
+      sw[f] = sc.v[f][J];                                                      \
+      ow[f] = AFF ? oc.v[f][J] : 0u;                                           \
+    }                                                                          \
+    stage_mfma<BITS, NF, MT, AFF>(LC, b[J], sw, ow, kb, K, acc);               \
     as.store(LN);                                                              \
     __syncthreads();                                                           \
     if (!more) break;                                                          \
@@ -727,6 +742,7 @@ __device__ __forceinline__ void tile_gemm(_Float16* lds, const GemmOperands<BITS
     MOE_TILE_STAGE(2, lds, lds + BUF)
     MOE_TILE_STAGE(3, lds + BUF, lds)
     sc = scn;
+    if (AFF) oc = ocn;
   }
 #undef MOE_TILE_STAGE
 }
@@ -826,18 +842,20 @@ __device__ __forceinline__ void narrow_prologue(_Float16* lds, __amdgpu_buffer_r
   a.store(lds);
 }
 
-// acc[f] += A[16][K] . W_f[16][K]^T for the wave's NF weight fragments
-template <int NF>
+// acc[f] += A[16][K] . W_f[16][K]^T for the wave's NF weight fragments (AFF:
+// unsigned codes and offsets through rb, laid out like the scales)
+template <int NF, bool AFF = false>
 __device__ __forceinline__ void narrow_gemm(_Float16* lds, __amdgpu_buffer_rsrc_t ra, const uint32_t* aoff, int K,
                                             __amdgpu_buffer_rsrc_t rq, __amdgpu_buffer_rsrc_t rs,
-                                            const uint32_t qoff[NF], const uint32_t soff[NF], f4 acc[NF]) {
+                                            __amdgpu_buffer_rsrc_t rb, const uint32_t qoff[NF],
+                                            const uint32_t soff[NF], f4 acc[NF]) {
   static_assert(kNarrowPF >= 1 && kNarrowPF <= 3, "the stage ring holds four stages");
   const int lane = threadIdx.x & 63, n = lane & 15, q = lane >> 4;
   const uint32_t ssel = (q & 2) ? 0x07060706u : 0x05040504u;  // the lane's group in the stage: half q/2 of a scale word
   const int src_byte = 4 * (4 * n + q);                          // coalesced lane holding this lane's weights
   const int nst = (K + kKS - 1) / kKS;
   NarrowB<NF> b[4];
-  ScaleBlock<NF> sc, scn;
+  ScaleBlock<NF> sc, scn, oc, ocn;
   // K is a multiple of 512 here, so the K loop runs whole iterations of four
   // stages with no exit inside one: every path into the loop head has issued
   // the same loads, and the compiler's wait counts keep kNarrowPF stages in
@@ -847,6 +865,7 @@ __device__ __forceinline__ void narrow_gemm(_Float16* lds, __amdgpu_buffer_rsrc_
     case 8: narrow_prologue<8, NF>(lds, ra, aoff, K, rq, rs, qoff, soff, b, sc, nst); break;
     default: narrow_prologue<16, NF>(lds, ra, aoff, K, rq, rs, qoff, soff, b, sc, nst); break;
   }
+  if (AFF) oc.load(rb, soff, 0, true);
   __syncthreads();
   const _Float16* La = lds + n * kNarrowStride + 32 * q;
   // Four stages per iteration (one scale block): stage s computes from ring
@@ -856,19 +875,27 @@ __device__ __forceinline__ void narrow_gemm(_Float16* lds, __amdgpu_buffer_rsrc_
     const int s_ = st + J;                                                                 \
     b[(J + kNarrowPF) & 3].load(rq, qoff, s_ + kNarrowPF, s_ + kNarrowPF < nst);           \
     if (J == 0) scn.load(rs, soff, st / 4 + 1, st + 4 < nst);                              \
+    if (AFF && J == 0) ocn.load(rb, soff, st / 4 + 1, st + 4 < nst);                       \
     __builtin_amdgcn_sched_barrier(0);                                                     \
-    h2 scl[NF];                                                                            \
+    h2 scl[NF], ofl[NF];                                                                   \
     u32x4 bw[NF];                                                                          \
     _Pragma("unroll") for (int f = 0; f < NF; ++f) {                                       \
       scl[f] = as_h2(__builtin_amdgcn_perm(sc.v[f][J], sc.v[f][J], ssel));                 \
+      ofl[f] = AFF ? as_h2(__builtin_amdgcn_perm(oc.v[f][J], oc.v[f][J], ssel)) : scl[f]; \
       bw[f] = to_mfma_lanes(b[J].q[f], src_byte);                                          \
     }                                                                                      \
     _Pragma("unroll") for (int t = 0; t < 4; ++t) {                                        \
       const h8 av = *reinterpret_cast<const h8*>(La + kKS * s_ + 8 * t);                  \
       _Pragma("unroll") for (int f = 0; f < NF; ++f) {                                     \
         h2 w[4];                                                                           \
-        int4x8_to_h2x4(bw[f][t], w);                                                       \
-        _Pragma("unroll") for (int i = 0; i < 4; ++i) w[i] *= scl[f];                      \
+        if (AFF) {                                                                         \
+          uint4x8_to_h2x4(bw[f][t], w);                                                    \
+          _Pragma("unroll") for (int i = 0; i < 4; ++i)                                    \
+            w[i] = __builtin_elementwise_fma(w[i], scl[f], ofl[f]);                        \
+        } else {                                                                           \
+          int4x8_to_h2x4(bw[f][t], w);                                                     \
+          _Pragma("unroll") for (int i = 0; i < 4; ++i) w[i] *= scl[f];                    \
+        }                                                                                  \
         acc[f] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, pack8(w), acc[f], 0, 0, 0);    \
       }                                                                                    \
     }                                                                                      \
@@ -879,6 +906,7 @@ __device__ __forceinline__ void narrow_gemm(_Float16* lds, __amdgpu_buffer_rsrc_
     MOE_NARROW_STAGE(2)
     MOE_NARROW_STAGE(3)
     sc = scn;
+    if (AFF) oc = ocn;
   }
 #undef MOE_NARROW_STAGE
 }
@@ -924,10 +952,10 @@ __device__ __forceinline__ void item_of(int r, int nb, int& tile, int& cb) {
 // 4. gate/up GEMM with SwiGLU epilogue.  Items: (column block of 128, tile),
 //    column-block major; routed tiles first, then shared-expert tiles.
 // ---------------------------------------------------------------------------
-template <int BITS, int MT>
+template <int BITS, int MT, bool AFF = false>
 __device__ __forceinline__ void up_tile(const ChunkArgs& a, _Float16* lds, const TileRows& tr,
-                                        __amdgpu_buffer_rsrc_t ra, const uint8_t* wq, const uint16_t* wsc, int inter,
-                                        int jb, _Float16* hout, int rows) {
+                                        __amdgpu_buffer_rsrc_t ra, const uint8_t* wq, const uint16_t* wsc,
+                                        const uint16_t* wof, int inter, int jb, _Float16* hout, int rows) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int j = jb * 128 + wave * 32 + (lane & 31);
   const uint32_t rb = (uint32_t)a.H * BITS / 8;
@@ -937,6 +965,7 @@ __device__ __forceinline__ void up_tile(const ChunkArgs& a, _Float16* lds, const
   op.ra = ra;
   op.rq = make_rsrc(wq, 2u * inter * rb);
   op.rs = make_rsrc(wsc, 2u * inter * ng * 2u);
+  if (AFF) op.rb = make_rsrc(wof, 2u * inter * ng * 2u);
   const uint32_t kl = 32u * (lane >> 5) * BITS / 8;  // the lane's K slice inside a group
   op.qoff[0] = ok ? (uint32_t)j * rb + kl : kOob;
   op.qoff[1] = ok ? (uint32_t)(inter + j) * rb + kl : kOob;
@@ -946,7 +975,7 @@ __device__ __forceinline__ void up_tile(const ChunkArgs& a, _Float16* lds, const
   f16v acc[MT][2];
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) acc[mt][0] = acc[mt][1] = f16v{};
-  tile_gemm<BITS, 2, MT>(lds, op, a.H, acc);  // ends with a workgroup barrier: the LDS is free
+  tile_gemm<BITS, 2, MT, AFF>(lds, op, a.H, acc);  // ends with a workgroup barrier: the LDS is free
   // The wave's h tile goes through LDS (row-major, 32 halves a row) so that
   // the stores are whole 16-byte pieces of rows, not one 2-byte value a lane.
   _Float16* ht = lds + wave * (32 * MT) * 32;
@@ -965,14 +994,16 @@ __device__ __forceinline__ void up_tile(const ChunkArgs& a, _Float16* lds, const
 
 // a narrow routed tile: each wave takes 32 gate and the same 32 up columns as
 // four 16-column fragments (gate j0.., gate j0+16.., up j0.., up j0+16..)
+template <bool AFF>
 __device__ __forceinline__ void up_narrow(const ChunkArgs& a, _Float16* lds, const TileRows& tr,
-                                          __amdgpu_buffer_rsrc_t ra, const uint8_t* wq, const uint16_t* wsc, int inter,
-                                          int jb, _Float16* hout, int rows) {
+                                          __amdgpu_buffer_rsrc_t ra, const uint8_t* wq, const uint16_t* wsc,
+                                          const uint16_t* wof, int inter, int jb, _Float16* hout, int rows) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, n = lane & 15, q = lane >> 4;
   const uint32_t rb = (uint32_t)a.H / 2;
   const uint32_t ng = a.H / kGroup;
   const __amdgpu_buffer_rsrc_t rq = make_rsrc(wq, 2u * inter * rb);
   const __amdgpu_buffer_rsrc_t rs = make_rsrc(wsc, 2u * inter * ng * 2u);
+  const __amdgpu_buffer_rsrc_t ro = AFF ? make_rsrc(wof, 2u * inter * ng * 2u) : rs;
   const int j0 = jb * 128 + wave * 32;
   uint32_t qoff[4], soff[4];
 #pragma unroll
@@ -985,7 +1016,7 @@ __device__ __forceinline__ void up_narrow(const ChunkArgs& a, _Float16* lds, con
   f4 acc[4];
 #pragma unroll
   for (int f = 0; f < 4; ++f) acc[f] = f4{0.f, 0.f, 0.f, 0.f};
-  narrow_gemm<4>(lds, ra, tr.aoff, a.H, rq, rs, qoff, soff, acc);
+  narrow_gemm<4, AFF>(lds, ra, tr.aoff, a.H, rq, rs, ro, qoff, soff, acc);
   // h through LDS (16 rows of 32 halves per wave) for 16-byte row stores;
   // the barrier first: other waves may still read the tile's rows
   __syncthreads();
@@ -1001,6 +1032,7 @@ __device__ __forceinline__ void up_narrow(const ChunkArgs& a, _Float16* lds, con
         *reinterpret_cast<const uint4*>(ht + r * 32 + 8 * c);
 }
 
+template <bool AFF>
 __global__ __launch_bounds__(256, 2) void up_gemm_kernel(ChunkArgs a) {
   __shared__ __attribute__((aligned(16))) _Float16 lds[kGemmLds];
   __shared__ TileRows tr;
@@ -1031,23 +1063,25 @@ __global__ __launch_bounds__(256, 2) void up_gemm_kernel(ChunkArgs a) {
   const __amdgpu_buffer_rsrc_t ra = make_rsrc(a.xa, (uint32_t)a.T * a.H * 2u);
   if (e >= 0) {
     const uint8_t* wq = a.w13_q + (size_t)e * 2 * a.I * (a.H / 2);
-    const uint16_t* wsc = a.w13_s + (size_t)e * 2 * a.I * (a.H / kGroup);
+    const size_t so = (size_t)e * 2 * a.I * (a.H / kGroup);
+    const uint16_t* wsc = a.w13_s + so;
+    const uint16_t* wof = AFF ? a.w13_b + so : nullptr;
     switch (mt) {
-      case 4: up_tile<4, 4>(a, lds, tr, ra, wq, wsc, a.I, jb, a.h, rows); break;
-      case 3: up_tile<4, 3>(a, lds, tr, ra, wq, wsc, a.I, jb, a.h, rows); break;
-      case 2: up_tile<4, 2>(a, lds, tr, ra, wq, wsc, a.I, jb, a.h, rows); break;
+      case 4: up_tile<4, 4, AFF>(a, lds, tr, ra, wq, wsc, wof, a.I, jb, a.h, rows); break;
+      case 3: up_tile<4, 3, AFF>(a, lds, tr, ra, wq, wsc, wof, a.I, jb, a.h, rows); break;
+      case 2: up_tile<4, 2, AFF>(a, lds, tr, ra, wq, wsc, wof, a.I, jb, a.h, rows); break;
       case 0:
         if (a.H >= kNarrowMinK && a.H <= kNarrowK) {
-          up_narrow(a, lds, tr, ra, wq, wsc, a.I, jb, a.h, rows);
+          up_narrow<AFF>(a, lds, tr, ra, wq, wsc, wof, a.I, jb, a.h, rows);
           break;
         }
         [[fallthrough]];
-      default: up_tile<4, 1>(a, lds, tr, ra, wq, wsc, a.I, jb, a.h, rows); break;
+      default: up_tile<4, 1, AFF>(a, lds, tr, ra, wq, wsc, wof, a.I, jb, a.h, rows); break;
     }
   } else {
     const uint8_t* wq = reinterpret_cast<const uint8_t*>(a.sh13_q);
-    if (mt == 2) up_tile<8, 2>(a, lds, tr, ra, wq, a.sh13_s, a.Is, jb, a.hs, rows);
-    else up_tile<8, 1>(a, lds, tr, ra, wq, a.sh13_s, a.Is, jb, a.hs, rows);
+    if (mt == 2) up_tile<8, 2>(a, lds, tr, ra, wq, a.sh13_s, nullptr, a.Is, jb, a.hs, rows);
+    else up_tile<8, 1>(a, lds, tr, ra, wq, a.sh13_s, nullptr, a.Is, jb, a.hs, rows);
   }
 }
 
@@ -1067,10 +1101,11 @@ __device__ __forceinline__ void publish_rows(TileRows& tr, int my_row, float my_
   }
 }
 
-template <int BITS, int MT>
+template <int BITS, int MT, bool AFF = false>
 __device__ __forceinline__ void down_tile(const ChunkArgs& a, _Float16* lds, TileRows& tr,
-                                          __amdgpu_buffer_rsrc_t ra, const uint8_t* wq, const uint16_t* wsc, int K,
-                                          int nb, _Float16* yout, int rows, int my_row, float my_scale) {
+                                          __amdgpu_buffer_rsrc_t ra, const uint8_t* wq, const uint16_t* wsc,
+                                          const uint16_t* wof, int K, int nb, _Float16* yout, int rows, int my_row,
+                                          float my_scale) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const uint32_t rb = (uint32_t)K * BITS / 8;
   const uint32_t ng = K / kGroup;
@@ -1078,6 +1113,7 @@ __device__ __forceinline__ void down_tile(const ChunkArgs& a, _Float16* lds, Til
   op.ra = ra;
   op.rq = make_rsrc(wq, (uint32_t)a.H * rb);
   op.rs = make_rsrc(wsc, (uint32_t)a.H * ng * 2u);
+  if (AFF) op.rb = make_rsrc(wof, (uint32_t)a.H * ng * 2u);
   const uint32_t kl = 32u * (lane >> 5) * BITS / 8;
   int n[2];
 #pragma unroll
@@ -1091,7 +1127,7 @@ __device__ __forceinline__ void down_tile(const ChunkArgs& a, _Float16* lds, Til
   f16v acc[MT][2];
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) acc[mt][0] = acc[mt][1] = f16v{};
-  tile_gemm<BITS, 2, MT>(lds, op, K, acc);  // ends with a workgroup barrier: the LDS is free
+  tile_gemm<BITS, 2, MT, AFF>(lds, op, K, acc);  // ends with a workgroup barrier: the LDS is free
   publish_rows(tr, my_row, my_scale);
   __syncthreads();
   // the wave's 64 outputs of each row through LDS (row-major, 64 halves a
@@ -1116,14 +1152,17 @@ __device__ __forceinline__ void down_tile(const ChunkArgs& a, _Float16* lds, Til
 }
 
 // a narrow routed tile: each wave takes 64 outputs as four 16-column fragments
+template <bool AFF>
 __device__ __forceinline__ void down_narrow(const ChunkArgs& a, _Float16* lds, TileRows& tr,
-                                            __amdgpu_buffer_rsrc_t ra, const uint8_t* wq, const uint16_t* wsc, int K,
-                                            int nb, _Float16* yout, int rows, int my_row, float my_scale) {
+                                            __amdgpu_buffer_rsrc_t ra, const uint8_t* wq, const uint16_t* wsc,
+                                            const uint16_t* wof, int K, int nb, _Float16* yout, int rows, int my_row,
+                                            float my_scale) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, n = lane & 15, q = lane >> 4;
   const uint32_t rb = (uint32_t)K / 2;
   const uint32_t ng = K / kGroup;
   const __amdgpu_buffer_rsrc_t rq = make_rsrc(wq, (uint32_t)a.H * rb);
   const __amdgpu_buffer_rsrc_t rs = make_rsrc(wsc, (uint32_t)a.H * ng * 2u);
+  const __amdgpu_buffer_rsrc_t ro = AFF ? make_rsrc(wof, (uint32_t)a.H * ng * 2u) : rs;
   int col[4];
   uint32_t qoff[4], soff[4];
 #pragma unroll
@@ -1136,7 +1175,7 @@ __device__ __forceinline__ void down_narrow(const ChunkArgs& a, _Float16* lds, T
   f4 acc[4];
 #pragma unroll
   for (int f = 0; f < 4; ++f) acc[f] = f4{0.f, 0.f, 0.f, 0.f};
-  narrow_gemm<4>(lds, ra, tr.aoff, K, rq, rs, qoff, soff, acc);
+  narrow_gemm<4, AFF>(lds, ra, tr.aoff, K, rq, rs, ro, qoff, soff, acc);
   // outputs through LDS (16 rows of 64 halves per wave) for 16-byte row
   // stores; the barrier first: other waves may still read the tile's rows
   publish_rows(tr, my_row, my_scale);
@@ -1157,6 +1196,7 @@ __device__ __forceinline__ void down_narrow(const ChunkArgs& a, _Float16* lds, T
           *reinterpret_cast<const uint4*>(yt + r * 64 + 8 * c);
 }
 
+template <bool AFF>
 __global__ __launch_bounds__(256, 2) void down_gemm_kernel(ChunkArgs a) {
   __shared__ __attribute__((aligned(16))) _Float16 lds[kGemmLds];
   __shared__ TileRows tr;
@@ -1194,23 +1234,25 @@ __global__ __launch_bounds__(256, 2) void down_gemm_kernel(ChunkArgs a) {
   const __amdgpu_buffer_rsrc_t ra = make_rsrc(abase, (uint32_t)rows * K * 2u);
   if (e >= 0) {
     const uint8_t* wq = a.w2_q + (size_t)e * a.H * (a.I / 2);
-    const uint16_t* wsc = a.w2_s + (size_t)e * a.H * (a.I / kGroup);
+    const size_t so = (size_t)e * a.H * (a.I / kGroup);
+    const uint16_t* wsc = a.w2_s + so;
+    const uint16_t* wof = AFF ? a.w2_b + so : nullptr;
     switch (mt) {
-      case 4: down_tile<4, 4>(a, lds, tr, ra, wq, wsc, a.I, nb, a.y, rows, my_row, my_scale); break;
-      case 3: down_tile<4, 3>(a, lds, tr, ra, wq, wsc, a.I, nb, a.y, rows, my_row, my_scale); break;
-      case 2: down_tile<4, 2>(a, lds, tr, ra, wq, wsc, a.I, nb, a.y, rows, my_row, my_scale); break;
+      case 4: down_tile<4, 4, AFF>(a, lds, tr, ra, wq, wsc, wof, a.I, nb, a.y, rows, my_row, my_scale); break;
+      case 3: down_tile<4, 3, AFF>(a, lds, tr, ra, wq, wsc, wof, a.I, nb, a.y, rows, my_row, my_scale); break;
+      case 2: down_tile<4, 2, AFF>(a, lds, tr, ra, wq, wsc, wof, a.I, nb, a.y, rows, my_row, my_scale); break;
       case 0:
         if (a.I >= kNarrowMinK && a.I <= kNarrowK) {
-          down_narrow(a, lds, tr, ra, wq, wsc, a.I, nb, a.y, rows, my_row, my_scale);
+          down_narrow<AFF>(a, lds, tr, ra, wq, wsc, wof, a.I, nb, a.y, rows, my_row, my_scale);
           break;
         }
         [[fallthrough]];
-      default: down_tile<4, 1>(a, lds, tr, ra, wq, wsc, a.I, nb, a.y, rows, my_row, my_scale); break;
+      default: down_tile<4, 1, AFF>(a, lds, tr, ra, wq, wsc, wof, a.I, nb, a.y, rows, my_row, my_scale); break;
     }
   } else {
     const uint8_t* wq = reinterpret_cast<const uint8_t*>(a.sh2_q);
-    if (mt == 2) down_tile<8, 2>(a, lds, tr, ra, wq, a.sh2_s, a.Is, nb, a.ys, rows, my_row, my_scale);
-    else down_tile<8, 1>(a, lds, tr, ra, wq, a.sh2_s, a.Is, nb, a.ys, rows, my_row, my_scale);
+    if (mt == 2) down_tile<8, 2>(a, lds, tr, ra, wq, a.sh2_s, nullptr, a.Is, nb, a.ys, rows, my_row, my_scale);
+    else down_tile<8, 1>(a, lds, tr, ra, wq, a.sh2_s, nullptr, a.Is, nb, a.ys, rows, my_row, my_scale);
   }
 }
 
@@ -1284,8 +1326,13 @@ static void launch_gemms(const ChunkArgs& a, hipStream_t s) {
   const int max_tiles = (a.max_route_tiles + a.shared_tiles + 7) & ~7;
   const int up_items = max_tiles * max((a.I + 127) / 128, (a.Is + 127) / 128);
   const int down_items = max_tiles * ((a.H + 255) / 256);
-  hipLaunchKernelGGL(up_gemm_kernel, dim3((up_items + 7) & ~7), dim3(256), 0, s, a);
-  hipLaunchKernelGGL(down_gemm_kernel, dim3((down_items + 7) & ~7), dim3(256), 0, s, a);
+  if (a.affine) {
+    hipLaunchKernelGGL(up_gemm_kernel<true>, dim3((up_items + 7) & ~7), dim3(256), 0, s, a);
+    hipLaunchKernelGGL(down_gemm_kernel<true>, dim3((down_items + 7) & ~7), dim3(256), 0, s, a);
+  } else {
+    hipLaunchKernelGGL(up_gemm_kernel<false>, dim3((up_items + 7) & ~7), dim3(256), 0, s, a);
+    hipLaunchKernelGGL(down_gemm_kernel<false>, dim3((down_items + 7) & ~7), dim3(256), 0, s, a);
+  }
   hipLaunchKernelGGL(combine_kernel, dim3((a.H / 8 + 255) / 256 * a.T), dim3(256), 0, s, a);
 }
 

@@ -41,6 +41,8 @@ struct ChunkArgs {
   int max_route_tiles; // bound on routed tiles for the grid
   int cus;             // compute units of the device (work pairing in the GEMM kernels)
   uint32_t* route_done;  // counter of finished top-k workgroups (zero between calls)
+  int affine;            // routed experts are affine int4 (unsigned codes, w = q s + b)
+  const uint16_t* w13_b; const uint16_t* w2_b;  // affine: per-group binary16 offsets
 };
 
 int launch_route_chunk(const ChunkArgs& a, hipStream_t s);

@@ -53,6 +53,19 @@ __device__ __forceinline__ void int4x8_to_h2x4(uint32_t w, h2 out[4]) {
   out[3] = as_h2(flip_into(v, 0x00F000F0u, 0x54805480u)) - hi_bias;  // (k3, k7)
 }
 
+// one word = 8 UNSIGNED 4-bit codes (affine int4), same output order: each
+// field is ORed into the mantissa of 1024 (unit spacing) or 64 (spacing 1/16)
+// and the constant subtracted, which is exact
+__device__ __forceinline__ void uint4x8_to_h2x4(uint32_t w, h2 out[4]) {
+  const uint32_t v = w >> 8;
+  const h2 lo_c = as_h2(0x64006400u);  // 1024
+  const h2 hi_c = as_h2(0x54005400u);  // 64
+  out[0] = as_h2((w & 0x000F000Fu) | 0x64006400u) - lo_c;  // (k0, k4)
+  out[1] = as_h2((w & 0x00F000F0u) | 0x54005400u) - hi_c;  // (k1, k5)
+  out[2] = as_h2((v & 0x000F000Fu) | 0x64006400u) - lo_c;  // (k2, k6)
+  out[3] = as_h2((v & 0x00F000F0u) | 0x54005400u) - hi_c;  // (k3, k7)
+}
+
 // two words = 8 int8 codes (w0: k0..k3, w1: k4..k7), same output order
 __device__ __forceinline__ void int8x8_to_h2x4(uint32_t w0, uint32_t w1, h2 out[4]) {
   const uint32_t a = __builtin_amdgcn_perm(w1, w0, 0x05040100u);  // k0 k1 k4 k5

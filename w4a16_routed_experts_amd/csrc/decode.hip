@@ -62,6 +62,21 @@ __device__ __forceinline__ uint64_t get_tagged(const uint64_t* p) {
 __device__ __forceinline__ bool tag_ok(uint64_t w, uint32_t tag) { return (uint32_t)(w >> 32) == tag; }
 __device__ __forceinline__ float word_f(uint64_t w) { return __builtin_bit_cast(float, (uint32_t)w); }
 
+// dst[c] = sum of the 32 halves src[32 c .. 32 c + 31], c < n, in index order
+__device__ __forceinline__ void chunk_sums(float* dst, const _Float16* src, int n) {
+  for (int c = threadIdx.x; c < n; c += blockDim.x) {
+    const h8* v = reinterpret_cast<const h8*>(src) + 4 * (size_t)c;
+    float s = 0.f;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const h8 w = v[q];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) s += (float)w[i];
+    }
+    dst[c] = s;
+  }
+}
+
 // copy n halves (n multiple of 8) global -> LDS with 16-byte accesses
 __device__ __forceinline__ void copy_halves(_Float16* dst, const void* src, int n) {
   const uint4* s = reinterpret_cast<const uint4*>(src);
@@ -106,12 +121,13 @@ __device__ __forceinline__ bool wave_poll(const uint64_t* w, int n, uint32_t tag
 // ------------------------------------------------------------------ kernel
 
 // HC, IC, ISC: compile-time H, I, Is (0: taken from the plan); TT: most tokens
-// the instance handles (1, or kDecMaxT).  Every phase of a launch runs once, so
+// the instance handles (1, or kDecMaxT); AFF: the routed experts are affine
+// int4 (unsigned codes, w = q s + b per group of 64).  Every phase of a launch runs once, so
 // code is kept short: the per-token loops are unrolled for TT tokens only, and
 // the loops that cover more rows than one wave-load holds (small grids) exist
 // only in the generic instances.  CB: column batches of the gate/up rows in
 // flight per wave; DB: row batches of the down rows prefetched per wave.
-template <int MODE, int HC, int IC, int ISC, int TT>
+template <int MODE, int HC, int IC, int ISC, int TT, bool AFF>
 __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
   extern __shared__ uint4 smem_raw[];
   const DecodePlan& p = a.p;
@@ -132,6 +148,8 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
   _Float16* act = reinterpret_cast<_Float16*>(smem_raw);  // [T][H]
   _Float16* hq = act + (size_t)T * H;                     // [npg][I] the group's routed h
   _Float16* hs = hq + (size_t)p.npg * I;                  // [T][sw] the group's shared slice
+  float* xsum = reinterpret_cast<float*>(hs + (size_t)T * sw);  // AFF: [T][H/32] chunk sums of act
+  float* hsum = xsum + (size_t)T * (H / 32);                    // AFF: [npg][I/32] chunk sums of hq
   __shared__ int s_ids[kDecMaxT][kMaxTopK];
   __shared__ float s_w[kDecMaxT][kMaxTopK];
   __shared__ TopkScratch s_topk[kDecMaxT];
@@ -296,6 +314,8 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
     if (wave >= 2) fd_s.load(rows, srow, g8s, base);
   }
   for (int t = tid; t < kDecMaxT * kMaxGroupWgs; t += blockDim.x) (&s_part[0][0])[t] = 0.f;
+  // AFF: the offsets multiply the sum of each 32-activation chunk
+  if (AFF) chunk_sums(xsum, act, T * (H / 32));
 
   // ---------------- routing of the group's pairs
   if (MODE != DEC_EXPERTS) {
@@ -374,7 +394,7 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
   const size_t rb13 = (size_t)H / 2, ng13 = H / kGroup;
   const size_t rb2 = (size_t)I / 2, ng2 = I / kGroup;
   const int nrb = (p.rw + g4i.rpb - 1) / g4i.rpb;  // row batches of the down rows
-  Frag<4, DB, CPL4I> fd0;
+  Frag<4, DB, CPL4I, AFF> fd0;
   {  // (no branch: a branch here would make the compiler wait for these loads inside it)
     const int e = np > 0 && s_pe[0] >= 0 ? s_pe[0] : 0;
     const uint8_t* rows[DB];
@@ -389,6 +409,12 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
       srow[d] = a.w2_s + ((size_t)e * H + (ok ? n : 0)) * ng2;
     }
     fd0.load(rows, srow, g4i, a.w2_q);
+    if (AFF) {
+      const uint16_t* orow[DB];
+#pragma unroll
+      for (int d = 0; d < DB; ++d) orow[d] = a.w2_b + (srow[d] - a.w2_s);
+      fd0.load_offsets(orow, g4i);
+    }
   }
   for (int q = 0; q < np; ++q) {
     const int e = s_pe[q];
@@ -410,10 +436,16 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
         srow[u] = a.w13_s + rg * ng13;
         srow[CB + u] = a.w13_s + ru * ng13;
       }
-      Frag<4, 2 * CB, CPL4H> f;
+      Frag<4, 2 * CB, CPL4H, AFF> f;
       f.load(rows, srow, g4h, a.w13_q);
+      if (AFF) {
+        const uint16_t* orow[2 * CB];
+#pragma unroll
+        for (int u = 0; u < 2 * CB; ++u) orow[u] = a.w13_b + (srow[u] - a.w13_s);
+        f.load_offsets(orow, g4h);
+      }
       float acc[2 * CB][1];
-      f.template dot_shared<1>(g4h, act + (size_t)t * H, H, 1, acc);
+      f.template dot_shared<1>(g4h, act + (size_t)t * H, H, 1, acc, xsum + (size_t)t * (H / 32), 0);
 #pragma unroll
       for (int u = 0; u < CB; ++u) {
         const float gt = lane_group_sum(acc[u][0], g4h.lpr);
@@ -445,6 +477,10 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
     }
   }
   __syncthreads();
+  if (AFF) {
+    chunk_sums(hsum, hq, np * (I / 32));
+    if (!shared_down) __syncthreads();  // otherwise the shared down's barrier orders it
+  }
 
   // ---------------- shared down: sigma * (this block's rows over the group's slice)
   if (shared_down) {
@@ -480,7 +516,7 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
     const int t = (kGroups * q + g) / k;
     const float wq = s_pw[q];
     for (int rb0 = wave; rb0 < nrb; rb0 += 4 * DB) {
-      Frag<4, DB, CPL4I> f;
+      Frag<4, DB, CPL4I, AFF> f;
       if (q == 0 && rb0 == wave) {
         f = fd0;
       } else {
@@ -496,12 +532,22 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
           srow[d] = a.w2_s + ((size_t)e * H + (ok ? n : 0)) * ng2;
         }
         f.load(rows, srow, g4i, a.w2_q);
+        if (AFF) {
+          const uint16_t* orow[DB];
+#pragma unroll
+          for (int d = 0; d < DB; ++d) orow[d] = a.w2_b + (srow[d] - a.w2_s);
+          f.load_offsets(orow, g4i);
+        }
       }
       const _Float16* hv[DB];
+      const float* hx[DB];
 #pragma unroll
-      for (int d = 0; d < DB; ++d) hv[d] = hq + (size_t)q * I;
+      for (int d = 0; d < DB; ++d) {
+        hv[d] = hq + (size_t)q * I;
+        hx[d] = hsum + (size_t)q * (I / 32);
+      }
       float acc[DB];
-      f.dot_per_batch(g4i, hv, acc);
+      f.dot_per_batch(g4i, hv, acc, hx);
 #pragma unroll
       for (int d = 0; d < DB; ++d) {
         const float y = lane_group_sum(acc[d], g4i.lpr);
@@ -559,25 +605,39 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
 
 bool decode_real_widths(int H, int I, int Is) { return H == 2048 && I == 512 && Is == 512; }
 
-template <int MODE>
-static int occupancy(bool real, size_t lds) {
+template <int MODE, int HC, int IC, int ISC>
+static int occupancy_of(int variant, size_t lds) {
   int n = 0;
-  hipError_t err = real ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_kernel<MODE, 2048, 512, 512, kDecMaxT>,
-                                                                       256, lds)
-                        : hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_kernel<MODE, 0, 0, 0, kDecMaxT>, 256, lds);
+  hipError_t err;
+  switch (variant) {
+    case 0: err = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_kernel<MODE, HC, IC, ISC, 1, false>, 256, lds); break;
+    case 1: err = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_kernel<MODE, HC, IC, ISC, kDecMaxT, false>, 256, lds); break;
+    case 2: err = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_kernel<MODE, HC, IC, ISC, 1, true>, 256, lds); break;
+    default: err = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_kernel<MODE, HC, IC, ISC, kDecMaxT, true>, 256, lds); break;
+  }
   return err == hipSuccess ? n : 0;
 }
 
-int decode_blocks_per_cu(int mode, bool real, size_t lds_bytes) {
-  if (mode == DEC_BLOCK) return occupancy<DEC_BLOCK>(real, lds_bytes);
-  return mode == DEC_FORWARD ? occupancy<DEC_FORWARD>(real, lds_bytes) : occupancy<DEC_EXPERTS>(real, lds_bytes);
+template <int MODE>
+static int occupancy(bool real, int variant, size_t lds) {
+  return real ? occupancy_of<MODE, 2048, 512, 512>(variant, lds) : occupancy_of<MODE, 0, 0, 0>(variant, lds);
+}
+
+int decode_blocks_per_cu(int mode, bool real, int variant, size_t lds_bytes) {
+  if (mode == DEC_BLOCK) return occupancy<DEC_BLOCK>(real, variant, lds_bytes);
+  return mode == DEC_FORWARD ? occupancy<DEC_FORWARD>(real, variant, lds_bytes)
+                             : occupancy<DEC_EXPERTS>(real, variant, lds_bytes);
 }
 
 template <int MODE, int HC, int IC, int ISC>
 static void launch_mode(const DecodeArgs& a, size_t lds_bytes, hipStream_t s) {
   const dim3 grid(a.p.nb), block(256);
-  if (a.p.T == 1) hipLaunchKernelGGL((decode_kernel<MODE, HC, IC, ISC, 1>), grid, block, lds_bytes, s, a);
-  else hipLaunchKernelGGL((decode_kernel<MODE, HC, IC, ISC, kDecMaxT>), grid, block, lds_bytes, s, a);
+  switch (decode_variant(a.p.T, a.affine != 0)) {
+    case 0: hipLaunchKernelGGL((decode_kernel<MODE, HC, IC, ISC, 1, false>), grid, block, lds_bytes, s, a); break;
+    case 1: hipLaunchKernelGGL((decode_kernel<MODE, HC, IC, ISC, kDecMaxT, false>), grid, block, lds_bytes, s, a); break;
+    case 2: hipLaunchKernelGGL((decode_kernel<MODE, HC, IC, ISC, 1, true>), grid, block, lds_bytes, s, a); break;
+    default: hipLaunchKernelGGL((decode_kernel<MODE, HC, IC, ISC, kDecMaxT, true>), grid, block, lds_bytes, s, a); break;
+  }
 }
 
 int launch_decode(const DecodeArgs& a, int mode, size_t lds_bytes, hipStream_t s) {

@@ -65,9 +65,11 @@ __host__ __device__ inline DecodePlan decode_plan(int H, int E, int k, int I, in
 }
 
 // dynamic LDS of one workgroup: activations [T][H], the group's routed h
-// [npg][I] and its shared slice [T][sw], all binary16
+// [npg][I] and its shared slice [T][sw], all binary16, then (affine experts)
+// float sums of every 32 consecutive activations of each: [T][H/32], [npg][I/32]
 __host__ __device__ inline size_t decode_lds_bytes(const DecodePlan& p) {
-  return ((size_t)p.T * p.H + (size_t)p.npg * p.I + (size_t)p.T * p.sw) * 2;
+  return ((size_t)p.T * p.H + (size_t)p.npg * p.I + (size_t)p.T * p.sw) * 2 +
+         ((size_t)p.T * (p.H / 32) + (size_t)p.npg * (p.I / 32)) * 4;
 }
 
 struct DecodeArgs {
@@ -85,11 +87,16 @@ struct DecodeArgs {
   uint32_t* sync;        // the workspace's sync area (kSyncBytes)
   uint64_t* tagged;      // tagged zones (plan.z_words words)
   int give_up;           // nonzero: every bounded wait gives up at once (exercises the failure path)
+  int affine;            // routed experts are affine int4 (unsigned codes, w = q s + b)
+  const uint16_t* w13_b; const uint16_t* w2_b;  // affine: per-group binary16 offsets
   DecodePlan p;
 };
 
 
-int decode_blocks_per_cu(int mode, bool real_widths, size_t lds_bytes);
+// kernel instances: by token count (1, or up to kDecMaxT) and weight format
+static constexpr int kDecVariants = 4;
+__host__ __device__ inline int decode_variant(int T, bool affine) { return (T == 1 ? 0 : 1) + (affine ? 2 : 0); }
+int decode_blocks_per_cu(int mode, bool real_widths, int variant, size_t lds_bytes);
 int launch_decode(const DecodeArgs& a, int mode, size_t lds_bytes, hipStream_t s);
 bool decode_real_widths(int H, int I, int Is);
 

@@ -68,6 +68,20 @@ __device__ __forceinline__ float chunk_dot4(uint4 wq, const h2 xp[16]) {
   return acc;
 }
 
+// the same for unsigned codes (affine int4)
+__device__ __forceinline__ float chunk_dot4u(uint4 wq, const h2 xp[16]) {
+  const uint32_t ws[4] = {wq.x, wq.y, wq.z, wq.w};
+  float acc = 0.f;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    h2 w[4];
+    uint4x8_to_h2x4(ws[q], w);
+#pragma unroll
+    for (int p = 0; p < 4; ++p) acc = dot2(w[p], xp[4 * q + p], acc);
+  }
+  return acc;
+}
+
 __device__ __forceinline__ float chunk_dot8(uint4 wq, const h2 xp[8]) {
   float acc = 0.f;
   h2 w[4];
@@ -85,11 +99,15 @@ __device__ __forceinline__ float chunk_dot8(uint4 wq, const h2 xp[8]) {
 template <int BITS>
 __device__ __forceinline__ int chunk_group(int c) { return BITS == 4 ? (c >> 1) : (c >> 2); }
 
-// per-lane 16-byte chunks of up to NB row-batches
-template <int BITS, int NB, int MAXCPL>
+// per-lane 16-byte chunks of up to NB row-batches.  AFF (int4 only): the codes
+// are unsigned and each group also has a binary16 offset b, so a chunk adds
+// s * (q . x) + b * (sum of the chunk's 32 activations); the chunk sums of an
+// activation vector come from the caller (xs, one float per 32 elements).
+template <int BITS, int NB, int MAXCPL, bool AFF = false>
 struct Frag {
   uint4 q[NB][MAXCPL];
   uint16_t s[NB][MAXCPL];  // binary16 scale bits (converted where they are used)
+  uint16_t o[NB][MAXCPL];  // AFF: binary16 offset bits
 
   // rows[b]: this lane's row pointer in batch b (nullptr = masked); srow: its
   // scales (always a valid row).  A masked lane reads `safe` (a valid row)
@@ -110,10 +128,31 @@ struct Frag {
       }
   }
 
+  // AFF: the offsets, same indexing as the scales (orow[b] a valid row)
+  __device__ __forceinline__ void load_offsets(const uint16_t* const orow[NB], const RowGeom& g) {
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int b = 0; b < NB; ++b)
+#pragma unroll
+      for (int m = 0; m < MAXCPL; ++m) {
+        const int c = (lane % g.lpr) + g.lpr * (m < g.cpl ? m : 0);
+        o[b][m] = orow[b][chunk_group<BITS>(c)];
+      }
+  }
+
+  __device__ __forceinline__ float chunk4(uint4 wq, const h2 xp[16], uint16_t sb, uint16_t ob, float xsum,
+                                          float acc) const {
+    if (AFF) {
+      acc = fmaf(chunk_dot4u(wq, xp), half_bits_to_float(sb), acc);
+      return fmaf(xsum, half_bits_to_float(ob), acc);
+    }
+    return fmaf(chunk_dot4(wq, xp), half_bits_to_float(sb), acc);
+  }
+
   // acc[b][t] = this lane's share of row_b . act_t (same activations for every batch)
   template <int TT>
   __device__ __forceinline__ void dot_shared(const RowGeom& g, const _Float16* act, int stride, int T,
-                                             float acc[NB][TT]) const {
+                                             float acc[NB][TT], const float* xs = nullptr, int xs_stride = 0) const {
     const int lane = threadIdx.x & 63;
     constexpr int EPC = BITS == 4 ? 32 : 16;
 #pragma unroll
@@ -131,8 +170,9 @@ struct Frag {
             if (BITS == 4) {
               h2 xp[16];
               act32(a, xp);
+              const float xsum = AFF ? xs[(size_t)t * xs_stride + c] : 0.f;
 #pragma unroll
-              for (int b = 0; b < NB; ++b) acc[b][t] = fmaf(chunk_dot4(q[b][m], xp), half_bits_to_float(s[b][m]), acc[b][t]);
+              for (int b = 0; b < NB; ++b) acc[b][t] = chunk4(q[b][m], xp, s[b][m], o[b][m], xsum, acc[b][t]);
             } else {
               h2 xp[8];
               act16(a, xp);
@@ -145,8 +185,10 @@ struct Frag {
     }
   }
 
-  // acc[b] = this lane's share of row_b . act_b (one activation vector per batch)
-  __device__ __forceinline__ void dot_per_batch(const RowGeom& g, const _Float16* const act[NB], float acc[NB]) const {
+  // acc[b] = this lane's share of row_b . act_b (one activation vector per batch;
+  // AFF: xs[b] its chunk sums)
+  __device__ __forceinline__ void dot_per_batch(const RowGeom& g, const _Float16* const act[NB], float acc[NB],
+                                                const float* const* xs = nullptr) const {
     const int lane = threadIdx.x & 63;
     constexpr int EPC = BITS == 4 ? 32 : 16;
 #pragma unroll
@@ -160,7 +202,7 @@ struct Frag {
           if (BITS == 4) {
             h2 xp[16];
             act32(act[b] + EPC * c, xp);
-            acc[b] = fmaf(chunk_dot4(q[b][m], xp), half_bits_to_float(s[b][m]), acc[b]);
+            acc[b] = chunk4(q[b][m], xp, s[b][m], o[b][m], AFF ? xs[b][c] : 0.f, acc[b]);
           } else {
             h2 xp[8];
             act16(act[b] + EPC * c, xp);

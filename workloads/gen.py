@@ -63,12 +63,22 @@ class Weights:
     sh13_s: np.ndarray    # uint16 [2Is][H/G]
     sh2_q: np.ndarray     # int8   [H][Is]
     sh2_s: np.ndarray     # uint16 [H][Is/G]
+    # affine int4 routed experts: unsigned codes in w13_q / w2_q and one
+    # binary16 offset per group; None for the symmetric (two's-complement) form
+    w13_b: Optional[np.ndarray] = None  # uint16 [E][2I][H/G]
+    w2_b: Optional[np.ndarray] = None   # uint16 [E][H][I/G]
 
     FIELDS = ("router_q", "router_s", "w13_q", "w13_s", "w2_q", "w2_s",
               "sh13_q", "sh13_s", "sh2_q", "sh2_s")
+    AFFINE_FIELDS = ("w13_b", "w2_b")
+
+    @property
+    def affine(self) -> bool:
+        return self.w13_b is not None
 
     def items(self):
-        return [(f, getattr(self, f)) for f in self.FIELDS]
+        fields = self.FIELDS + (self.AFFINE_FIELDS if self.affine else ())
+        return [(f, getattr(self, f)) for f in fields]
 
     def nbytes(self) -> int:
         return sum(a.nbytes for _, a in self.items())
@@ -281,3 +291,35 @@ def make_case(dims: Dims, T: int, seed: int, bias: str = "none", c: float = 0.0,
 
 def with_dims(d: Dims, **kw) -> Dims:
     return replace(d, **kw)
+
+
+def pack_uint4(u: np.ndarray) -> np.ndarray:
+    """Pack unsigned 4-bit codes (values in [0, 15]) two per byte, even element low."""
+    u = np.asarray(u)
+    if u.shape[-1] % 2:
+        raise ValueError("int4 rows need an even length")
+    if u.min(initial=0) < 0 or u.max(initial=0) > 15:
+        raise ValueError("unsigned 4-bit code out of [0, 15]")
+    u = u.astype(np.uint8)
+    return (u[..., 0::2] | (u[..., 1::2] << 4)).astype(np.uint8)
+
+
+def with_affine_offsets(W: Weights, seed: int) -> Weights:
+    """The same routed-expert bytes and scales read as affine int4: each byte's
+    nibbles become unsigned codes q in [0, 15] (uniform, as the bytes are), and
+    every group gets a binary16 offset b = -s * u with u ~ U(7, 9), so that
+    w = s q + b is centred near zero as in an affine 4-bit checkpoint."""
+    rng = np.random.default_rng(seed)
+
+    def offsets(s_bits):
+        s = s_bits.view(np.float16).astype(np.float64)
+        return f16_bits(-s * rng.uniform(7.0, 9.0, size=s.shape))
+
+    return replace(W, w13_b=offsets(W.w13_s), w2_b=offsets(W.w2_s))
+
+
+def make_affine_case(dims: Dims, T: int, seed: int, bias: str = "none", c: float = 0.0,
+                     real_experts: bool = False) -> Case:
+    """An ad-hoc case whose routed experts are affine int4."""
+    case = make_case(dims, T, seed, bias=bias, c=c, real_experts=real_experts)
+    return replace(case, name=case.name + "_affine", weights=with_affine_offsets(case.weights, seed + 77))
