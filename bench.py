@@ -146,6 +146,82 @@ def time_block(cfg, steps, warmup, R, torch, m, gen):
     return us
 
 
+def time_layers(L, steps, warmup, R, torch, m, gen):
+    """Per-layer time of L MoE sub-blocks at T=1, real widths, each layer's
+    weights drawn anew (the decode-token recipe: no router bias): one
+    moe_layers_forward launch per step, against L moe_block_forward launches
+    per step.  R device copies of the L-layer stack are rotated so no step
+    finds its weights in the last-level cache."""
+    import ctypes
+    import numpy as np
+    d = gen.REAL
+    Ws, gains = [], []
+    for l in range(L):
+        W, _, rng = gen.make_weights(d, 4000 + l)
+        Ws.append(W)
+        gains.append(gen.f16_bits(rng.uniform(0.5, 1.5, size=d.H)))
+    x = gen.make_x(1, d.H, np.random.default_rng(4999))
+    stacks = [m.LayerStack(Ws, gains)]
+    del Ws
+    for _ in range(R - 1):
+        s_ = object.__new__(m.LayerStack)
+        s_.buffer = stacks[0].buffer.clone()
+        off = s_.buffer.data_ptr() - stacks[0].buffer.data_ptr()
+        s_.struct = m.MoeWeights(*[(getattr(stacks[0].struct, f) + off) if getattr(stacks[0].struct, f) else None
+                                   for f in m.binding.WEIGHT_FIELDS])
+        s_.gain, s_.stride, s_.L = stacks[0].gain + off, stacks[0].stride, L
+        stacks.append(s_)
+    dims = m.make_dims(d.H, d.E, d.k, d.I, d.Is, d.G)
+    xt = torch.from_numpy(x.view(np.int16)).cuda()
+    out = torch.empty_like(xt)
+    tmp = [torch.empty_like(xt) for _ in range(2)]
+    ws = m.layers_workspace(dims, 1, L)
+    stream = torch.cuda.current_stream().cuda_stream
+    lib = m.lib()
+
+    def one_launch(st):
+        return lib.moe_layers_forward(ctypes.byref(dims), ctypes.byref(st.struct), st.gain, st.stride, L, 1e-6,
+                                      xt.data_ptr(), 1, out.data_ptr(), ws.data_ptr(), ws.numel(), stream)
+
+    per_layer = []
+    for st in stacks:
+        row = []
+        for l in range(L):
+            row.append(m.MoeWeights(*[(getattr(st.struct, f) + l * st.stride) if getattr(st.struct, f) else None
+                                      for f in m.binding.WEIGHT_FIELDS]))
+        per_layer.append(row)
+
+    def chained(i):
+        cur = xt
+        for l in range(L):
+            dst = out if l == L - 1 else tmp[l % 2]
+            r = lib.moe_block_forward(ctypes.byref(dims), ctypes.byref(per_layer[i][l]), cur.data_ptr(),
+                                      stacks[i].gain + l * stacks[i].stride, 1e-6, 1, dst.data_ptr(), None, None,
+                                      None, ws.data_ptr(), ws.numel(), stream)
+            if r != 0:
+                return r
+            cur = dst
+        return 0
+
+    res = {}
+    for name, fn in (("one_launch", lambda i: one_launch(stacks[i])), ("launch_per_layer", chained)):
+        for s in range(warmup):
+            st_ = fn(s % R)
+            if st_ != 0:
+                raise RuntimeError(f"{name}: {m.moe_status_string(st_)}")
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for s in range(steps):
+            fn((warmup + s) % R)
+        e1.record()
+        torch.cuda.synchronize()
+        res[name] = e0.elapsed_time(e1) * 1e3 / steps
+    del stacks, per_layer
+    torch.cuda.empty_cache()
+    return res
+
+
 def time_config(cfg, steps, warmup, R, torch, m, gen, per_launch_events):
     import ctypes
     import numpy as np
@@ -320,6 +396,7 @@ def main():
     ap.add_argument("--no-other-workloads", action="store_true", help="time only T=1 and T=512")
     ap.add_argument("--no-sub-block", action="store_true",
                     help="skip the RMSNorm + residual sub-block timing (its launches share the block's kernel names)")
+    ap.add_argument("--layers", type=int, default=8, help="sub-blocks per call in the multi-layer timing (0: skip)")
     ap.add_argument("--profile-run", choices=["decode", "chunk"], default=None,
                     help="untimed steps plus a calibration copy, for rocprofv3 counter passes (no JSON metric line)")
     args = ap.parse_args()
@@ -359,6 +436,12 @@ def main():
         sb1 = time_block(1, args.steps, args.warmup, args.copies, torch, m, gen)
         sb4 = time_block(4, args.chunk_steps, max(10, args.warmup // 10), max(4, args.copies // 8), torch, m, gen)
         log(f"  {sb1:.3f} / {sb4:.3f} us/step")
+
+    lay = None
+    if args.layers > 0:
+        log(f"{args.layers} sub-blocks per step at T=1: one launch, and one launch per layer ...")
+        lay = time_layers(args.layers, max(20, args.steps // 10), max(5, args.warmup // 10), 4, torch, m, gen)
+        log(f"  {lay['one_launch']:.3f} / {lay['launch_per_layer']:.3f} us/step")
 
     d1 = r1["dims"]
     b1 = algorithmic_bytes(d1, 1, r1["distinct_experts"])
@@ -406,6 +489,15 @@ def main():
                              "t1_tokens_per_s": round(1e6 / sb1, 1), "t512_tokens_per_s": round(512e6 / sb4, 1),
                              "t1_extra_us_vs_block": round(sb1 - r1["us_per_step"], 3),
                              "t512_extra_us_vs_block": round(sb4 - r4["us_per_step"], 3)}
+    if lay is not None:
+        L = args.layers
+        line["layers"] = {"workload": f"{L} MoE sub-blocks in turn at T=1, real widths, weights drawn anew per layer, "
+                                      "4 copies of the stack rotated",
+                          "layers": L,
+                          "one_launch_us_per_layer": round(lay["one_launch"] / L, 3),
+                          "launch_per_layer_us_per_layer": round(lay["launch_per_layer"] / L, 3),
+                          "one_launch_tokens_per_s": round(1e6 / lay["one_launch"], 1),
+                          "speedup": round(lay["launch_per_layer"] / lay["one_launch"], 3)}
     if not args.no_cpu:
         log("cpu baseline ...")
         line["cpu_baseline"] = cpu_baseline(gen)

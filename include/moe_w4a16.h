@@ -177,6 +177,30 @@ MOE_API int moe_block_forward(const moe_dims* dims, const moe_weights* w, const 
                               float eps, int32_t T, uint16_t* out, int32_t* ids, float* weights,
                               float* shared_gate, void* ws, size_t ws_bytes, hipStream_t stream);
 
+/* L MoE sub-blocks applied in turn (the Chimera notebook, "Pipeline": the
+ * decoder runs as one kernel per token, every layer's weights a fixed offset
+ * from the previous layer's, so the entry takes the same pointers for any
+ * depth):
+ *   h_0 = h,  h_{l+1} = moe_block_forward(layer l)(h_l)  (binary16 between layers),
+ *   out = h_L.
+ * Layer l's arrays are those of `w` and `gain` (layer 0) each moved on by
+ * l * layer_stride bytes; layer_stride is a multiple of 16 (0: the same weights
+ * every layer).  The result equals L moe_block_forward calls chained through
+ * binary16 buffers, bit for bit.
+ *   L     1 .. 256 (else MOE_ERR_SHAPE)
+ *   h     [T][H] binary16, must not alias out; gain as for moe_block_forward
+ *   ws    ws_bytes >= moe_layers_workspace_bytes(dims, T, L), with the
+ *         workspace rules above
+ * With T <= 4 (and MOE_PATH_CHUNK not set) all L layers are one persistent
+ * launch: a layer's output reaches the next layer through the workspace and
+ * the next layer's router and shared-expert rows are loaded while the current
+ * layer's last sums are formed.  Otherwise the layers are L launches in order.
+ * No routing outputs. */
+MOE_API size_t moe_layers_workspace_bytes(const moe_dims* dims, int32_t T, int32_t L);
+MOE_API int moe_layers_forward(const moe_dims* dims, const moe_weights* w, const uint16_t* gain, int64_t layer_stride,
+                               int32_t L, float eps, const uint16_t* h, int32_t T, uint16_t* out, void* ws,
+                               size_t ws_bytes, hipStream_t stream);
+
 /* moe_forward without a workspace argument and without any allocation, for
  * callers that cannot allocate device memory: code under HIP graph capture,
  * tight serving loops, harnesses that forbid hipMalloc.  Same arguments and
@@ -188,7 +212,8 @@ MOE_API int moe_block_forward(const moe_dims* dims, const moe_weights* w, const 
  * enqueued (at real widths the limit admits 160 tokens and more).  Every call on
  * one GPU shares that GPU's array: calls that may overlap on one GPU (other
  * streams, other threads) race and must be ordered by the caller.  Each
- * completed call leaves the array's counters zero, as the next call needs. */
+ * completed call leaves the array as the next call needs it (arrival counters
+ * zero, call counters advanced). */
 #define MOE_NOALLOC_SCRATCH_BYTES ((size_t)8 << 20)
 MOE_API int moe_forward_noalloc(const moe_dims* dims, const moe_weights* w, const uint16_t* x, int32_t T,
                                 uint16_t* out, int32_t* ids, float* weights, float* shared_gate,

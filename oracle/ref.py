@@ -15,6 +15,8 @@ What it computes (all in float64, no intermediate rounding):
 * The MoE sub-block of a decoder layer (the Chimera notebook, sections 7 and
   10, the decoder-layer assemblies): post-attention RMSNorm, the MoE block on
   the normalised activations, then the residual add.
+* Several sub-blocks in turn (the Chimera notebook, "Pipeline"), with each
+  layer's output stored as binary16 before the next layer reads it.
 * The router and the shared-gate row are stored 8-bit, group-64 rows, stacked
   (the TensorFold PR, "Design").  Routed experts int4, shared expert int8,
   activations fp16 (the Chimera notebook, pipeline intro and "Key takeaways").
@@ -281,3 +283,18 @@ def block_forward(h_bits, gain_bits, eps: float, W, dims):
     r["out"] = half_bits_to_f64(h_bits) + r["moe"]
     r["a_bits"] = a_bits
     return r
+
+
+def layers_forward(h_bits, gain_bits_per_layer, eps: float, W_per_layer, dims) -> np.ndarray:
+    """Several MoE sub-blocks applied in turn (the Chimera notebook,
+    "Pipeline": the decoder's layers run one after another inside one kernel
+    per token).  Reading: each layer's output is stored as binary16 before the
+    next layer reads it, as it would be between separate calls, so
+    h_{l+1} = binary16(block_forward(h_l)["out"]).  Returns the last layer's
+    output in float64 (before its own binary16 rounding)."""
+    h = np.asarray(h_bits)
+    out = None
+    for gain_bits, W in zip(gain_bits_per_layer, W_per_layer):
+        out = block_forward(h, gain_bits, eps, W, dims)["out"]
+        h = f64_to_half_bits(out)
+    return out

@@ -43,7 +43,8 @@ def test_every_declared_symbol_is_exported(L):
     text = open(HEADER).read()
     names = re.findall(r"MOE_API\s+[\w\s\*]+?\b(moe_\w+)\s*\(", text)
     assert set(names) == {"moe_workspace_bytes", "moe_route", "moe_experts_w4a16", "moe_forward", "moe_block_forward",
-                          "moe_forward_noalloc", "moe_status_string"}
+                          "moe_forward_noalloc", "moe_status_string", "moe_layers_workspace_bytes",
+                          "moe_layers_forward"}
     for n in names:
         assert hasattr(L, n), n
 
@@ -181,3 +182,37 @@ def test_refusals_forward_noalloc(L):
     assert big > 128
     assert _noalloc(L, d, W, T=big) == -7
     assert _noalloc(L, d, W, T=512) == -7
+
+
+def _layers(L, dims=None, W=None, gain=FAKE + 4096 * 20, stride=1 << 20, nl=2, eps=1e-6, h=FAKE + 4096 * 30, T=1,
+            out=FAKE + 4096 * 40, ws=FAKE, ws_bytes=1 << 30):
+    dims = dims if dims is not None else _dims()
+    W = W if W is not None else _weights()
+    return L.moe_layers_forward(ctypes.byref(dims), ctypes.byref(W), gain, stride, nl, eps, h, T, out, ws, ws_bytes,
+                                None)
+
+
+def test_layers_workspace_sizes(L):
+    d = _dims()
+    one = m.moe_workspace_bytes(d, 1)
+    assert m.moe_layers_workspace_bytes(d, 1, 1) >= one
+    # each layer of the persistent launch has its own hand-off zones
+    assert m.moe_layers_workspace_bytes(d, 1, 8) > m.moe_layers_workspace_bytes(d, 1, 2)
+    assert m.moe_layers_workspace_bytes(d, 1, 0) == 0
+    assert m.moe_layers_workspace_bytes(d, 1, 257) == 0
+    # T > 4: the grouped-GEMM path's workspace plus one [T][H] buffer
+    assert m.moe_layers_workspace_bytes(d, 64, 3) >= m.moe_workspace_bytes(d, 64) + 64 * 2048 * 2
+
+
+def test_refusals_layers(L):
+    assert _layers(L, nl=0) == -2
+    assert _layers(L, nl=257) == -2
+    assert _layers(L, stride=8) == -3              # layer stride keeps 16-byte alignment
+    assert _layers(L, gain=None) == -1
+    assert _layers(L, W=_weights(sh2_s=None)) == -1
+    assert _layers(L, h=FAKE + 4096 * 30 + 2) == -3
+    assert _layers(L, out=FAKE + 4096 * 30) == -2  # out aliases h
+    assert _layers(L, eps=float("nan")) == -2
+    need = m.moe_layers_workspace_bytes(_dims(), 1, 2)
+    assert _layers(L, ws_bytes=need - 1) == -4
+    assert _layers(L, T=0) == 0

@@ -422,3 +422,59 @@ def test_planted_residual_mistake_is_caught():
         return r
     with pytest.raises(AssertionError):
         _block_pins(no_residual)
+
+
+def _zero_layer(W):
+    """The same arrays with every routed and shared code zero: the sub-block is the identity."""
+    return Weights(**{f: (np.zeros_like(v) if f in ("w13_q", "w2_q", "sh13_q", "sh2_q") else v)
+                      for f, v in W.items()})
+
+
+def _layers_pins(layers):
+    case = _tiny_case(seed=31, T=3)
+    d = case.dims
+    rng = np.random.default_rng(32)
+    h = f16_bits(rng.standard_normal((3, d.H)) * 2.0)
+    g1, g2 = f16_bits(rng.uniform(0.5, 1.5, d.H)), f16_bits(rng.uniform(0.5, 1.5, d.H))
+    B = case.weights
+    Z = _zero_layer(_tiny_case(seed=33, T=1).weights)
+    one = ref.block_forward(h, g2, 1e-6, B, d)["out"]
+    # one layer is the sub-block itself
+    assert np.array_equal(layers(h, [g2], 1e-6, [B], d), one)
+    # identity layers leave the residual stream exactly as it is
+    assert np.array_equal(layers(h, [g1, g2, g1], 1e-6, [Z, Z, Z], d), ref.half_bits_to_f64(h))
+    # an identity layer first: the second layer, with its own weights and gain, sees h itself
+    assert np.array_equal(layers(h, [g1, g2], 1e-6, [Z, B], d), one)
+    # an identity layer last: it returns what it reads, the binary16 value of the first layer's output
+    want = ref.half_bits_to_f64(ref.f64_to_half_bits(one))
+    assert np.array_equal(layers(h, [g2, g1], 1e-6, [B, Z], d), want)
+    assert not np.array_equal(want, one)  # the case does exercise the rounding
+
+
+def test_layers_forward_pins():
+    _layers_pins(ref.layers_forward)
+
+
+def _layers_unrounded(h_bits, gains, eps, Ws, dims):
+    X = ref.half_bits_to_f64(h_bits)
+    for g, W in zip(gains, Ws):
+        X = X + ref.block_forward(ref.f64_to_half_bits(X), g, eps, W, dims)["moe"]
+    return X
+
+
+def _layers_first_weights(h_bits, gains, eps, Ws, dims):
+    return ref.layers_forward(h_bits, gains, eps, [Ws[0]] * len(Ws), dims)
+
+
+def _layers_first_gain(h_bits, gains, eps, Ws, dims):
+    return ref.layers_forward(h_bits, [gains[0]] * len(gains), eps, Ws, dims)
+
+
+@pytest.mark.parametrize("name,bad", [
+    ("residual carried in float64 between layers", _layers_unrounded),
+    ("every layer reads layer 0's weights", _layers_first_weights),
+    ("every layer reads layer 0's gain", _layers_first_gain),
+])
+def test_planted_layer_mistakes_are_caught(name, bad):
+    with pytest.raises(AssertionError):
+        _layers_pins(bad)

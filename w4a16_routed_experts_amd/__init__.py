@@ -25,6 +25,10 @@ from .binding import (  # noqa: F401
     moe_forward_noalloc,
     NOALLOC_SCRATCH_BYTES,
     moe_block_forward,
+    moe_layers_workspace_bytes,
+    moe_layers_forward,
+    layers_workspace,
+    LayerStack,
     DeviceWeights,
     make_dims,
     workspace,

@@ -76,6 +76,12 @@ def lib() -> ctypes.CDLL:
         if hasattr(L, "moe_block_forward"):  # a library without it raises when it is called
             L.moe_block_forward.argtypes = [dims_p, w_p, vp, vp, ctypes.c_float, i32, vp, vp, vp, vp, vp, sz, vp]
             L.moe_block_forward.restype = ctypes.c_int
+        if hasattr(L, "moe_layers_forward"):
+            L.moe_layers_workspace_bytes.argtypes = [dims_p, i32, i32]
+            L.moe_layers_workspace_bytes.restype = sz
+            L.moe_layers_forward.argtypes = [dims_p, w_p, vp, ctypes.c_int64, i32, ctypes.c_float, vp, i32, vp, vp,
+                                             sz, vp]
+            L.moe_layers_forward.restype = ctypes.c_int
         _lib = L
     return _lib
 
@@ -164,6 +170,51 @@ def moe_block_forward(dims, weights, h, gain, eps, T, out, ids=None, w=None, sha
                                  _ptr(out), _ptr(ids), _ptr(w), _ptr(shared_gate), _ptr(ws), _nbytes(ws),
                                  _stream(stream))
     return _check(st, "moe_block_forward", raise_on_error)
+
+
+def moe_layers_workspace_bytes(dims: MoeDims, T: int, L: int) -> int:
+    return int(lib().moe_layers_workspace_bytes(ctypes.byref(dims), T, L))
+
+
+def layers_workspace(dims: MoeDims, T: int, L: int, device="cuda"):
+    """A zero-filled workspace for moe_layers_forward (uint8 tensor)."""
+    import torch
+    return torch.zeros(max(256, moe_layers_workspace_bytes(dims, T, L)), dtype=torch.uint8, device=device)
+
+
+def moe_layers_forward(dims, weights, gain, layer_stride, L, eps, h, T, out, ws=None, stream=None,
+                       raise_on_error=True) -> int:
+    st = lib().moe_layers_forward(ctypes.byref(dims), ctypes.byref(weights), _ptr(gain), int(layer_stride), L,
+                                  float(eps), _ptr(h), T, _ptr(out), _ptr(ws), _nbytes(ws), _stream(stream))
+    return _check(st, "moe_layers_forward", raise_on_error)
+
+
+class LayerStack:
+    """L layers' weights and norm gains in one device buffer, every array of
+    layer l at the same offset inside layer l's region and the regions a fixed
+    stride apart: the layout moe_layers_forward reads.  `struct` and `gain`
+    point into layer 0; `stride` is the region size in bytes."""
+
+    def __init__(self, host_weights, gains, device="cuda"):
+        import numpy as np
+        import torch
+        fields = [f for f in WEIGHT_FIELDS if getattr(host_weights[0], f, None) is not None]
+        offs, o = {}, 0
+        for f in fields + ["gain"]:
+            a = gains[0] if f == "gain" else getattr(host_weights[0], f)
+            offs[f] = o
+            o = (o + a.nbytes + 255) // 256 * 256
+        self.stride = o
+        host = np.zeros((len(host_weights), o), dtype=np.uint8)
+        for l, (W, g) in enumerate(zip(host_weights, gains)):
+            for f in fields + ["gain"]:
+                a = np.ascontiguousarray(g if f == "gain" else getattr(W, f))
+                host[l, offs[f]:offs[f] + a.nbytes] = a.reshape(-1).view(np.uint8)
+        self.buffer = torch.from_numpy(host).to(device)
+        base = self.buffer.data_ptr()
+        self.struct = MoeWeights(*[base + offs[f] if f in offs else None for f in WEIGHT_FIELDS])
+        self.gain = base + offs["gain"]
+        self.L = len(host_weights)
 
 
 class DeviceWeights:

@@ -91,11 +91,12 @@ struct DecodeWs {
   uint64_t* tagged;
 };
 
-DecodeWs carve_decode(const moe_dims* d, int T, Carve& c) {
+// L: sub-blocks per call (each has its own tagged zones)
+DecodeWs carve_decode(const moe_dims* d, int T, Carve& c, int L = 1) {
   const DecodePlan p = plan_of(d, T);
   DecodeWs w;
   w.sync = c.take<uint32_t>(kSyncBytes);
-  w.tagged = c.take<uint64_t>(p.z_words * 8);
+  w.tagged = c.take<uint64_t>(p.z_words * 8 * (size_t)L);
   return w;
 }
 
@@ -129,6 +130,24 @@ size_t workspace_bytes(const moe_dims* d, int T) {
   if (decode_admissible(d, T)) {
     Carve c2{nullptr};
     carve_decode(d, T, c2);
+    bytes = std::max(bytes, c2.off);
+  }
+  return bytes;
+}
+
+// moe_layers_forward: the few-token path's zones for L layers, or the
+// grouped-GEMM path's workspace followed by one [T][H] binary16 buffer (the
+// output of every other layer)
+size_t layers_workspace_bytes(const moe_dims* d, int T, int L) {
+  if (T == 0) return 0;
+  Carve c{nullptr};
+  ChunkArgs a{};
+  carve_chunk(d, T, c, a);
+  c.take<uint16_t>((size_t)T * d->hidden * 2);
+  size_t bytes = c.off;
+  if (decode_admissible(d, T)) {
+    Carve c2{nullptr};
+    carve_decode(d, T, c2, L);
     bytes = std::max(bytes, c2.off);
   }
   return bytes;
@@ -200,7 +219,7 @@ void fill_weights(const moe_weights* w, int8_t const** rq, uint16_t const** rs, 
 
 int run_decode(const moe_dims* d, const moe_weights* w, const uint16_t* x, int T, uint16_t* out, int mode,
                int32_t* ids_out, float* w_out, float* sig_out, const int32_t* ids_in, const float* w_in, void* ws,
-               hipStream_t s, const uint16_t* gain = nullptr, float eps = 0.f) {
+               hipStream_t s, const uint16_t* gain = nullptr, float eps = 0.f, int L = 1, long long lstride = 0) {
   DeviceInfo* di = nullptr;
   int st = device_info(&di);
   if (st != MOE_OK) return st;
@@ -214,20 +233,27 @@ int run_decode(const moe_dims* d, const moe_weights* w, const uint16_t* x, int T
   a.give_up = (d->flags & MOE_DEBUG_WAIT_GIVE_UP) ? 1 : 0;
   a.affine = (d->flags & MOE_FMT_AFFINE4) ? 1 : 0;
   a.w13_b = w->w13_b; a.w2_b = w->w2_b;
+  a.L = L; a.lstride = lstride;
   Carve c{static_cast<char*>(ws)};
-  DecodeWs dw = carve_decode(d, T, c);
+  DecodeWs dw = carve_decode(d, T, c, L);
   a.sync = dw.sync; a.tagged = dw.tagged;
   const size_t lds = decode_lds_bytes(plan_of(d, T));
-  const bool real = decode_real_widths(d->hidden, d->expert_inter, d->shared_inter);
-  const int per_cu = di->occ[mode][real ? 1 : 0][decode_variant(T, a.affine != 0)][(lds + 4095) / 4096];
+  const int variant = decode_variant(T, a.affine != 0), step = (int)((lds + 4095) / 4096);
   // Every workgroup must be resident at once (they wait for each other, with
   // bounded waits): the grid is what an idle device holds, in whole groups of
   // 8, at most 8 x kMaxGroupWgs; a group needs at least H / 64 members (its
-  // members' output rows fit the per-block row buffer).
-  const int nj = std::min(kMaxGroupWgs, per_cu * di->cus / kGroups);
+  // members' output rows fit the per-block row buffer).  The instances built
+  // for the real widths cover the router rows and shared columns only with
+  // kMaxGroupWgs members per group; with fewer the generic instance runs.
+  bool real = decode_real_widths(d->hidden, d->expert_inter, d->shared_inter);
+  int nj = std::min(kMaxGroupWgs, di->occ[mode][real ? 1 : 0][variant][step] * di->cus / kGroups);
+  if (real && nj < kMaxGroupWgs) {
+    real = false;
+    nj = std::min(kMaxGroupWgs, di->occ[mode][0][variant][step] * di->cus / kGroups);
+  }
   if (nj < 1 || nj * kMaxGroupWgs < d->hidden) return MOE_ERR_LAUNCH;
   a.p = plan_of(d, T, kGroups * nj);
-  return launch_decode(a, mode, lds, s);
+  return launch_decode(a, mode, real, lds, s);
 }
 
 ChunkArgs chunk_args(const moe_dims* d, const moe_weights* w, const uint16_t* x, int T, uint16_t* out, void* ws) {
@@ -409,35 +435,40 @@ int launch_forward(const moe_dims* dims, const moe_weights* w, const uint16_t* x
   return launch_forward_chunk(a, stream);
 }
 
-}  // namespace
-
-extern "C" {
-
-MOE_API int moe_block_forward(const moe_dims* dims, const moe_weights* w, const uint16_t* h, const uint16_t* gain,
-                              float eps, int32_t T, uint16_t* out, int32_t* ids, float* weights,
-                              float* shared_gate, void* ws, size_t ws_bytes, hipStream_t stream) {
-  int st = check_common(dims, h, T, ws, ws_bytes);
+// the MoE sub-block's checks (every one but the workspace size)
+int validate_block(const moe_dims* dims, const moe_weights* w, const uint16_t* h, const uint16_t* gain, float eps,
+                   int32_t T, const uint16_t* out, const int32_t* ids, const float* weights, const float* shared_gate,
+                   const void* ws) {
+  int st = check_dims(dims, T);
   if (st != MOE_OK || T == 0) return st;
-  if (!w) return MOE_ERR_NULL;
+  if (!h || !ws || !w) return MOE_ERR_NULL;
   if (any_null({w->router_q, w->router_s, w->w13_q, w->w13_s, w->w2_q, w->w2_s, w->sh13_q, w->sh13_s, w->sh2_q,
                 w->sh2_s, out, gain}))
     return MOE_ERR_NULL;
+  if (!aligned(h, 16) || !aligned(ws, 256)) return MOE_ERR_ALIGN;
   if (!all16({w->router_q, w->router_s, w->w13_q, w->w13_s, w->w2_q, w->w2_s, w->sh13_q, w->sh13_s, w->sh2_q,
               w->sh2_s, out, gain}) ||
       !all4({ids, weights, shared_gate}))
     return MOE_ERR_ALIGN;
+  if ((dims->flags & kPathMask) == MOE_PATH_DECODE && !decode_admissible(dims, T)) return MOE_ERR_SHAPE;
   if ((st = check_affine(dims, w)) != MOE_OK) return st;
   if (!(eps >= 0.f && eps <= 3.0e38f)) return MOE_ERR_SHAPE;  // also refuses NaN and infinity
-  {
-    const uintptr_t hb = reinterpret_cast<uintptr_t>(h), ob = reinterpret_cast<uintptr_t>(out);
-    const uintptr_t n = (uintptr_t)T * dims->hidden * 2;
-    if (hb < ob + n && ob < hb + n) return MOE_ERR_SHAPE;  // out overlaps the residual stream
-  }
+  const uintptr_t hb = reinterpret_cast<uintptr_t>(h), ob = reinterpret_cast<uintptr_t>(out);
+  const uintptr_t n = (uintptr_t)T * dims->hidden * 2;
+  if (hb < ob + n && ob < hb + n) return MOE_ERR_SHAPE;  // out overlaps the residual stream
+  return MOE_OK;
+}
+
+// the sub-block on validated arguments
+int launch_block(const moe_dims* dims, const moe_weights* w, const uint16_t* h, const uint16_t* gain, float eps,
+                 int32_t T, uint16_t* out, int32_t* ids, float* weights, float* shared_gate, void* ws,
+                 hipStream_t stream) {
   if (use_decode(dims, T))
     return run_decode(dims, w, h, T, out, DEC_BLOCK, ids, weights, shared_gate, nullptr, nullptr, ws, stream, gain,
                       eps);
   DeviceInfo* di = nullptr;
-  if ((st = device_info(&di)) != MOE_OK) return st;
+  int st = device_info(&di);
+  if (st != MOE_OK) return st;
   ChunkArgs a = chunk_args(dims, w, h, T, out, ws);
   if (ids) a.ids = ids;
   if (weights) a.wts = weights;
@@ -449,6 +480,72 @@ MOE_API int moe_block_forward(const moe_dims* dims, const moe_weights* w, const 
   a.shared_tiles = (T + kSharedRows - 1) / kSharedRows;
   a.cus = di->cus;
   return launch_forward_chunk(a, stream);
+}
+
+template <typename P>
+P* offset_ptr(P* p, long long off) {
+  return p ? reinterpret_cast<P*>(reinterpret_cast<uintptr_t>(p) + off) : p;
+}
+
+// the weights of the layer `off` bytes on from w
+moe_weights layer_weights(const moe_weights* w, long long off) {
+  moe_weights r = *w;
+  r.router_q = offset_ptr(w->router_q, off); r.router_s = offset_ptr(w->router_s, off);
+  r.w13_q = offset_ptr(w->w13_q, off); r.w13_s = offset_ptr(w->w13_s, off);
+  r.w2_q = offset_ptr(w->w2_q, off); r.w2_s = offset_ptr(w->w2_s, off);
+  r.sh13_q = offset_ptr(w->sh13_q, off); r.sh13_s = offset_ptr(w->sh13_s, off);
+  r.sh2_q = offset_ptr(w->sh2_q, off); r.sh2_s = offset_ptr(w->sh2_s, off);
+  r.w13_b = offset_ptr(w->w13_b, off); r.w2_b = offset_ptr(w->w2_b, off);
+  return r;
+}
+
+}  // namespace
+
+extern "C" {
+
+MOE_API int moe_block_forward(const moe_dims* dims, const moe_weights* w, const uint16_t* h, const uint16_t* gain,
+                              float eps, int32_t T, uint16_t* out, int32_t* ids, float* weights,
+                              float* shared_gate, void* ws, size_t ws_bytes, hipStream_t stream) {
+  int st = validate_block(dims, w, h, gain, eps, T, out, ids, weights, shared_gate, ws);
+  if (st != MOE_OK || T == 0) return st;
+  if (ws_bytes < workspace_bytes(dims, T)) return MOE_ERR_WORKSPACE;
+  return launch_block(dims, w, h, gain, eps, T, out, ids, weights, shared_gate, ws, stream);
+}
+
+MOE_API size_t moe_layers_workspace_bytes(const moe_dims* dims, int32_t T, int32_t L) {
+  if (check_dims(dims, T) != MOE_OK || L < 1 || L > kMaxLayers) return 0;
+  return layers_workspace_bytes(dims, T, L);
+}
+
+MOE_API int moe_layers_forward(const moe_dims* dims, const moe_weights* w, const uint16_t* gain, int64_t layer_stride,
+                               int32_t L, float eps, const uint16_t* h, int32_t T, uint16_t* out, void* ws,
+                               size_t ws_bytes, hipStream_t stream) {
+  int st = validate_block(dims, w, h, gain, eps, T, out, nullptr, nullptr, nullptr, ws);
+  if (st != MOE_OK) return st;
+  if (L < 1 || L > kMaxLayers) return MOE_ERR_SHAPE;
+  if (layer_stride % 16 != 0) return MOE_ERR_ALIGN;
+  if (T == 0) return MOE_OK;
+  if (ws_bytes < layers_workspace_bytes(dims, T, L)) return MOE_ERR_WORKSPACE;
+  if (use_decode(dims, T))
+    return run_decode(dims, w, h, T, out, L > 1 ? DEC_LAYERS : DEC_BLOCK, nullptr, nullptr, nullptr, nullptr, nullptr,
+                      ws, stream, gain, eps, L, layer_stride);
+  // grouped-GEMM path: one sub-block launch per layer; layer l writes out when
+  // L - 1 - l is even and the buffer after the workspace otherwise, so no
+  // layer reads and writes the same rows
+  Carve c{static_cast<char*>(ws)};
+  ChunkArgs scratch{};
+  carve_chunk(dims, T, c, scratch);
+  uint16_t* buf = c.take<uint16_t>((size_t)T * dims->hidden * 2);
+  const uint16_t* in = h;
+  for (int l = 0; l < L; ++l) {
+    const long long off = layer_stride * l;
+    const moe_weights wl = layer_weights(w, off);
+    uint16_t* dst = ((L - 1 - l) % 2 == 0) ? out : buf;
+    st = launch_block(dims, &wl, in, offset_ptr(gain, off), eps, T, dst, nullptr, nullptr, nullptr, ws, stream);
+    if (st != MOE_OK) return st;
+    in = dst;
+  }
+  return MOE_OK;
 }
 
 }  // extern "C"

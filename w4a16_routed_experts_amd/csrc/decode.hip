@@ -118,6 +118,27 @@ __device__ __forceinline__ bool wave_poll(const uint64_t* w, int n, uint32_t tag
   return ok;
 }
 
+// the arguments of layer l: every weight and gain array l strides on, the
+// layer's own tagged zones
+__device__ __forceinline__ DecodeArgs layer_args(const DecodeArgs& a0, int l) {
+  DecodeArgs a = a0;
+  if (l == 0) return a;
+  const long long off = a0.lstride * l;
+  auto mv = [off](auto* ptr) {
+    using P = decltype(ptr);
+    return ptr ? reinterpret_cast<P>(reinterpret_cast<uintptr_t>(ptr) + off) : ptr;
+  };
+  a.router_q = mv(a0.router_q); a.router_s = mv(a0.router_s);
+  a.w13_q = mv(a0.w13_q); a.w13_s = mv(a0.w13_s);
+  a.w2_q = mv(a0.w2_q); a.w2_s = mv(a0.w2_s);
+  a.sh13_q = mv(a0.sh13_q); a.sh13_s = mv(a0.sh13_s);
+  a.sh2_q = mv(a0.sh2_q); a.sh2_s = mv(a0.sh2_s);
+  a.w13_b = mv(a0.w13_b); a.w2_b = mv(a0.w2_b);
+  a.gain = mv(a0.gain);
+  a.tagged = a0.tagged + (size_t)l * a0.p.z_words;
+  return a;
+}
+
 // ------------------------------------------------------------------ kernel
 
 // HC, IC, ISC: compile-time H, I, Is (0: taken from the plan); TT: most tokens
@@ -128,28 +149,13 @@ __device__ __forceinline__ bool wave_poll(const uint64_t* w, int n, uint32_t tag
 // only in the generic instances.  CB: column batches of the gate/up rows in
 // flight per wave; DB: row batches of the down rows prefetched per wave.
 template <int MODE, int HC, int IC, int ISC, int TT, bool AFF>
-__global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
+__device__ __forceinline__ void decode_layer(const DecodeArgs& a0, int l, int L) {
   extern __shared__ uint4 smem_raw[];
-  const DecodePlan& p = a.p;
-  const int H = HC ? HC : p.H;
-  const int I = IC ? IC : p.I;
-  const int Is = ISC ? ISC : p.Is;
   constexpr int CPL8H = HC ? (HC / 1024 > 1 ? HC / 1024 : 1) : 4;  // int8 rows of H
   constexpr int CPL4H = HC ? (HC / 2048 > 1 ? HC / 2048 : 1) : 2;  // int4 rows of H
   constexpr int CPL4I = IC ? (IC / 2048 > 1 ? IC / 2048 : 1) : 2;  // int4 rows of I
   constexpr int CB = HC ? 2 : 1;
   constexpr int DB = HC ? 2 : 1;
-  const int T = p.T, E = p.E, k = p.k, nb = p.nb, nj = p.nj;
-  const int S = p.S, sw = p.sw;
-
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int b = blockIdx.x, g = b % kGroups, j = b / kGroups;
-
-  _Float16* act = reinterpret_cast<_Float16*>(smem_raw);  // [T][H]
-  _Float16* hq = act + (size_t)T * H;                     // [npg][I] the group's routed h
-  _Float16* hs = hq + (size_t)p.npg * I;                  // [T][sw] the group's shared slice
-  float* xsum = reinterpret_cast<float*>(hs + (size_t)T * sw);  // AFF: [T][H/32] chunk sums of act
-  float* hsum = xsum + (size_t)T * (H / 32);                    // AFF: [npg][I/32] chunk sums of hq
   __shared__ int s_ids[kDecMaxT][kMaxTopK];
   __shared__ float s_w[kDecMaxT][kMaxTopK];
   __shared__ TopkScratch s_topk[kDecMaxT];
@@ -159,9 +165,34 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
   __shared__ float s_part[kDecMaxT][kMaxGroupWgs];  // this block's output rows, per token
   __shared__ uint32_t s_tag;
   __shared__ int s_bad;
-  __shared__ int s_last[kDecMaxT];
-  __shared__ __attribute__((aligned(16))) _Float16 s_gain[MODE == DEC_BLOCK ? kMaxHidden : 8];
+  constexpr bool BLK = MODE == DEC_BLOCK || MODE == DEC_LAYERS;  // RMSNorm in front, residual after
+  __shared__ __attribute__((aligned(16))) _Float16 s_gain[BLK ? kMaxHidden : 8];
   __shared__ float s_rn[kDecMaxT];
+  // With several layers, the indices are taken anew in every layer through
+  // empty asm statements: otherwise the compiler hoists the body's index and
+  // address arithmetic out of the loop and keeps it in registers across the
+  // whole body.
+  int tid_ = threadIdx.x, b_ = blockIdx.x;
+  if (MODE == DEC_LAYERS) {
+    asm volatile("" : "+v"(tid_));
+    asm volatile("" : "+s"(b_));
+  }
+  const DecodeArgs al = MODE == DEC_LAYERS ? layer_args(a0, l) : DecodeArgs{};
+  const DecodeArgs& a = MODE == DEC_LAYERS ? al : a0;
+  const DecodePlan& p = a.p;
+  const int H = HC ? HC : p.H;
+  const int I = IC ? IC : p.I;
+  const int Is = ISC ? ISC : p.Is;
+  const int T = p.T, E = p.E, k = p.k, nb = p.nb, nj = p.nj;
+  const int S = p.S, sw = p.sw;
+  const int tid = tid_, wave = tid >> 6, lane = tid & 63;
+  const int b = b_, g = b % kGroups, j = b / kGroups;
+  _Float16* act = reinterpret_cast<_Float16*>(smem_raw);  // [T][H]
+  _Float16* hq = act + (size_t)T * H;                     // [npg][I] the group's routed h
+  _Float16* hs = hq + (size_t)p.npg * I;                  // [T][sw] the group's shared slice
+  float* xsum = reinterpret_cast<float*>(hs + (size_t)T * sw);  // AFF: [T][H/32] chunk sums of act
+  float* hsum = xsum + (size_t)T * (H / 32);                    // AFF: [npg][I/32] chunk sums of hq
+  uint64_t* const zx_prev = l > 0 ? a.tagged - p.z_words + p.z_x : nullptr;  // the previous layer's output
   uint64_t* const zl = a.tagged + p.z_logits;
   uint64_t* const zr = a.tagged + p.z_route;
   uint64_t* const zs = a.tagged + p.z_hs;
@@ -192,7 +223,7 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
       fs.load(rows, srow, g8h, base);
     }
   }
-  if (tid == 0) {
+  if (tid == 0 && l == 0) {
     // join this call: the additions of one call to each group counter sum to kJoinQuantum
     const uint64_t add = j == 0 ? kJoinQuantum - (uint64_t)(nj - 1) : 1u;
     const uint64_t before = __hip_atomic_fetch_add(reinterpret_cast<uint64_t*>(a.sync + kJoinWord + kSyncStride * g),
@@ -200,14 +231,28 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
     s_tag = (uint32_t)(before / kJoinQuantum) + 1u;
     s_bad = 0;
   }
-  copy_halves(act, a.x, T * H);
-  if (MODE == DEC_BLOCK) copy_halves(s_gain, a.gain, H);
+  if (l == 0) {
+    copy_halves(act, a.x, T * H);
+  } else {
+    // the previous layer's output, once its reducers have published all of it
+    // (the tag is read in a barrier-ordered copy: s_tag was set before layer 0's barrier)
+    const uint32_t tg = s_tag;
+    const int n = T * H;
+    for (int base = wave * 64 * 4; base < n; base += 256 * 4) {
+      const bool ok = wave_poll<4>(zx_prev + base, min(256, n - base), tg, give_up, [](int i) { return i; },
+                                   [&](int, int i, uint64_t w) {
+                                     act[base + i] = __builtin_bit_cast(_Float16, (uint16_t)w);
+                                   });
+      if (!ok && lane == 0) s_bad = 1;
+    }
+  }
+  if (BLK) copy_halves(s_gain, a.gain, H);
   __syncthreads();
   const uint32_t tag = s_tag;
-  // DEC_BLOCK (the Chimera notebook, sections 7 and 10: post-attention RMSNorm
+  // DEC_BLOCK, DEC_LAYERS (the Chimera notebook, sections 7 and 10: post-attention RMSNorm
   // in front of the block, residual after it): wave t sums token t's squares
   // in a fixed order, so every block derives the same binary16 activations.
-  if (MODE == DEC_BLOCK) {
+  if (BLK) {
     if (wave < T) {
       const h8* row = reinterpret_cast<const h8*>(act + (size_t)wave * H);
       float ss = 0.f;
@@ -589,70 +634,74 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
       }
     }
     if (mine) {
-      float sum = MODE == DEC_BLOCK ? half_bits_to_float(a.x[(size_t)t * H + n]) : 0.f;
+      // DEC_BLOCK, DEC_LAYERS: the residual stream (layer l >= 1: the previous layer's
+      // output, whose words this block has already seen complete)
+      float sum = 0.f;
+      if (BLK)
+        sum = half_bits_to_float(l == 0 ? a.x[(size_t)t * H + n] : (uint16_t)get_tagged(zx_prev + (size_t)t * H + n));
 #pragma unroll
       for (int gg = 0; gg < kGroups; ++gg) sum += word_f(v[gg]);
-      a.out[(size_t)t * H + n] = __builtin_bit_cast(uint16_t, (_Float16)(ok ? sum : __builtin_nanf("")));
+      const uint16_t o = __builtin_bit_cast(uint16_t, (_Float16)(ok ? sum : __builtin_nanf("")));
+      if (l == L - 1) a.out[(size_t)t * H + n] = o;
+      else put_tagged(a.tagged + p.z_x + (size_t)t * H + n, tag, o);
     }
     if (!ok && lane == 0) s_bad = 1;
   }
   __syncthreads();
-  if (tid == 0 && s_bad)
-    __hip_atomic_fetch_add(a.sync + kGiveUpWord, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (l == L - 1 && threadIdx.x == 0 && s_bad)
+    __hip_atomic_fetch_add(a0.sync + kGiveUpWord, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+template <int MODE, int HC, int IC, int ISC, int TT, bool AFF>
+__global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a0) {
+  // DEC_LAYERS applies L sub-blocks in turn (the Chimera notebook, "Pipeline":
+  // every layer's weights at one fixed offset from the previous layer's); a
+  // layer's output reaches every block of the next one through the tagged
+  // words of its x zone.  The other modes run one layer.
+  if (MODE == DEC_LAYERS) {
+    for (int l = 0; l < a0.L; ++l) decode_layer<MODE, HC, IC, ISC, TT, AFF>(a0, l, a0.L);
+  } else {
+    decode_layer<MODE, HC, IC, ISC, TT, AFF>(a0, 0, 1);
+  }
 }
 
 // ------------------------------------------------------------------ host side
 
 bool decode_real_widths(int H, int I, int Is) { return H == 2048 && I == 512 && Is == 512; }
 
+// the kernel instance of a mode and widths for a variant (decode_variant)
 template <int MODE, int HC, int IC, int ISC>
-static int occupancy_of(int variant, size_t lds) {
-  int n = 0;
-  hipError_t err;
+static const void* kernel_of(int variant) {
   switch (variant) {
-    case 0: err = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_kernel<MODE, HC, IC, ISC, 1, false>, 256, lds); break;
-    case 1: err = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_kernel<MODE, HC, IC, ISC, kDecMaxT, false>, 256, lds); break;
-    case 2: err = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_kernel<MODE, HC, IC, ISC, 1, true>, 256, lds); break;
-    default: err = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_kernel<MODE, HC, IC, ISC, kDecMaxT, true>, 256, lds); break;
+    case 0: return reinterpret_cast<const void*>(&decode_kernel<MODE, HC, IC, ISC, 1, false>);
+    case 1: return reinterpret_cast<const void*>(&decode_kernel<MODE, HC, IC, ISC, kDecMaxT, false>);
+    case 2: return reinterpret_cast<const void*>(&decode_kernel<MODE, HC, IC, ISC, 1, true>);
+    default: return reinterpret_cast<const void*>(&decode_kernel<MODE, HC, IC, ISC, kDecMaxT, true>);
   }
-  return err == hipSuccess ? n : 0;
 }
 
 template <int MODE>
-static int occupancy(bool real, int variant, size_t lds) {
-  return real ? occupancy_of<MODE, 2048, 512, 512>(variant, lds) : occupancy_of<MODE, 0, 0, 0>(variant, lds);
+static const void* kernel_of(bool real, int variant) {
+  return real ? kernel_of<MODE, 2048, 512, 512>(variant) : kernel_of<MODE, 0, 0, 0>(variant);
+}
+
+static const void* kernel_of(int mode, bool real, int variant) {
+  if (mode == DEC_BLOCK) return kernel_of<DEC_BLOCK>(real, variant);
+  if (mode == DEC_LAYERS) return kernel_of<DEC_LAYERS>(real, variant);
+  return mode == DEC_FORWARD ? kernel_of<DEC_FORWARD>(real, variant) : kernel_of<DEC_EXPERTS>(real, variant);
 }
 
 int decode_blocks_per_cu(int mode, bool real, int variant, size_t lds_bytes) {
-  if (mode == DEC_BLOCK) return occupancy<DEC_BLOCK>(real, variant, lds_bytes);
-  return mode == DEC_FORWARD ? occupancy<DEC_FORWARD>(real, variant, lds_bytes)
-                             : occupancy<DEC_EXPERTS>(real, variant, lds_bytes);
+  int n = 0;
+  const hipError_t err = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kernel_of(mode, real, variant), 256, lds_bytes);
+  return err == hipSuccess ? n : 0;
 }
 
-template <int MODE, int HC, int IC, int ISC>
-static void launch_mode(const DecodeArgs& a, size_t lds_bytes, hipStream_t s) {
-  const dim3 grid(a.p.nb), block(256);
-  switch (decode_variant(a.p.T, a.affine != 0)) {
-    case 0: hipLaunchKernelGGL((decode_kernel<MODE, HC, IC, ISC, 1, false>), grid, block, lds_bytes, s, a); break;
-    case 1: hipLaunchKernelGGL((decode_kernel<MODE, HC, IC, ISC, kDecMaxT, false>), grid, block, lds_bytes, s, a); break;
-    case 2: hipLaunchKernelGGL((decode_kernel<MODE, HC, IC, ISC, 1, true>), grid, block, lds_bytes, s, a); break;
-    default: hipLaunchKernelGGL((decode_kernel<MODE, HC, IC, ISC, kDecMaxT, true>), grid, block, lds_bytes, s, a); break;
-  }
-}
-
-int launch_decode(const DecodeArgs& a, int mode, size_t lds_bytes, hipStream_t s) {
-  const bool real = decode_real_widths(a.p.H, a.p.I, a.p.Is);
-  if (mode == DEC_FORWARD) {
-    if (real) launch_mode<DEC_FORWARD, 2048, 512, 512>(a, lds_bytes, s);
-    else launch_mode<DEC_FORWARD, 0, 0, 0>(a, lds_bytes, s);
-  } else if (mode == DEC_BLOCK) {
-    if (real) launch_mode<DEC_BLOCK, 2048, 512, 512>(a, lds_bytes, s);
-    else launch_mode<DEC_BLOCK, 0, 0, 0>(a, lds_bytes, s);
-  } else {
-    if (real) launch_mode<DEC_EXPERTS, 2048, 512, 512>(a, lds_bytes, s);
-    else launch_mode<DEC_EXPERTS, 0, 0, 0>(a, lds_bytes, s);
-  }
-  return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_LAUNCH;
+int launch_decode(const DecodeArgs& a, int mode, bool real, size_t lds_bytes, hipStream_t s) {
+  if (real && (!decode_real_widths(a.p.H, a.p.I, a.p.Is) || a.p.nj != kMaxGroupWgs)) return MOE_ERR_LAUNCH;
+  const void* k = kernel_of(mode, real, decode_variant(a.p.T, a.affine != 0));
+  void* args[] = {const_cast<DecodeArgs*>(&a)};
+  return hipLaunchKernel(k, dim3(a.p.nb), dim3(256), args, lds_bytes, s) == hipSuccess ? MOE_OK : MOE_ERR_LAUNCH;
 }
 
 }  // namespace moe

@@ -12,8 +12,11 @@ static constexpr int kCounterPages = 2;   // words [0, 2048) of the sync area: p
 static constexpr int kFlagPage = 1024;    // words per page
 static constexpr int kSyncBytes = (kCounterPages + 8) * kFlagPage * 4;  // 40 KiB, zero between calls
 static constexpr int kMaxHidden = 4096;   // widest admitted hidden size
-enum { DEC_FORWARD = 0, DEC_EXPERTS = 1, DEC_BLOCK = 2 };  // DEC_BLOCK: the forward with RMSNorm and residual
-static constexpr int kDecModes = 3;
+static constexpr int kMaxLayers = 256;    // sub-blocks per call at most (moe_layers_forward)
+// DEC_BLOCK: the forward with RMSNorm in front and the residual after;
+// DEC_LAYERS: DEC_BLOCK applied to L layers in turn
+enum { DEC_FORWARD = 0, DEC_EXPERTS = 1, DEC_BLOCK = 2, DEC_LAYERS = 3 };
+static constexpr int kDecModes = 4;
 
 // Sync-area words used by the few-token path (the grouped-GEMM path uses the
 // word at kCounterPages * kFlagPage - kSyncStride).
@@ -37,7 +40,8 @@ struct DecodePlan {
   size_t z_hs;      // [8][T][sw] shared SwiGLU activations of each slice
   size_t z_h;       // [8][npg][I] routed SwiGLU activations of each group's pairs
   size_t z_part;    // [8][T][H] each group's partial output rows
-  size_t z_words;   // total tagged words
+  size_t z_x;       // [T][H] the layer's output (binary16 bits), read by every block of the next layer
+  size_t z_words;   // tagged words of one layer (each layer of a call has its own zones)
 };
 
 __host__ __device__ inline DecodePlan decode_plan(int H, int E, int k, int I, int Is, int T, int nb) {
@@ -60,6 +64,8 @@ __host__ __device__ inline DecodePlan decode_plan(int H, int E, int k, int I, in
   p.z_h = o; o += (size_t)kGroups * p.npg * I;
   o = (o + 15) / 16 * 16;
   p.z_part = o; o += (size_t)kGroups * T * H;
+  o = (o + 15) / 16 * 16;
+  p.z_x = o; o += (size_t)T * H;
   p.z_words = (o + 15) / 16 * 16;
   return p;
 }
@@ -80,15 +86,17 @@ struct DecodeArgs {
   const int8_t* sh2_q; const uint16_t* sh2_s;
   const uint16_t* x;
   uint16_t* out;
-  const uint16_t* gain;  // DEC_BLOCK: RMSNorm gain [H] (x is the residual stream)
-  float eps;             // DEC_BLOCK: RMSNorm epsilon
+  const uint16_t* gain;  // DEC_BLOCK, DEC_LAYERS: RMSNorm gain [H] (x is the residual stream)
+  float eps;             // DEC_BLOCK, DEC_LAYERS: RMSNorm epsilon
   int32_t* ids_out; float* w_out; float* sigma_out;  // nullable
   const int32_t* ids_in; const float* w_in;          // routing given by the caller
   uint32_t* sync;        // the workspace's sync area (kSyncBytes)
-  uint64_t* tagged;      // tagged zones (plan.z_words words)
+  uint64_t* tagged;      // tagged zones (L x plan.z_words words)
   int give_up;           // nonzero: every bounded wait gives up at once (exercises the failure path)
   int affine;            // routed experts are affine int4 (unsigned codes, w = q s + b)
   const uint16_t* w13_b; const uint16_t* w2_b;  // affine: per-group binary16 offsets
+  int L;                 // DEC_LAYERS: sub-blocks applied in turn (1 otherwise)
+  long long lstride;     // bytes from one layer's weight (and gain) arrays to the next layer's
   DecodePlan p;
 };
 
@@ -97,7 +105,10 @@ struct DecodeArgs {
 static constexpr int kDecVariants = 4;
 __host__ __device__ inline int decode_variant(int T, bool affine) { return (T == 1 ? 0 : 1) + (affine ? 2 : 0); }
 int decode_blocks_per_cu(int mode, bool real_widths, int variant, size_t lds_bytes);
-int launch_decode(const DecodeArgs& a, int mode, size_t lds_bytes, hipStream_t s);
+// real: the instance built for H = 2048, I = Is = 512, which needs
+// p.nj == kMaxGroupWgs (it has no loop for a second router row or shared
+// column per member)
+int launch_decode(const DecodeArgs& a, int mode, bool real, size_t lds_bytes, hipStream_t s);
 bool decode_real_widths(int H, int I, int Is);
 
 }  // namespace moe
