@@ -25,7 +25,12 @@
  *     the low nibble of byte j, element 2j+1 the high nibble;
  *   - int8 code: two's complement;
  *   - scales: IEEE binary16 bit patterns, one per 64 consecutive K elements of
- *     a row ([rows][K/64]); dequantised weight = code * scale (no zero point);
+ *     a row ([rows][K/64]); dequantised weight = code * scale (no zero point).
+ *     Every dequantised weight must be a finite binary16 value (|code * scale|
+ *     <= 65504).  The few-token path and the router GEMM apply scales in fp32;
+ *     the grouped expert GEMMs round each dequantised weight to binary16 before
+ *     the matrix core (relative error <= 2^-11, or an absolute error <= 2^-25
+ *     for weights under 2^-14 in magnitude, which binary16 holds as subnormals);
  *   - activations x and out: IEEE binary16 [T][H].
  *
  * Conventions for every entry point:
@@ -104,6 +109,11 @@ extern "C" {
  * (w13_s, w2_s) and a binary16 offset b (w13_b, w2_b):  w = q * s + b.
  * The router and the shared expert keep their symmetric int8 form. */
 #define MOE_FMT_AFFINE4 0x200u
+/* dims.flags bit for moe_block_forward and moe_layers_forward: `gain` holds w
+ * and the norm multiplies by (1 + w), formed in fp32 (the form of the
+ * published Qwen3.5-MoE RMSNorm, whose weight is stored as w).  Without it
+ * `gain` is the multiplier as applied.  Other entry points ignore it. */
+#define MOE_NORM_GAIN_PLUS_ONE 0x400u
 
 typedef struct {
   int32_t hidden;       /* H */
@@ -112,7 +122,7 @@ typedef struct {
   int32_t expert_inter; /* I: routed-expert intermediate width */
   int32_t shared_inter; /* Is: shared-expert intermediate width */
   int32_t group;        /* G: quantisation group along K, must be 64 */
-  uint32_t flags;       /* MOE_PATH_*, optionally | MOE_FMT_AFFINE4 | MOE_DEBUG_WAIT_GIVE_UP */
+  uint32_t flags;       /* MOE_PATH_*, optionally | MOE_FMT_AFFINE4 | MOE_NORM_GAIN_PLUS_ONE | MOE_DEBUG_WAIT_GIVE_UP */
 } moe_dims;
 
 typedef struct {
@@ -168,8 +178,8 @@ MOE_API int moe_forward(const moe_dims* dims, const moe_weights* w, const uint16
  *   out[t] = binary16( h[t] + moe_forward's block applied to a[t] )
  * with one rounding of out.
  *   h     [T][H] binary16, the residual stream (16-byte aligned; must not alias out)
- *   gain  [H] binary16, the norm's multiplier as applied (16-byte aligned); a
- *         model that stores w for a (1 + w) multiplier passes 1 + w
+ *   gain  [H] binary16, the norm's multiplier as applied (16-byte aligned), or
+ *         w of a (1 + w) multiplier with MOE_NORM_GAIN_PLUS_ONE
  *   eps   finite, >= 0; anything else is refused with MOE_ERR_SHAPE
  * ids, weights and shared_gate receive the routing of a[t] when non-NULL, as
  * for moe_forward. */

@@ -260,24 +260,26 @@ def f64_to_half_bits(v) -> np.ndarray:
     return np.asarray(v, dtype=np.float64).astype(np.float16).view(np.uint16)
 
 
-def rmsnorm(h_bits, gain_bits, eps: float) -> np.ndarray:
+def rmsnorm(h_bits, gain_bits, eps: float, plus_one: bool = False) -> np.ndarray:
     """Post-attention RMSNorm (the Chimera notebook, sections 7 and 10: the
     norm in front of the MoE FFN), float64 [T, H]: each token's row divided by
-    the square root of (the mean of its squares + eps), times the gain vector."""
+    the square root of (the mean of its squares + eps), times the gain vector.
+    plus_one: the stored vector is w and the gain is 1 + w (the form of the
+    published Qwen3.5-MoE norm)."""
     X = half_bits_to_f64(h_bits)
-    g = half_bits_to_f64(gain_bits)
+    g = half_bits_to_f64(gain_bits) + (1.0 if plus_one else 0.0)
     ms = np.mean(X * X, axis=1, keepdims=True)
     return X / np.sqrt(ms + eps) * g
 
 
-def block_forward(h_bits, gain_bits, eps: float, W, dims):
+def block_forward(h_bits, gain_bits, eps: float, W, dims, plus_one: bool = False):
     """The MoE sub-block (same sections: post-attn RMSNorm -> MoE FFN ->
     residual): a = binary16(rmsnorm(h)), out = h + forward(a)["out"].
 
     Returns forward's dict with out replaced by the sub-block's output, the
     block's own output as moe, and the normalised activations as a_bits.
     """
-    a_bits = f64_to_half_bits(rmsnorm(h_bits, gain_bits, eps))
+    a_bits = f64_to_half_bits(rmsnorm(h_bits, gain_bits, eps, plus_one))
     r = forward(a_bits, W, dims)
     r["moe"] = r["out"]
     r["out"] = half_bits_to_f64(h_bits) + r["moe"]
@@ -285,7 +287,7 @@ def block_forward(h_bits, gain_bits, eps: float, W, dims):
     return r
 
 
-def layers_forward(h_bits, gain_bits_per_layer, eps: float, W_per_layer, dims) -> np.ndarray:
+def layers_forward(h_bits, gain_bits_per_layer, eps: float, W_per_layer, dims, plus_one: bool = False) -> np.ndarray:
     """Several MoE sub-blocks applied in turn (the Chimera notebook,
     "Pipeline": the decoder's layers run one after another inside one kernel
     per token).  Reading: each layer's output is stored as binary16 before the
@@ -295,6 +297,6 @@ def layers_forward(h_bits, gain_bits_per_layer, eps: float, W_per_layer, dims) -
     h = np.asarray(h_bits)
     out = None
     for gain_bits, W in zip(gain_bits_per_layer, W_per_layer):
-        out = block_forward(h, gain_bits, eps, W, dims)["out"]
+        out = block_forward(h, gain_bits, eps, W, dims, plus_one)["out"]
         h = f64_to_half_bits(out)
     return out

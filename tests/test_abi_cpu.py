@@ -88,7 +88,7 @@ def test_refusals_forward(L):
     assert _forward(L, _dims(E=4, k=8), W) == -2
     assert _forward(L, _dims(I=96), W) == -2
     assert _forward(L, _dims(flags=7), W) == -2
-    assert _forward(L, _dims(flags=0x400), W) == -2                 # an unknown flag bit
+    assert _forward(L, _dims(flags=0x800), W) == -2                 # an unknown flag bit
     assert _forward(L, _dims(flags=0x103), W) == -2                 # an unknown path with the debug bit
     assert _forward(L, d, W, T=-1) == -2
     assert _forward(L, _dims(flags=m.PATH_DECODE), W, T=5) == -2  # few-token path holds at most 4 tokens

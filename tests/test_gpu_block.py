@@ -56,9 +56,9 @@ def _run_block(case, h_bits, gain_bits, flags):
                 sigma=sig.cpu().numpy().astype(np.float64))
 
 
-def _check(case, h_bits, gain_bits, gpu, label):
+def _check(case, h_bits, gain_bits, gpu, label, plus_one=False):
     d = case.dims
-    r = ref.block_forward(h_bits, gain_bits, EPS, case.weights, d)
+    r = ref.block_forward(h_bits, gain_bits, EPS, case.weights, d, plus_one=plus_one)
     differ = _gpu.check_routing(case, r, gpu, label)
     want = r["out"].copy()
     lr = r["logits"][:, : d.E]
@@ -105,3 +105,32 @@ def test_block_other_widths(shape, T, flags):
     h_bits, gain_bits = _inputs(case, 7400 + H + T)
     gpu = _run_block(case, h_bits, gain_bits, flags)
     _check(case, h_bits, gain_bits, gpu, f"block-{shape}-T{T}-f{flags}")
+
+
+@pytest.mark.parametrize("T,flags", [(3, m.PATH_DECODE), (40, m.PATH_CHUNK)])
+def test_block_gain_plus_one(T, flags):
+    """MOE_NORM_GAIN_PLUS_ONE: the gain array holds w and the norm multiplies by
+    1 + w formed in fp32 (w here is small, so 1 + w would lose most of its bits
+    if rounded to binary16 first)."""
+    case = gen.make_case(gen.REAL, T, seed=9300 + T, real_experts=True)
+    rng = np.random.default_rng(9301 + T)
+    h_bits = f16_bits(gen_x(case) * rng.uniform(0.5, 3.0, size=(T, 1)))
+    w_bits = f16_bits(rng.uniform(-0.02, 0.02, size=case.dims.H))
+    gpu = _run_block(case, h_bits, w_bits, flags | m.NORM_GAIN_PLUS_ONE)
+    _check(case, h_bits, w_bits, gpu, f"block (1 + w) T{T}", plus_one=True)
+    # without the flag the same array is the gain itself: a different result
+    other = _run_block(case, h_bits, w_bits, flags)
+    assert _gpu.row_rel_l2(other["out"], gpu["out"]).max() > 0.1
+
+
+@pytest.mark.parametrize("T,flags", [(3, m.PATH_DECODE), (40, m.PATH_CHUNK)])
+def test_block_residual_in_the_thousands(T, flags):
+    """A residual stream with elements in the thousands: the norm's sums of
+    squares and the residual add stay exact enough on both paths."""
+    case = gen.make_case(gen.REAL, T, seed=9400 + T, real_experts=True)
+    rng = np.random.default_rng(9401 + T)
+    h_bits = f16_bits(gen_x(case) * rng.uniform(256.0, 1024.0, size=(T, 1)))
+    gain_bits = f16_bits(rng.uniform(0.5, 1.5, size=case.dims.H))
+    assert np.abs(ref.half_bits_to_f64(h_bits)).max() > 1000.0
+    gpu = _run_block(case, h_bits, gain_bits, flags)
+    _check(case, h_bits, gain_bits, gpu, f"block large residual T{T}")

@@ -95,3 +95,27 @@ def test_path_boundary(T):
     r = ref.forward(case.x, case.weights, case.dims)
     g = _gpu.run_forward(case, flags=m.PATH_AUTO)
     _gpu.check_forward(case, r, g, f"boundary-T{T}")
+
+
+def _near_max_case(T, seed):
+    """Shared-expert down weights |code x scale| up to about 41600 (the largest
+    binary16 is 65504) and outputs in the tens of thousands, with small
+    activations: x divided by 11, and the router and routed gate/up scales
+    multiplied by 11 so routing and the routed half are as in the unscaled case."""
+    from dataclasses import replace
+    case = gen.make_case(gen.REAL, T, seed=seed, real_experts=True)
+    W = case.weights
+    f = lambda b: b.view(np.float16).astype(np.float64)  # noqa: E731
+    W2 = replace(W, router_s=gen.f16_bits(f(W.router_s) * 11), w13_s=gen.f16_bits(f(W.w13_s) * 11),
+                 sh2_s=gen.f16_bits(f(W.sh2_s) * 2.0 ** 18))
+    return replace(case, name=f"near_max_T{T}", weights=W2, x=gen.f16_bits(f(case.x) / 11))
+
+
+@pytest.mark.parametrize("T,flags", [(3, m.PATH_DECODE), (40, m.PATH_CHUNK), (3, m.PATH_CHUNK)])
+def test_weights_and_outputs_near_binary16_max(T, flags):
+    case = _near_max_case(T, 9500 + T)
+    r = ref.forward(case.x, case.weights, case.dims)
+    sh2 = ref.dequant(case.weights.sh2_q, case.weights.sh2_s, case.dims.G)
+    assert np.abs(sh2).max() > 30000.0 and 10000.0 < np.abs(r["out"]).max() < 65504.0
+    g = _gpu.run_forward(case, flags=flags)
+    _gpu.check_forward(case, r, g, f"near binary16 max T{T} f{flags}")

@@ -131,6 +131,27 @@ def test_rmsnorm_matches_transformers(H):
     assert np.mean(a == b) > 0.95  # almost every element rounds identically
 
 
+@pytest.mark.parametrize("H", [256, 2048])
+def test_rmsnorm_plus_one_matches_transformers(H):
+    """The oracle's (1 + w) form takes w as stored (transformers' weight) and
+    agrees with Qwen3_5MoeRMSNorm to within one binary16 ulp, also for small w
+    whose 1 + w binary16 cannot hold."""
+    rng = np.random.default_rng(H + 1)
+    h_bits = gen.f16_bits(rng.normal(0.0, 3.0, size=(5, H)))
+    w_bits = gen.f16_bits(rng.uniform(-0.02, 0.02, size=H))
+    eps = 1e-6
+    norm = qmoe.Qwen3_5MoeRMSNorm(H, eps=eps)
+    with torch.no_grad():
+        norm.weight.data = torch.from_numpy(ref.half_bits_to_f64(w_bits).astype(np.float32))
+        hf = norm(torch.from_numpy(h_bits.view(np.float16))).numpy().astype(np.float64)
+    ours = ref.f64_to_half_bits(ref.rmsnorm(h_bits, w_bits, eps, plus_one=True)).view(np.float16).astype(np.float64)
+    ulp = np.spacing(np.abs(ours).astype(np.float16)).astype(np.float64)
+    assert np.all(np.abs(hf - ours) <= ulp)
+    # read as the gain itself, the same array gives another norm altogether
+    plain = ref.rmsnorm(h_bits, w_bits, eps)
+    assert np.abs(plain - ours).max() > 0.5
+
+
 def test_control_swapped_gate_up_is_caught(monkeypatch):
     """A planted mistake in the oracle (gate and up halves swapped) turns this
     pin red: the comparison with transformers is not blind to it."""

@@ -14,6 +14,7 @@ from .binding import (  # noqa: F401
     PATH_CHUNK,
     DEBUG_WAIT_GIVE_UP,
     FMT_AFFINE4,
+    NORM_GAIN_PLUS_ONE,
     GIVE_UP_WORD_OFFSET,
     lib,
     library_path,

@@ -25,6 +25,7 @@ NOALLOC_SCRATCH_BYTES = 8 << 20
 WEIGHT_FIELDS = ("router_q", "router_s", "w13_q", "w13_s", "w2_q", "w2_s",
                  "sh13_q", "sh13_s", "sh2_q", "sh2_s", "w13_b", "w2_b")
 FMT_AFFINE4 = 0x200  # dims.flags: affine int4 routed experts (unsigned codes, per-group scale and offset)
+NORM_GAIN_PLUS_ONE = 0x400  # dims.flags: the norm gain holds w of a (1 + w) multiplier
 
 
 class MoeDims(ctypes.Structure):

@@ -44,7 +44,7 @@ int check_dims(const moe_dims* d, int32_t T) {
   if (d->top_k < 1 || d->top_k > kMaxTopK || d->top_k > d->num_experts) return MOE_ERR_SHAPE;
   if (!width_ok(d->hidden) || !width_ok(d->expert_inter) || !width_ok(d->shared_inter)) return MOE_ERR_SHAPE;
   if ((d->flags & kPathMask) > MOE_PATH_CHUNK ||
-      (d->flags & ~(kPathMask | MOE_DEBUG_WAIT_GIVE_UP | MOE_FMT_AFFINE4)))
+      (d->flags & ~(kPathMask | MOE_DEBUG_WAIT_GIVE_UP | MOE_FMT_AFFINE4 | MOE_NORM_GAIN_PLUS_ONE)))
     return MOE_ERR_SHAPE;
   if (T < 0 || T > kMaxT) return MOE_ERR_SHAPE;
   return MOE_OK;
@@ -228,6 +228,7 @@ int run_decode(const moe_dims* d, const moe_weights* w, const uint16_t* x, int T
                &a.sh2_s);
   a.x = x; a.out = out;
   a.gain = gain; a.eps = eps;
+  a.gain_add = (d->flags & MOE_NORM_GAIN_PLUS_ONE) ? 1.0f : 0.0f;
   a.ids_out = ids_out; a.w_out = w_out; a.sigma_out = sig_out;
   a.ids_in = ids_in; a.w_in = w_in;
   a.give_up = (d->flags & MOE_DEBUG_WAIT_GIVE_UP) ? 1 : 0;
@@ -475,6 +476,7 @@ int launch_block(const moe_dims* dims, const moe_weights* w, const uint16_t* h, 
   if (shared_gate) a.sigma = shared_gate;
   a.gain = gain;
   a.eps = eps;
+  a.gain_add = (dims->flags & MOE_NORM_GAIN_PLUS_ONE) ? 1.0f : 0.0f;
   a.xa = a.xn;   // the expert GEMMs read the normalised activations the router GEMM writes
   a.resid = h;   // and the combine adds the residual stream
   a.shared_tiles = (T + kSharedRows - 1) / kSharedRows;

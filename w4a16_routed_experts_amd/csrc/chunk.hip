@@ -206,7 +206,7 @@ __global__ __launch_bounds__(64 * kRouterWaves) void router_gemm_kernel(ChunkArg
           const float rn = s_rn[(64 * j + lane) >> 3];
           h8 hv = __builtin_bit_cast(h8, xa[u][j]);
 #pragma unroll
-          for (int i = 0; i < 8; ++i) hv[i] = (_Float16)((float)hv[i] * rn * (float)gv[i]);
+          for (int i = 0; i < 8; ++i) hv[i] = (_Float16)((float)hv[i] * rn * ((float)gv[i] + a.gain_add));
           xa[u][j] = __builtin_bit_cast(u32x4, hv);
           if (gi < ngr) __builtin_amdgcn_raw_buffer_store_b128(xa[u][j], rxn, xoff[j] + 128u * gi, 0, 0);
         }

@@ -21,6 +21,7 @@ struct ChunkArgs {
   uint16_t* out;       // [T][H]
   const uint16_t* gain;  // sub-block: RMSNorm gain [H], or null
   float eps;             // sub-block: RMSNorm epsilon
+  float gain_add;        // sub-block: added to every gain element in fp32 (1: the gain holds w of 1 + w)
   uint16_t* xn;          // sub-block: normalised activations [T][H], written by the router GEMM
   const uint16_t* resid; // sub-block: residual added by the combine, or null
   float* logits;       // [T][E+1]

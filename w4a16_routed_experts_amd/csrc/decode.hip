@@ -271,7 +271,7 @@ __device__ __forceinline__ void decode_layer(const DecodeArgs& a0, int l, int L)
       const h8 gv = reinterpret_cast<const h8*>(s_gain)[c];
       h8 v = *pp;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) v[i] = (_Float16)((float)v[i] * s_rn[t] * (float)gv[i]);
+      for (int i = 0; i < 8; ++i) v[i] = (_Float16)((float)v[i] * s_rn[t] * ((float)gv[i] + a.gain_add));
       *pp = v;
     }
     __syncthreads();

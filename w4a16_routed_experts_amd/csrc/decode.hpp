@@ -88,6 +88,7 @@ struct DecodeArgs {
   uint16_t* out;
   const uint16_t* gain;  // DEC_BLOCK, DEC_LAYERS: RMSNorm gain [H] (x is the residual stream)
   float eps;             // DEC_BLOCK, DEC_LAYERS: RMSNorm epsilon
+  float gain_add;        // added to every gain element in fp32 (1: the gain holds w of 1 + w)
   int32_t* ids_out; float* w_out; float* sigma_out;  // nullable
   const int32_t* ids_in; const float* w_in;          // routing given by the caller
   uint32_t* sync;        // the workspace's sync area (kSyncBytes)
