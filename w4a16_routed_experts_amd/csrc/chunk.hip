@@ -461,7 +461,8 @@ __device__ __forceinline__ void bucket_body(const ChunkArgs& a) {
     }
     for (int st = threadIdx.x; st < a.shared_tiles; st += blockDim.x) {
       const int4 t = shared_tile(st, a.T);
-      a.tiles[atomicAdd(&s_cls[1][t.w], 1)] = t;
+      const int ti = atomicAdd(&s_cls[1][t.w], 1);
+      a.tiles[t.w == top ? top_slot(ti, n_top) : ti] = t;  // the heaviest class's slots follow top_slot
     }
   }
   // stable scatter: position of pair p in expert-major order, with its
@@ -556,7 +557,11 @@ __global__ __launch_bounds__(64 * kTopkBucketWaves) void topk_bucket_kernel(Chun
 // ---------------------------------------------------------------------------
 static constexpr int kKS = 128;
 static constexpr int kAStride = kKS + 8;       // halves per LDS row (padding against bank conflicts)
-static constexpr int kTilePF = 1;  // weight stages in flight in the 32-row-block path (more spills at 256 VGPRs)
+// Weight stages in flight in the 32-row-block path, by row blocks: a tile with
+// fewer rows has less MFMA work per stage to cover a weight fetch with, and
+// smaller accumulators, which leave registers for more stages (128-row tiles
+// have no registers for a second one).
+__host__ __device__ constexpr int tile_pf(int mt) { return mt >= 3 ? 1 : (mt == 2 ? 2 : 3); }
 
 template <int MT>
 struct AStage {
@@ -697,7 +702,7 @@ template <int BITS, int NF, int MT, bool AFF = false>
 __device__ __forceinline__ void tile_gemm(_Float16* lds, const GemmOperands<BITS, NF, MT>& op, int K,
                                           f16v acc[MT][NF]) {
   constexpr int BUF = 32 * MT * kAStride;
-  constexpr int PF = kTilePF;  // weight stages in flight
+  constexpr int PF = tile_pf(MT);  // weight stages in flight
   static_assert(PF >= 1 && PF <= 3, "the stage ring holds four stages");
   const int nst = (K + kKS - 1) / kKS;
   AStage<MT> as;
@@ -1067,7 +1072,12 @@ __global__ __launch_bounds__(256, 2) void up_gemm_kernel(ChunkArgs a) {
     const uint16_t* wsc = a.w13_s + so;
     const uint16_t* wof = AFF ? a.w13_b + so : nullptr;
     switch (mt) {
-      case 4: up_tile<4, 4, AFF>(a, lds, tr, ra, wq, wsc, wof, a.I, jb, a.h, rows); break;
+      case 4:
+        if constexpr (kTileRows >= 128) {
+          up_tile<4, 4, AFF>(a, lds, tr, ra, wq, wsc, wof, a.I, jb, a.h, rows);
+          break;
+        }
+        [[fallthrough]];
       case 3: up_tile<4, 3, AFF>(a, lds, tr, ra, wq, wsc, wof, a.I, jb, a.h, rows); break;
       case 2: up_tile<4, 2, AFF>(a, lds, tr, ra, wq, wsc, wof, a.I, jb, a.h, rows); break;
       case 0:
@@ -1238,7 +1248,12 @@ __global__ __launch_bounds__(256, 2) void down_gemm_kernel(ChunkArgs a) {
     const uint16_t* wsc = a.w2_s + so;
     const uint16_t* wof = AFF ? a.w2_b + so : nullptr;
     switch (mt) {
-      case 4: down_tile<4, 4, AFF>(a, lds, tr, ra, wq, wsc, wof, a.I, nb, a.y, rows, my_row, my_scale); break;
+      case 4:
+        if constexpr (kTileRows >= 128) {
+          down_tile<4, 4, AFF>(a, lds, tr, ra, wq, wsc, wof, a.I, nb, a.y, rows, my_row, my_scale);
+          break;
+        }
+        [[fallthrough]];
       case 3: down_tile<4, 3, AFF>(a, lds, tr, ra, wq, wsc, wof, a.I, nb, a.y, rows, my_row, my_scale); break;
       case 2: down_tile<4, 2, AFF>(a, lds, tr, ra, wq, wsc, wof, a.I, nb, a.y, rows, my_row, my_scale); break;
       case 0:
