@@ -495,11 +495,24 @@ __device__ __forceinline__ void decode_layer(const DecodeArgs& a0, int l, int L)
       for (int u = 0; u < CB; ++u) {
         const float gt = lane_group_sum(acc[u][0], g4h.lpr);
         const float up = lane_group_sum(acc[CB + u][0], g4h.lpr);
-        if (col[u] >= 0 && (lane % g4h.lpr) == 0)
-          put_tagged_f(zh + ((size_t)g * p.npg + q) * I + col[u], tag, s_bad ? __builtin_nanf("") : silu_f(gt) * up);
+        // staged in the LDS rows the gather below fills (with the same binary16 value)
+        if (col[u] >= 0 && (lane % g4h.lpr) == 0) hq[(size_t)q * I + col[u]] = (_Float16)(silu_f(gt) * up);
       }
     }
   }
+  // Publish this member's columns: consecutive lanes write consecutive words,
+  // so each member's run leaves as whole pieces of lines rather than one
+  // 8-byte store per column (single-word stores from several waves took
+  // microseconds longer to become visible).  Then wait for the acknowledgement
+  // of this block's own stores before polling the other members' words.
+  __syncthreads();
+  for (int q = 0; q < np; ++q) {
+    if (s_pe[q] < 0) continue;  // uniform
+    for (int c = c_lo + tid; c < c_hi; c += blockDim.x)
+      put_tagged_f(zh + ((size_t)g * p.npg + q) * I + c, tag,
+                   s_bad ? __builtin_nanf("") : (float)hq[(size_t)q * I + c]);
+  }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
   // ---------------- the group's routed activations (pairs with an expert only:
   // nothing is written for a dropped pair) and its shared slice -> LDS
@@ -615,6 +628,7 @@ __device__ __forceinline__ void decode_layer(const DecodeArgs& a0, int l, int L)
       put_tagged_f(zp + ((size_t)g * T + t) * H + n0 + r, tag, s_bad ? __builtin_nanf("") : s_part[t][r]);
   }
   if (g == j % kGroups) {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this block's own partial sums acknowledged first
     const int t = tid / p.rw, r = tid - t * p.rw, n = n0 + r;
     const bool mine = tid < T * p.rw && n < H;  // T * rw <= 256: one output per thread
     uint64_t v[kGroups];
