@@ -11,9 +11,10 @@
 // p = 8q + g and slice g of the shared expert's intermediate columns, so the
 // hand-off of SwiGLU activations stays among the group's members:
 //   A  router rows (all groups, spread over every block) and the group's
-//      shared gate/up columns                       -> logits, shared h slice
-//   R  one member per group ranks the logits (top-k, renormalised weights,
-//      sigmoid gate) and publishes the group's pairs
+//      shared gate/up columns       -> logits (one copy per group), shared h slice
+//   R  every block ranks the logits in its group's copy (top-k, renormalised
+//      weights, sigmoid gate); the ranking is deterministic, so all blocks
+//      agree on the pairs without a further hand-off
 //   B  the group's pairs: gate/up columns (member j: its share of the I
 //      columns)                                     -> routed h
 //   C  member j: output rows [j rw, (j+1) rw) of the group's partial sum
@@ -24,13 +25,13 @@
 // Hand-offs.  Values pass between blocks as 64-bit words (call tag << 32 |
 // value bits) written and read with device-scope (sc1) atomic accesses; a
 // reader polls the words themselves until every tag equals this call's tag,
-// so no store acknowledgement, counter or flag sits between producer and
-// consumer, and nothing has to be cleared after a call.  The tag is the call
+// so no counter or flag sits between producer and consumer, and nothing has
+// to be cleared after a call.  The tag is the call
 // number: every block adds to its group's 64-bit call counter once, the
 // additions of one call sum to kJoinQuantum, so floor(counter / kJoinQuantum)
 // read by any block of a call is that call's number.  Each polled region is
-// read by few blocks: the logits by the 8 ranking members, a group's pairs
-// and activations by its nj members, a row block's 8 partial sums by one
+// read by the blocks of one group at most: a group's copy of the logits and
+// its activations by its nj members, a row block's 8 partial sums by one
 // block.  A wave that polls waits for every load it has in flight (the load
 // counter is in order), so the big weight loads are issued after the polls
 // that precede them, and loads meant to stay in flight across a poll are held
@@ -194,7 +195,6 @@ __device__ __forceinline__ void decode_layer(const DecodeArgs& a0, int l, int L)
   float* hsum = xsum + (size_t)T * (H / 32);                    // AFF: [npg][I/32] chunk sums of hq
   uint64_t* const zx_prev = l > 0 ? a.tagged - p.z_words + p.z_x : nullptr;  // the previous layer's output
   uint64_t* const zl = a.tagged + p.z_logits;
-  uint64_t* const zr = a.tagged + p.z_route;
   uint64_t* const zs = a.tagged + p.z_hs;
   uint64_t* const zh = a.tagged + p.z_h;
   const bool give_up = a.give_up != 0;
@@ -285,8 +285,10 @@ __device__ __forceinline__ void decode_layer(const DecodeArgs& a0, int l, int L)
 #pragma unroll
       for (int t = 0; t < TT; ++t)
         if (t < T) {
-          const float v = lane_group_sum(acc[0][t], g8h.lpr);
-          if (r_row >= 0 && (lane % g8h.lpr) == 0) put_tagged_f(zl + (size_t)t * (E + 1) + r_row, tag, v);
+          const float v = lane_group_sum(acc[0][t], g8h.lpr);  // in every lane of the row's lanes
+          if (r_row >= 0)
+            for (int c = lane % g8h.lpr; c < kGroups; c += g8h.lpr)
+              put_tagged_f(zl + c * p.zl_copy + (size_t)t * (E + 1) + r_row, tag, v);
         }
     }
     if (wave == 1 && g < S && j < sw) {
@@ -315,7 +317,9 @@ __device__ __forceinline__ void decode_layer(const DecodeArgs& a0, int l, int L)
       for (int t = 0; t < TT; ++t)
         if (t < T) {
           const float v = lane_group_sum(acc[0][t], g8h.lpr);
-          if (r <= E && (lane % g8h.lpr) == 0) put_tagged_f(zl + (size_t)t * (E + 1) + r, tag, v);
+          if (r <= E)
+            for (int c = lane % g8h.lpr; c < kGroups; c += g8h.lpr)
+              put_tagged_f(zl + c * p.zl_copy + (size_t)t * (E + 1) + r, tag, v);
         }
     }
     for (int c0 = j + nj * g8h.rpb; HC == 0 && g < S && c0 < sw; c0 += nj * g8h.rpb) {
@@ -362,63 +366,42 @@ __device__ __forceinline__ void decode_layer(const DecodeArgs& a0, int l, int L)
   // AFF: the offsets multiply the sum of each 32-activation chunk
   if (AFF) chunk_sums(xsum, act, T * (H / 32));
 
-  // ---------------- routing of the group's pairs
+  // ---------------- routing: every block ranks its tokens (wave t: token t, lane
+  // l: experts 4l..4l+3) from its group's copy of the logits
   if (MODE != DEC_EXPERTS) {
-    if (j == nj - 1) {
-      // this group's ranking member: wave t ranks token t (lane l: experts 4l..4l+3)
-      if (wave < T) {
-        const int t = wave;
-        float v[4] = {0.f, 0.f, 0.f, 0.f};
-        float gate = 0.f;
-        const uint64_t* lw = zl + (size_t)t * (E + 1);
-        // word 4 of every lane is the gate logit E; experts at or past E are ignored by the ranking
-        const bool ok = wave_poll<5>(lw, 5 * 64, tag, give_up,
-                                     [&](int i) { return i < 256 ? min(4 * (i % 64) + i / 64, E) : E; },
-                                     [&](int u, int, uint64_t w) {
-                                       if (u < 4) v[u] = word_f(w);
-                                       else gate = word_f(w);
-                                     });
-        if (ok) {
-          wave_topk(v, E, k, s_ids[t], s_w[t], s_topk[t]);
-          if (lane == 0) s_sig[t] = sigmoid_f(gate);
-        } else {
-          if (lane < k) { s_ids[t][lane] = 0; s_w[t][lane] = __builtin_nanf(""); }
-          if (lane == 0) { s_sig[t] = __builtin_nanf(""); s_bad = 1; }
-        }
-      }
-      __syncthreads();
-      for (int q = tid; q < kDecMaxT; q += blockDim.x) {
-        const int pp = kGroups * q + g;
-        s_pe[q] = pp < T * k ? s_ids[pp / k][pp % k] : -1;
-        s_pw[q] = pp < T * k ? s_w[pp / k][pp % k] : 0.f;
-      }
-      // publish the group's pairs and the gates (one line per group)
-      if (tid < 12) {
-        const int q = tid & 3;
-        const int pp = kGroups * q + g;
-        if (tid < 4) put_tagged(zr + 16 * g + tid, tag, (uint32_t)(pp < T * k ? s_ids[pp / k][pp % k] : -1));
-        else if (tid < 8) put_tagged_f(zr + 16 * g + tid, tag, pp < T * k ? s_w[pp / k][pp % k] : 0.f);
-        else put_tagged_f(zr + 16 * g + tid, tag, q < T ? s_sig[q] : 0.f);
-      }
-      if (g == 0) {
-        for (int q = tid; q < T * k; q += blockDim.x) {
-          if (a.ids_out) a.ids_out[q] = s_ids[q / k][q % k];
-          if (a.w_out) a.w_out[q] = s_w[q / k][q % k];
-        }
-        for (int t = tid; t < T; t += blockDim.x)
-          if (a.sigma_out) a.sigma_out[t] = s_sig[t];
-      }
-    } else if (wave == 0) {
-      const bool ok = wave_poll<1>(zr + 16 * g, 12, tag, give_up, [](int i) { return i; },
-                                   [&](int, int i, uint64_t w) {
-                                     if (i < 4) s_pe[i] = (int)(uint32_t)w;
-                                     else if (i < 8) s_pw[i - 4] = word_f(w);
-                                     else s_sig[i - 8] = word_f(w);
+    if (wave < T) {
+      const int t = wave;
+      float v[4] = {0.f, 0.f, 0.f, 0.f};
+      float gate = 0.f;
+      const uint64_t* lw = zl + g * p.zl_copy + (size_t)t * (E + 1);
+      // word 4 of every lane is the gate logit E; experts at or past E are ignored by the ranking
+      const bool ok = wave_poll<5>(lw, 5 * 64, tag, give_up,
+                                   [&](int i) { return i < 256 ? min(4 * (i % 64) + i / 64, E) : E; },
+                                   [&](int u, int, uint64_t w) {
+                                     if (u < 4) v[u] = word_f(w);
+                                     else gate = word_f(w);
                                    });
-      if (!ok) {
-        if (lane < 4) { s_pe[lane] = kGroups * lane + g < T * k ? 0 : -1; s_pw[lane] = __builtin_nanf(""); }
-        if (lane == 0) s_bad = 1;
+      if (ok) {
+        wave_topk(v, E, k, s_ids[t], s_w[t], s_topk[t]);
+        if (lane == 0) s_sig[t] = sigmoid_f(gate);
+      } else {
+        if (lane < k) { s_ids[t][lane] = 0; s_w[t][lane] = __builtin_nanf(""); }
+        if (lane == 0) { s_sig[t] = __builtin_nanf(""); s_bad = 1; }
       }
+    }
+    __syncthreads();
+    for (int q = tid; q < kDecMaxT; q += blockDim.x) {
+      const int pp = kGroups * q + g;
+      s_pe[q] = pp < T * k ? s_ids[pp / k][pp % k] : -1;
+      s_pw[q] = pp < T * k ? s_w[pp / k][pp % k] : 0.f;
+    }
+    if (b == nb - 1) {
+      for (int q = tid; q < T * k; q += blockDim.x) {
+        if (a.ids_out) a.ids_out[q] = s_ids[q / k][q % k];
+        if (a.w_out) a.w_out[q] = s_w[q / k][q % k];
+      }
+      for (int t = tid; t < T; t += blockDim.x)
+        if (a.sigma_out) a.sigma_out[t] = s_sig[t];
     }
   } else if (tid < kDecMaxT) {
     const int pp = kGroups * tid + g;

@@ -35,8 +35,8 @@ struct DecodePlan {
   int rw;         // output rows per workgroup: ceil(H / nj)
   int scw;        // shared columns per workgroup: ceil(sw / nj)
   // tagged zones (64-bit words: call tag << 32 | value bits)
-  size_t z_logits;  // [T][E + 1]
-  size_t z_route;   // [8][16]: per group, pair experts (4), pair weights (4), sigma per token (4)
+  size_t z_logits;  // [8][T][E + 1]: one copy of the logits per group, zl_copy words apart
+  size_t zl_copy;
   size_t z_hs;      // [8][T][sw] shared SwiGLU activations of each slice
   size_t z_h;       // [8][npg][I] routed SwiGLU activations of each group's pairs
   size_t z_part;    // [8][T][H] each group's partial output rows
@@ -56,9 +56,8 @@ __host__ __device__ inline DecodePlan decode_plan(int H, int E, int k, int I, in
   p.rw = (H + p.nj - 1) / p.nj;
   p.scw = (p.sw + p.nj - 1) / p.nj;
   size_t o = 0;
-  p.z_logits = o; o += (size_t)T * (E + 1);
-  o = (o + 15) / 16 * 16;
-  p.z_route = o; o += (size_t)kGroups * 16;
+  p.zl_copy = ((size_t)T * (E + 1) + 15) / 16 * 16;
+  p.z_logits = o; o += kGroups * p.zl_copy;
   p.z_hs = o; o += (size_t)kGroups * T * p.sw;
   o = (o + 15) / 16 * 16;
   p.z_h = o; o += (size_t)kGroups * p.npg * I;
