@@ -235,14 +235,14 @@ __device__ __forceinline__ void decode_layer(const DecodeArgs& a0, int l, int L)
     copy_halves(act, a.x, T * H);
   } else {
     // the previous layer's output, once its reducers have published all of it
-    // (the tag is read in a barrier-ordered copy: s_tag was set before layer 0's barrier)
+    // (the tag is read in a barrier-ordered copy: s_tag was set before layer 0's
+    // barrier); word i carries outputs 2i (low half) and 2i + 1
     const uint32_t tg = s_tag;
-    const int n = T * H;
-    for (int base = wave * 64 * 4; base < n; base += 256 * 4) {
-      const bool ok = wave_poll<4>(zx_prev + base, min(256, n - base), tg, give_up, [](int i) { return i; },
-                                   [&](int, int i, uint64_t w) {
-                                     act[base + i] = __builtin_bit_cast(_Float16, (uint16_t)w);
-                                   });
+    const int nw = T * H / 2;
+    uint32_t* act2 = reinterpret_cast<uint32_t*>(act);
+    for (int base = wave * 64 * 4; base < nw; base += 256 * 4) {
+      const bool ok = wave_poll<4>(zx_prev + base, min(256, nw - base), tg, give_up, [](int i) { return i; },
+                                   [&](int, int i, uint64_t w) { act2[base + i] = (uint32_t)w; });
       if (!ok && lane == 0) s_bad = 1;
     }
   }
@@ -630,17 +630,31 @@ __device__ __forceinline__ void decode_layer(const DecodeArgs& a0, int l, int L)
         __builtin_amdgcn_s_sleep(2);
       }
     }
+    uint32_t o = 0;
     if (mine) {
       // DEC_BLOCK, DEC_LAYERS: the residual stream (layer l >= 1: the previous layer's
       // output, whose words this block has already seen complete)
       float sum = 0.f;
-      if (BLK)
-        sum = half_bits_to_float(l == 0 ? a.x[(size_t)t * H + n] : (uint16_t)get_tagged(zx_prev + (size_t)t * H + n));
+      if (BLK) {
+        uint16_t rb = 0;
+        if (l == 0) {
+          rb = a.x[(size_t)t * H + n];
+        } else {
+          const uint32_t w = (uint32_t)get_tagged(zx_prev + ((size_t)t * H + n) / 2);
+          rb = (uint16_t)(n & 1 ? w >> 16 : w);
+        }
+        sum = half_bits_to_float(rb);
+      }
 #pragma unroll
       for (int gg = 0; gg < kGroups; ++gg) sum += word_f(v[gg]);
-      const uint16_t o = __builtin_bit_cast(uint16_t, (_Float16)(ok ? sum : __builtin_nanf("")));
-      if (l == L - 1) a.out[(size_t)t * H + n] = o;
-      else put_tagged(a.tagged + p.z_x + (size_t)t * H + n, tag, o);
+      o = __builtin_bit_cast(uint16_t, (_Float16)(ok ? sum : __builtin_nanf("")));
+      if (l == L - 1) a.out[(size_t)t * H + n] = (uint16_t)o;
+    }
+    if (l < L - 1) {
+      // outputs n (even) and n + 1 share one word: rw is even, so they are
+      // this thread's and the next one's
+      const uint32_t o_next = (uint32_t)__shfl_xor((int)o, 1, 64);
+      if (mine && (n & 1) == 0) put_tagged(a.tagged + p.z_x + ((size_t)t * H + n) / 2, tag, o | (o_next << 16));
     }
     if (!ok && lane == 0) s_bad = 1;
   }

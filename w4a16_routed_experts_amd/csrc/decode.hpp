@@ -40,7 +40,7 @@ struct DecodePlan {
   size_t z_hs;      // [8][T][sw] shared SwiGLU activations of each slice
   size_t z_h;       // [8][npg][I] routed SwiGLU activations of each group's pairs
   size_t z_part;    // [8][T][H] each group's partial output rows
-  size_t z_x;       // [T][H] the layer's output (binary16 bits), read by every block of the next layer
+  size_t z_x;       // [T][H/2] the layer's output (two binary16 values a word), read by every block of the next layer
   size_t z_words;   // tagged words of one layer (each layer of a call has its own zones)
 };
 
@@ -53,7 +53,7 @@ __host__ __device__ inline DecodePlan decode_plan(int H, int E, int k, int I, in
   p.sw = Is / p.S;
   p.npg = (T * k + kGroups - 1) / kGroups;
   p.cw = (I + p.nj - 1) / p.nj;
-  p.rw = (H + p.nj - 1) / p.nj;
+  p.rw = ((H + p.nj - 1) / p.nj + 1) & ~1;  // even: a layer's output words carry two outputs
   p.scw = (p.sw + p.nj - 1) / p.nj;
   size_t o = 0;
   p.zl_copy = ((size_t)T * (E + 1) + 15) / 16 * 16;
@@ -64,7 +64,7 @@ __host__ __device__ inline DecodePlan decode_plan(int H, int E, int k, int I, in
   o = (o + 15) / 16 * 16;
   p.z_part = o; o += (size_t)kGroups * T * H;
   o = (o + 15) / 16 * 16;
-  p.z_x = o; o += (size_t)T * H;
+  p.z_x = o; o += (size_t)T * H / 2;
   p.z_words = (o + 15) / 16 * 16;
   return p;
 }
