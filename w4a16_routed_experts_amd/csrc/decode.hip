@@ -26,16 +26,17 @@
 // value bits) written and read with device-scope (sc1) atomic accesses; a
 // reader polls the words themselves until every tag equals this call's tag,
 // so no counter or flag sits between producer and consumer, and nothing has
-// to be cleared after a call.  The tag is the call
-// number: every block adds to its group's 64-bit call counter once, the
-// additions of one call sum to kJoinQuantum, so floor(counter / kJoinQuantum)
-// read by any block of a call is that call's number.  Each polled region is
-// read by the blocks of one group at most: a group's copy of the logits and
-// its activations by its nj members, a row block's 8 partial sums by one
-// block.  A wave that polls waits for every load it has in flight (the load
-// counter is in order), so the big weight loads are issued after the polls
-// that precede them, and loads meant to stay in flight across a poll are held
-// by waves that do not poll.
+// to be cleared after a call.  The tag is the call number: every block adds
+// to its group's 64-bit call counter once, the additions of one call sum to
+// kJoinQuantum, so floor(counter / kJoinQuantum) read by any block of a call
+// is that call's number.  Each polled region is read by the blocks of one
+// group at most: a group's copy of the logits and its activations by its nj
+// members, a row block's 8 partial sums by one block.  Only a layer's output,
+// with several layers per launch, is read by every block (two binary16
+// outputs a word, to halve that poll).  A wave that polls waits for every
+// load it has in flight (the load counter is in order), so the big weight
+// loads are issued after the polls that precede them, and loads meant to stay
+// in flight across a poll are held by waves that do not poll.
 //
 // Every wait is bounded.  A block whose wait gives up (its producers were not
 // running) publishes NaN in place of the values it could not compute and
