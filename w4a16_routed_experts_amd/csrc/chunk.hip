@@ -242,9 +242,11 @@ __global__ __launch_bounds__(64 * kRouterWaves) void router_gemm_kernel(ChunkArg
 #pragma unroll
   for (int i = 0; i < 16; ++i) red[wave][i][lane] = acc[i];
   __syncthreads();
-  if (wave == 0 && r < nrows) {
+  // the 8 waves' partial sums, added in wave order; wave w writes accumulator
+  // elements i = w, w + 8 (the lanes' rows and columns as in the MFMA layout)
+  if (r < nrows) {
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
+    for (int i = wave; i < 16; i += kRouterWaves) {
       const int tt = t0 + acc_row(i);
       float v = 0.f;
 #pragma unroll
