@@ -90,7 +90,9 @@ __device__ __forceinline__ float dot2(h2 a, h2 b, float c) {
   return __builtin_amdgcn_fdot2(a, b, c, false);
 }
 
-__device__ __forceinline__ float silu_f(float z) { return z / (1.0f + __expf(-z)); }
+// z sigmoid(z) with the hardware reciprocal (about 1 ulp) in place of an IEEE
+// division: the result is rounded to binary16 where it is used
+__device__ __forceinline__ float silu_f(float z) { return z * __builtin_amdgcn_rcpf(1.0f + __expf(-z)); }
 __device__ __forceinline__ float sigmoid_f(float z) { return 1.0f / (1.0f + expf(-z)); }
 
 __device__ __forceinline__ float half_bits_to_float(uint16_t b) {
