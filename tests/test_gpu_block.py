@@ -107,6 +107,20 @@ def test_block_other_widths(shape, T, flags):
     _check(case, h_bits, gain_bits, gpu, f"block-{shape}-T{T}-f{flags}")
 
 
+@pytest.mark.parametrize("T", [40, 70])
+def test_block_narrow_rows_chunk(T):
+    """Hidden 256: four 64-groups, fewer than the router GEMM's eight waves, so
+    half its waves have no group; they must still take part in the workgroup
+    barriers of the norm (a wave that skipped them once left the partial sums
+    of tokens 8..31 of every 32-token block unfinished when they were added)."""
+    d = gen.Dims(H=256, E=8, k=2, I=64, Is=64)
+    case = gen.make_case(d, T, seed=7600 + T)
+    _gpu.log(f"sub-block hidden 256 T={T} (grouped-GEMM path)")
+    h_bits, gain_bits = _inputs(case, 7700 + T)
+    gpu = _run_block(case, h_bits, gain_bits, m.PATH_CHUNK)
+    _check(case, h_bits, gain_bits, gpu, f"block-H256-T{T}")
+
+
 @pytest.mark.parametrize("T,flags", [(3, m.PATH_DECODE), (40, m.PATH_CHUNK)])
 def test_block_gain_plus_one(T, flags):
     """MOE_NORM_GAIN_PLUS_ONE: the gain array holds w and the norm multiplies by

@@ -106,6 +106,7 @@ void carve_chunk(const moe_dims* d, int T, Carve& c, ChunkArgs& a) {
   uint32_t* sync = c.take<uint32_t>(kSyncBytes);
   a.route_done = sync ? sync + (kCounterPages * kFlagPage - kSyncStride) : nullptr;
   a.logits = c.take<float>((size_t)T * (d->num_experts + 1) * 4);
+  a.logits_hi = c.take<float>((size_t)T * (d->num_experts + 1) * 4);
   a.ids = c.take<int32_t>(P * 4);
   a.wts = c.take<float>(P * 4);
   a.sigma = c.take<float>((size_t)T * 4);

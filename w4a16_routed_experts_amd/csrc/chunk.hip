@@ -3,7 +3,8 @@
 // The same block as the few-token path (the Chimera notebook, section 5; the
 // router ordering of section 5.2; int8 group-64 router rows stacked with the
 // shared gate, the TensorFold PR "Design"), organised for many tokens:
-//   1. router GEMM          logits[T][E+1]   (int8 rows, MFMA, per-group scales)
+//   1. router GEMM          logits[T][E+1]   (int8 rows, MFMA, per-group scales; for
+//                           the complete block in two K halves, added by the top-k)
 //   2. top-k per token      ids, renormalised weights, sigma
 //   3. bucketing            (token, slot) pairs sorted by expert, then pair
 //                           index; tiles of up to 128 rows per expert, shared
@@ -91,10 +92,22 @@ static constexpr int kRouterWaves = 8;
 static constexpr int kRxStride = 9;  // 16-byte chunks per LDS row of activations (8 + 1 against bank conflicts)
 static constexpr int kRwStride = 5;  // ... of router codes (4 + 1)
 
-__global__ __launch_bounds__(64 * kRouterWaves) void router_gemm_kernel(ChunkArgs a) {
-  __shared__ float red[kRouterWaves][16][64];
-  __shared__ uint4 stage[kRouterWaves][32 * (kRxStride + kRwStride)];
+// With gridDim.z = 2 (the complete block, few tokens) workgroup z takes K groups
+// [z ngr / 2, (z + 1) ngr / 2) and writes its partial sums to logits (z = 0)
+// or logits_hi (z = 1); the top-k adds the two in that order.  The staging
+// slices and the partial-sum buffer share their LDS (a barrier separates
+// them), so two workgroups fit on a compute unit.
+static constexpr int kRouterStage = kRouterWaves * 32 * (kRxStride + kRwStride);  // uint4s
+static constexpr int kRouterRed = kRouterWaves * 16 * 64 / 4;                        // uint4s
+// BATCH: K groups per wave in flight at once (2 for the K halves, whose
+// registers then let two workgroups share a compute unit)
+template <int BATCH>
+__global__ __launch_bounds__(64 * kRouterWaves, BATCH == 2 ? 4 : 1) void router_gemm_kernel(ChunkArgs a) {
+  __shared__ uint4 router_lds[kRouterStage > kRouterRed ? kRouterStage : kRouterRed];
+  auto red = reinterpret_cast<float (*)[16][64]>(router_lds);
+  auto stage = reinterpret_cast<uint4 (*)[32 * (kRxStride + kRwStride)]>(router_lds);
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int gb = blockIdx.z * (a.H / kGroup) / gridDim.z, ge = (blockIdx.z + 1) * (a.H / kGroup) / gridDim.z;
   const int m = lane & 31, g = lane >> 5;
   const int t0 = blockIdx.x * 32, r0 = blockIdx.y * 32;
   const int r = r0 + m;  // B row (router row) of this MFMA lane
@@ -124,7 +137,6 @@ __global__ __launch_bounds__(64 * kRouterWaves) void router_gemm_kernel(ChunkArg
   __shared__ float s_rn[32];
   const bool sub = a.gain != nullptr;  // uniform
   const __amdgpu_buffer_rsrc_t rg = make_rsrc(a.gain, sub ? (uint32_t)H * 2u : 0u);
-  constexpr int BATCH = 4;
   const bool one_batch = ngr <= kRouterWaves * BATCH;  // H <= 2048: the batch holds the wave's whole share
   // reciprocal RMS of the 32 tokens from each lane's partial sums of squares
   // of rows 8j + lane / 8 (four rows per lane)
@@ -174,13 +186,16 @@ __global__ __launch_bounds__(64 * kRouterWaves) void router_gemm_kernel(ChunkArg
   uint4* xs = stage[wave];
   uint4* wsl = stage[wave] + 32 * kRxStride;
   f16v acc = {};
-  for (int g0 = wave; g0 < ngr; g0 += kRouterWaves * BATCH) {
+  // Every wave runs the body at least once, also a wave with no group in
+  // [gb, ge) (narrow rows, or a K half): its loads are all out of range and
+  // read zeros, and it joins the workgroup barriers of the norm below.
+  for (int g0 = gb + wave;; g0 += kRouterWaves * BATCH) {
     u32x4 xa[BATCH][4], wb[BATCH][2], gn[BATCH];
     uint16_t sc[BATCH];
 #pragma unroll
     for (int u = 0; u < BATCH; ++u) {
       const int gi = g0 + kRouterWaves * u;
-      const bool ok = gi < ngr;  // uniform
+      const bool ok = gi < ge;  // uniform
       const uint32_t kx = ok ? 128u * gi : kOob, kq = ok ? 64u * gi : kOob, ks = ok ? 2u * gi : kOob;
 #pragma unroll
       for (int j = 0; j < 4; ++j) xa[u][j] = __builtin_amdgcn_raw_buffer_load_b128(rx, xoff[j] + kx, 0, 0);
@@ -208,7 +223,7 @@ __global__ __launch_bounds__(64 * kRouterWaves) void router_gemm_kernel(ChunkArg
 #pragma unroll
           for (int i = 0; i < 8; ++i) hv[i] = (_Float16)((float)hv[i] * rn * ((float)gv[i] + a.gain_add));
           xa[u][j] = __builtin_bit_cast(u32x4, hv);
-          if (gi < ngr) __builtin_amdgcn_raw_buffer_store_b128(xa[u][j], rxn, xoff[j] + 128u * gi, 0, 0);
+          if (gi < ge) __builtin_amdgcn_raw_buffer_store_b128(xa[u][j], rxn, xoff[j] + 128u * gi, 0, 0);
         }
       }
       // the wave's slice: written by all its lanes, then read in MFMA layout
@@ -238,12 +253,15 @@ __global__ __launch_bounds__(64 * kRouterWaves) void router_gemm_kernel(ChunkArg
 #pragma unroll
       for (int i = 0; i < 16; ++i) acc[i] = fmaf(p[i], scf, acc[i]);
     }
+    if (g0 + kRouterWaves * BATCH >= ge) break;
   }
+  __syncthreads();  // every wave is done with its staging slice (red shares the LDS)
 #pragma unroll
   for (int i = 0; i < 16; ++i) red[wave][i][lane] = acc[i];
   __syncthreads();
   // the 8 waves' partial sums, added in wave order; wave w writes accumulator
   // elements i = w, w + 8 (the lanes' rows and columns as in the MFMA layout)
+  float* const lo = blockIdx.z ? a.logits_hi : a.logits;
   if (r < nrows) {
 #pragma unroll
     for (int i = wave; i < 16; i += kRouterWaves) {
@@ -251,7 +269,7 @@ __global__ __launch_bounds__(64 * kRouterWaves) void router_gemm_kernel(ChunkArg
       float v = 0.f;
 #pragma unroll
       for (int w2 = 0; w2 < kRouterWaves; ++w2) v += red[w2][i][lane];
-      if (tt < a.T) a.logits[(size_t)tt * nrows + r] = v;
+      if (tt < a.T) lo[(size_t)tt * nrows + r] = v;
     }
   }
 }
@@ -270,10 +288,16 @@ __global__ __launch_bounds__(256) void topk_kernel(ChunkArgs a) {
   const float* lg = a.logits + (size_t)t * nrows;
   // all loads issued before any use (clamped indices: entries past E are
   // ignored by the ranking)
-  const float gate = lg[a.E];
+  float gate = lg[a.E];
   float v[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) v[j] = lg[min(4 * lane + j, a.E)];
+  if (a.logits_hi) {  // the second K half's partial sums, added after the first
+    const float* lh = a.logits_hi + (size_t)t * nrows;
+    gate += lh[a.E];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) v[j] += lh[min(4 * lane + j, a.E)];
+  }
   wave_topk(v, a.E, a.k, ids[wave], w[wave], sc[wave]);
   __builtin_amdgcn_wave_barrier();
   if (lane < a.k) {
@@ -520,10 +544,16 @@ __global__ __launch_bounds__(64 * kTopkBucketWaves) void topk_bucket_kernel(Chun
   if (t < a.T) {
     const int nrows = a.E + 1;
     const float* lg = a.logits + (size_t)t * nrows;
-    const float gate = lg[a.E];
+    float gate = lg[a.E];
     float v[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) v[j] = lg[min(4 * lane + j, a.E)];
+    if (a.logits_hi) {  // the second K half's partial sums, added after the first
+      const float* lh = a.logits_hi + (size_t)t * nrows;
+      gate += lh[a.E];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) v[j] += lh[min(4 * lane + j, a.E)];
+    }
     wave_topk(v, a.E, a.k, ids[wave], w[wave], sc[wave]);
     __builtin_amdgcn_wave_barrier();
     if (lane < a.k) {
@@ -1315,8 +1345,11 @@ __global__ __launch_bounds__(256) void combine_kernel(ChunkArgs a) {
 // ---------------------------------------------------------------------------
 // launchers
 // ---------------------------------------------------------------------------
-int launch_route_chunk(const ChunkArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL(router_gemm_kernel, dim3((a.T + 31) / 32, (a.E + 1 + 31) / 32), dim3(64 * kRouterWaves), 0, s, a);
+int launch_route_chunk(const ChunkArgs& a0, hipStream_t s) {
+  ChunkArgs a = a0;
+  a.logits_hi = nullptr;  // whole logits: the caller may ask for them
+  hipLaunchKernelGGL(router_gemm_kernel<4>, dim3((a.T + 31) / 32, (a.E + 1 + 31) / 32), dim3(64 * kRouterWaves), 0, s,
+                     a);
   hipLaunchKernelGGL(topk_kernel, dim3((a.T + 3) / 4), dim3(256), 0, s, a);
   return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_LAUNCH;
 }
@@ -1329,8 +1362,21 @@ int launch_experts_chunk(const ChunkArgs& a, hipStream_t s) {
   return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_LAUNCH;
 }
 
-int launch_forward_chunk(const ChunkArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL(router_gemm_kernel, dim3((a.T + 31) / 32, (a.E + 1 + 31) / 32), dim3(64 * kRouterWaves), 0, s, a);
+int launch_forward_chunk(const ChunkArgs& a0, hipStream_t s) {
+  // The router GEMM is split over K when its grid would be small (at most 64
+  // workgroups: up to 224 tokens at 257 rows), except in the sub-block, whose
+  // norm needs each workgroup to see whole rows.  (Measured: 1.3-1.6 us faster
+  // at 32 and 128 tokens, 0.6 us slower at 512.)
+  ChunkArgs a = a0;
+  const int router_wgs = ((a.T + 31) / 32) * ((a.E + 1 + 31) / 32);
+  if (a.gain || router_wgs > 64) a.logits_hi = nullptr;
+  const int ks = a.logits_hi ? 2 : 1;
+  if (ks == 2)
+    hipLaunchKernelGGL(router_gemm_kernel<2>, dim3((a.T + 31) / 32, (a.E + 1 + 31) / 32, 2), dim3(64 * kRouterWaves), 0,
+                       s, a);
+  else
+    hipLaunchKernelGGL(router_gemm_kernel<4>, dim3((a.T + 31) / 32, (a.E + 1 + 31) / 32), dim3(64 * kRouterWaves), 0,
+                       s, a);
   hipLaunchKernelGGL(topk_bucket_kernel, dim3((a.T + kTopkBucketWaves - 1) / kTopkBucketWaves),
                      dim3(64 * kTopkBucketWaves), 0, s, a);
   launch_gemms(a, s);

@@ -24,7 +24,8 @@ struct ChunkArgs {
   float gain_add;        // sub-block: added to every gain element in fp32 (1: the gain holds w of 1 + w)
   uint16_t* xn;          // sub-block: normalised activations [T][H], written by the router GEMM
   const uint16_t* resid; // sub-block: residual added by the combine, or null
-  float* logits;       // [T][E+1]
+  float* logits;       // [T][E+1] (the first K half's partial sums when logits_hi is set)
+  float* logits_hi;    // [T][E+1] the second K half's partial sums (router GEMM split over K), or null
   int32_t* ids;        // [T][k]
   float* wts;          // [T][k]
   float* sigma;        // [T]
