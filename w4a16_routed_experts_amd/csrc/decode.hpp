@@ -32,7 +32,7 @@ struct DecodePlan {
   int sw;         // shared intermediate columns per slice (Is / S)
   int npg;        // routed (token, slot) pairs per group at most: ceil(T k / 8)
   int cw;         // routed intermediate columns per workgroup and pair: ceil(I / nj)
-  int rw;         // output rows per workgroup: ceil(H / nj)
+  int rw;         // output rows per workgroup: ceil(H / nj), rounded up to even
   int scw;        // shared columns per workgroup: ceil(sw / nj)
   // tagged zones (64-bit words: call tag << 32 | value bits)
   size_t z_logits;  // [8][T][E + 1]: one copy of the logits per group, zl_copy words apart
