@@ -19,6 +19,7 @@ from __future__ import annotations
 
 import argparse
 import hashlib
+import re
 import json
 import os
 import sys
@@ -58,14 +59,23 @@ def algorithmic_flops(d, T):
 DECODE_SOURCES = ("api.hip", "common.hpp", "decode.hip", "decode.hpp", "gemv.hpp")
 
 
+def _code_only(text):
+    """C/C++ source without its comments and blank space, so that an edit of
+    the comments leaves the digest alone (the sources hold no string literal
+    with a comment marker in it)."""
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    return " ".join(text.split())
+
+
 def source_digest():
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "w4a16_routed_experts_amd", "csrc")
-    for name in DECODE_SOURCES:
-        with open(os.path.join(csrc, name), "rb") as f:
-            h.update(name.encode() + f.read())
-    with open(os.path.join(ROOT, "include", "moe_w4a16.h"), "rb") as f:
-        h.update(b"moe_w4a16.h" + f.read())
+    paths = [(name, os.path.join(csrc, name)) for name in DECODE_SOURCES]
+    paths.append(("moe_w4a16.h", os.path.join(ROOT, "include", "moe_w4a16.h")))
+    for name, path in paths:
+        with open(path, encoding="utf-8") as f:
+            h.update(name.encode() + _code_only(f.read()).encode())
     return h.hexdigest()[:16]
 
 
