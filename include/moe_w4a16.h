@@ -219,7 +219,7 @@ MOE_API int moe_layers_forward(const moe_dims* dims, const moe_weights* w, const
  * runs on, held until the process ends (its address is looked up once per
  * device, on the first call there).  A call whose moe_workspace_bytes(dims, T)
  * exceeds that size is refused with MOE_ERR_SCRATCH before anything is
- * enqueued (at real widths the limit admits 160 tokens and more).  Every call on
+ * enqueued (at real widths the limit admits up to 159 tokens).  Every call on
  * one GPU shares that GPU's array: calls that may overlap on one GPU (other
  * streams, other threads) race and must be ordered by the caller.  Each
  * completed call leaves the array as the next call needs it (arrival counters
