@@ -6,10 +6,10 @@
 //   1. router GEMM          logits[T][E+1]   (int8 rows, MFMA, per-group scales; for
 //                           the complete block in two K halves, added by the top-k)
 //   2. top-k per token      ids, renormalised weights, sigma
-//   3. bucketing            (token, slot) pairs sorted by expert, then pair
-//                           index; tiles of up to 128 rows per expert, shared
-//                           tiles (2 and 3 run in one launch for the complete
-//                           block: the last top-k workgroup sorts)
+//   3. bucketing            (token, slot) pairs grouped by expert; tiles of up
+//                           to 128 rows per expert, shared tiles (2 and 3 run
+//                           in one launch for the complete block: the last
+//                           top-k workgroup sorts)
 //   4. gate/up GEMM         h[row][I] = silu(x W_gate^T) * (x W_up^T)   (fp16)
 //   5. down GEMM            y[t*k+i][H] = w * (h W_down^T)                (fp16)
 //   6. combine              out[t] = sum_i y[t*k+i] + sigma_t * s[t]
@@ -310,23 +310,17 @@ __global__ __launch_bounds__(256) void topk_kernel(ChunkArgs a) {
 // ---------------------------------------------------------------------------
 // 3. bucketing: one workgroup of 1024 threads (16 waves)
 //
-// Pairs p = t*k + i are ordered by (expert, p): a stable counting sort.  Each
-// wave owns a contiguous run of pairs; ranks inside a 64-pair batch come from
-// ballots over the 8 bits of the expert id.  Each expert's rows are cut into
-// kTileRows-row tiles and one last tile of 1..kTileRows rows, which uses only
-// as many 32-row MFMA blocks as it needs (or the narrow path, for at most
-// kNarrowRows rows).
+// Pairs p = t*k + i are grouped by expert: a counting sort.  Each wave owns
+// a contiguous run of pairs and its own per-expert counters in LDS, and
+// places inside the wave's share of an expert's run come from LDS atomic adds
+// on those counters.  Only one wave touches a counter, and the lanes of one
+// instruction are served in a fixed order, so the order is the same in every
+// call on the same routing.  That matters: it decides which pairs fall into
+// an expert's last tile, which may take another MFMA shape (and rounding)
+// than its full tiles.  Each expert's rows are cut into kTileRows-row tiles
+// and one last tile of 1..kTileRows rows, which uses only as many 32-row MFMA
+// blocks as it needs (or the narrow path, for at most kNarrowRows rows).
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ uint64_t peers_of(int e) {
-  uint64_t peers = ~0ull;
-#pragma unroll
-  for (int bit = 0; bit < 8; ++bit) {
-    const uint64_t m = __ballot((e >> bit) & 1);
-    peers &= ((e >> bit) & 1) ? m : ~m;
-  }
-  return peers;
-}
-
 // the tile's MFMA row blocks of 32; 0 marks a narrow tile (at most kNarrowRows rows)
 __device__ __forceinline__ int4 make_tile(int e, int r0, int rows) {
   return make_int4(e, r0, rows, rows <= kNarrowRows ? 0 : (rows + 31) / 32);
@@ -372,27 +366,52 @@ __device__ __forceinline__ float load_wt(const float* p) {
   return *p;
 }
 
+// LDS of the bucketing.  bucket_clear must run, and a workgroup barrier
+// follow it, before bucket_body.
+struct BucketLds {
+  int cnt[16][kMaxExperts];      // pairs per wave and expert, then the wave's next place
+  int off[kMaxExperts];          // first place of each expert's run
+  int cls[2][kTileClasses];      // tiles per cost class, then each class's next slot
+  int total;                     // pairs kept (ids in [0, E))
+};
+
+__device__ __forceinline__ void bucket_clear(BucketLds& s) {
+  for (int i = threadIdx.x; i < 16 * kMaxExperts; i += blockDim.x) (&s.cnt[0][0])[i] = 0;
+  if (threadIdx.x < kTileClasses) s.cls[0][threadIdx.x] = 0;
+}
+
+// This lane's slot among the slots of cost class c handed out from next[c]
+// (want: the lane has a tile of class c).  One LDS add per class and wave;
+// the whole wave calls it.
+__device__ __forceinline__ int take_slot(int* next, int c, bool want) {
+  const int lane = threadIdx.x & 63;
+  const uint64_t lt = (1ull << lane) - 1ull;
+  int slot = 0;
+#pragma unroll
+  for (int cc = 0; cc < kTileClasses; ++cc) {
+    const uint64_t m = __ballot(want && c == cc);
+    if (m == 0) continue;  // uniform
+    int base = 0;
+    if (lane == 0) base = atomicAdd(&next[cc], __popcll(m));
+    base = __shfl(base, 0);
+    if (want && c == cc) slot = base + __popcll(m & lt);
+  }
+  return slot;
+}
+
 template <bool CO>
-__device__ __forceinline__ void bucket_body(const ChunkArgs& a) {
-  __shared__ int hist[16][kMaxExperts + 1];  // per-wave counts, then per-wave bases
-  __shared__ int s_off[kMaxExperts + 1];
-  __shared__ int s_cls[2][kTileClasses];  // tiles per cost class, then each class's next slot
-  __shared__ int s_total;
+__device__ __forceinline__ void bucket_body(const ChunkArgs& a, BucketLds& s) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int P = a.T * a.k;
   const int E = a.E;
   const int per = (P + 15) / 16;
   const int p_begin = min(P, wave * per), p_end = min(P, p_begin + per);
-  const uint64_t lt = (1ull << lane) - 1ull;
 
-  for (int i = threadIdx.x; i < 16 * (kMaxExperts + 1); i += blockDim.x) (&hist[0][0])[i] = 0;
-  if (threadIdx.x < kTileClasses) s_cls[0][threadIdx.x] = 0;
-  __syncthreads();
-  // per-wave histograms (ids outside [0, E) are dropped: they never index
-  // weights).  Ids are loaded kBatch rounds at a time with clamped (always
-  // valid) indices, so the loads are in flight together.  The first batch of
-  // ids and routing weights stays in registers for the scatter below (with
-  // T * k <= 16 * 64 * kBatch it is the wave's whole share).
+  // counts (ids outside [0, E) are dropped: they never index weights).  Ids
+  // are loaded kBatch rounds at a time with clamped (always valid) indices,
+  // so the loads are in flight together.  The first batch of ids and routing
+  // weights stays in registers for the scatter below (with T * k <= 16 * 64 *
+  // kBatch it is the wave's whole share).
   constexpr int kBatch = 4;
   int ev0[kBatch];
   float wv0[kBatch];
@@ -406,9 +425,7 @@ __device__ __forceinline__ void bucket_body(const ChunkArgs& a) {
     for (int u = 0; u < kBatch; ++u) {
       const int p = p0 + 64 * u + lane;
       const int e = p < p_end ? ev[u] : -1;
-      const bool ok = e >= 0 && e < E;
-      const uint64_t pe = peers_of(ok ? e : 255) & __ballot(ok);
-      if (ok && (pe & lt) == 0) hist[wave][e] += __popcll(pe);  // one leader per expert
+      if (e >= 0 && e < E) atomicAdd(&s.cnt[wave][e], 1);
     }
   };
   count(p_begin, ev0);
@@ -419,18 +436,30 @@ __device__ __forceinline__ void bucket_body(const ChunkArgs& a) {
     count(p0, ev);
   }
   __syncthreads();
-  if (threadIdx.x < kMaxExperts + 1) {
+  constexpr int top = kTileRows / 32;  // the heaviest class
+  if (threadIdx.x < kMaxExperts) {  // the waves' counts -> their first places; tiles per cost class
     const int e = threadIdx.x;
     int tot = 0;
     if (e < E)
-      for (int w = 0; w < 16; ++w) { const int c = hist[w][e]; hist[w][e] = tot; tot += c; }
-    s_off[e] = e < E ? tot : 0;  // counts for now
-    if (e < E && tot > 0) {        // tiles per cost class: full tiles, then the last one
-      if (tot >= kTileRows) atomicAdd(&s_cls[0][kTileRows / 32], tot / kTileRows);
-      if (tot % kTileRows) atomicAdd(&s_cls[0][make_tile(e, 0, tot % kTileRows).w], 1);
+#pragma unroll
+      for (int w = 0; w < 16; ++w) {
+        const int c = s.cnt[w][e];
+        s.cnt[w][e] = tot;
+        tot += c;
+      }
+    s.off[e] = tot;  // the count for now
+    if (tot >= kTileRows) atomicAdd(&s.cls[0][top], tot / kTileRows);
+    const int tc = tot % kTileRows ? make_tile(e, 0, tot % kTileRows).w : -1;
+#pragma unroll
+    for (int c = 0; c < kTileClasses; ++c) {
+      const uint64_t m = __ballot(tc == c);
+      if (m && lane == 0) atomicAdd(&s.cls[0][c], __popcll(m));
     }
+  } else if (threadIdx.x == kMaxExperts && a.shared_tiles > 0) {  // all full but perhaps the last
+    const int ns = a.shared_tiles;
+    if (ns > 1) atomicAdd(&s.cls[0][shared_tile(0, a.T).w], ns - 1);
+    atomicAdd(&s.cls[0][shared_tile(ns - 1, a.T).w], 1);
   }
-  for (int st = threadIdx.x; st < a.shared_tiles; st += blockDim.x) atomicAdd(&s_cls[0][shared_tile(st, a.T).w], 1);
   __syncthreads();
   if (wave == 0) {  // exclusive scan of counts (E <= 256: 4 per lane)
     int c[4];
@@ -438,7 +467,7 @@ __device__ __forceinline__ void bucket_body(const ChunkArgs& a) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int e = 4 * lane + j;
-      c[j] = e < E ? s_off[e] : 0;
+      c[j] = e < E ? s.off[e] : 0;
       sc += c[j];
     }
     int ic = sc;
@@ -449,16 +478,15 @@ __device__ __forceinline__ void bucket_body(const ChunkArgs& a) {
     int ec = ic - sc;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const int e = 4 * lane + j;
-      if (e <= kMaxExperts) s_off[e] = ec;
+      s.off[4 * lane + j] = ec;
       ec += c[j];
     }
-    if (lane == 63) s_total = ic;
+    if (lane == 63) s.total = ic;
     if (lane == 0) {  // classes in decreasing cost: the tile list starts with the heaviest tiles
       int base = 0;
       for (int c2 = kTileClasses - 1; c2 >= 0; --c2) {
-        s_cls[1][c2] = base;
-        base += s_cls[0][c2];
+        s.cls[1][c2] = base;
+        base += s.cls[0][c2];
       }
       *a.n_tiles = base;
     }
@@ -466,46 +494,44 @@ __device__ __forceinline__ void bucket_body(const ChunkArgs& a) {
   __syncthreads();
   {
     // Tiles in cost order (the order inside a class is immaterial: every
-    // output row and column belongs to exactly one tile).  An expert's full
-    // tiles take one run of slots.
-    const int total = s_total;
-    constexpr int top = kTileRows / 32;  // the heaviest class: slots [0, n_top)
-    const int n_top = s_cls[0][top];
-    for (int e = threadIdx.x; e < E; e += blockDim.x) {
-      const int start = s_off[e];
-      const int end = (e + 1 < E) ? s_off[e + 1] : total;
-      const int nfull = (end - start) / kTileRows;
-      const bool tail_top = (end - start) % kTileRows != 0 && make_tile(e, 0, (end - start) % kTileRows).w == top;
-      const int run = nfull + (tail_top ? 1 : 0);  // the expert's tiles of the heaviest class
-      int ti = run ? atomicAdd(&s_cls[1][top], run) : 0;
+    // output row and column belongs to exactly one tile).  An expert's tiles
+    // of the heaviest class take one run of slots.
+    const int total = s.total;
+    const int n_top = s.cls[0][top];
+    if (threadIdx.x < kMaxExperts) {
+      const int e = threadIdx.x;
+      const int start = e < E ? s.off[e] : 0;
+      const int end = e + 1 < E ? s.off[e + 1] : (e < E ? total : 0);
+      const int tail = (end - start) % kTileRows;
+      const int tc = tail ? make_tile(e, 0, tail).w : -1;
+      const int run = (end - start) / kTileRows + (tc == top ? 1 : 0);  // the expert's tiles of the heaviest class
+      int ti = run ? atomicAdd(&s.cls[1][top], run) : 0;
       int r = start;
       for (int i = 0; i < run; ++i, r += kTileRows) a.tiles[top_slot(ti++, n_top)] = make_tile(e, r, min(kTileRows, end - r));
-      if (r < end) {
-        const int4 t = make_tile(e, r, end - r);
-        a.tiles[atomicAdd(&s_cls[1][t.w], 1)] = t;
-      }
+      const bool last = tc >= 0 && tc != top;  // a last tile of a lighter class
+      const int slot = take_slot(s.cls[1], tc, last);
+      if (last) a.tiles[slot] = make_tile(e, r, end - r);
     }
-    for (int st = threadIdx.x; st < a.shared_tiles; st += blockDim.x) {
-      const int4 t = shared_tile(st, a.T);
-      const int ti = atomicAdd(&s_cls[1][t.w], 1);
-      a.tiles[t.w == top ? top_slot(ti, n_top) : ti] = t;  // the heaviest class's slots follow top_slot
+    for (int st0 = 64 * wave; st0 < a.shared_tiles; st0 += blockDim.x) {  // wave-uniform trip count
+      const int st = st0 + lane;
+      const bool mine = st < a.shared_tiles;
+      const int4 t = shared_tile(mine ? st : 0, a.T);
+      const int slot = take_slot(s.cls[1], t.w, mine);
+      if (mine) a.tiles[t.w == top ? top_slot(slot, n_top) : slot] = t;  // the heaviest class's slots follow top_slot
     }
   }
-  // stable scatter: position of pair p in expert-major order, with its
-  // routing weight (so the down GEMM reads both by position)
+  // scatter: each pair's place in its expert's run, with its routing weight
+  // (so the down GEMM reads both by place)
   auto scatter = [&](int p0, const int* ev, const float* wv) {
 #pragma unroll
     for (int u = 0; u < kBatch; ++u) {
       const int p = p0 + 64 * u + lane;
       const int e = p < p_end ? ev[u] : -1;
-      const bool ok = e >= 0 && e < E;
-      const uint64_t pe = peers_of(ok ? e : 255) & __ballot(ok);
-      if (ok) {
-        const int pos = s_off[e] + hist[wave][e] + __popcll(pe & lt);
+      if (e >= 0 && e < E) {
+        const int pos = s.off[e] + atomicAdd(&s.cnt[wave][e], 1);
         a.sorted_pair[pos] = p;
         a.sorted_wt[pos] = wv[u];
       }
-      if (ok && (pe & lt) == 0) hist[wave][e] += __popcll(pe);
     }
   };
   scatter(p_begin, ev0, wv0);
@@ -522,12 +548,18 @@ __device__ __forceinline__ void bucket_body(const ChunkArgs& a) {
 }
 
 // caller-supplied routing (the routed half alone)
-__global__ __launch_bounds__(1024) void bucket_kernel(ChunkArgs a) { bucket_body<false>(a); }
+__global__ __launch_bounds__(1024) void bucket_kernel(ChunkArgs a) {
+  __shared__ BucketLds bs;
+  bucket_clear(bs);
+  __syncthreads();
+  bucket_body<false>(a, bs);
+}
 
 // ---------------------------------------------------------------------------
 // 2 + 3 in one launch (the complete block): each wave ranks one token as in
-// topk_kernel, and the last workgroup to finish, found with a device-scope
-// counter, sorts the pairs.  ids and weights are written with device-coherent
+// topk_kernel (up to 1024 tokens, four per workgroup, so that the ranking is
+// spread over many compute units), and the last workgroup to finish, found
+// with a device-scope counter, sorts the pairs.  ids and weights are written with device-coherent
 // stores and acknowledged before the counter moves, and that workgroup reads
 // them back with device-coherent loads, so no L2 serves it a stale copy.  No
 // workgroup waits for another: the kernel always drains.
@@ -538,10 +570,12 @@ __global__ __launch_bounds__(64 * kTopkBucketWaves) void topk_bucket_kernel(Chun
   __shared__ TopkScratch sc[kTopkBucketWaves];
   __shared__ int ids[kTopkBucketWaves][kMaxTopK];
   __shared__ float w[kTopkBucketWaves][kMaxTopK];
+  __shared__ BucketLds bs;
   __shared__ int s_last;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int t = blockIdx.x * kTopkBucketWaves + wave;
-  if (t < a.T) {
+  const int tpw = (a.T + gridDim.x - 1) / gridDim.x;  // tokens per workgroup (at most kTopkBucketWaves)
+  const int t = blockIdx.x * tpw + wave;
+  if (wave < tpw && t < a.T) {
     const int nrows = a.E + 1;
     const float* lg = a.logits + (size_t)t * nrows;
     float gate = lg[a.E];
@@ -563,6 +597,7 @@ __global__ __launch_bounds__(64 * kTopkBucketWaves) void topk_bucket_kernel(Chun
     }
     if (lane == 0) a.sigma[t] = sigmoid_f(gate);
   }
+  bucket_clear(bs);  // while the stores drain (only the last workgroup uses it)
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's stores are acknowledged
   __syncthreads();
   if (threadIdx.x == 0)
@@ -570,7 +605,7 @@ __global__ __launch_bounds__(64 * kTopkBucketWaves) void topk_bucket_kernel(Chun
   __syncthreads();
   if (!s_last) return;
   if (threadIdx.x == 0) __hip_atomic_store(a.route_done, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  bucket_body<true>(a);
+  bucket_body<true>(a, bs);
 }
 
 // ---------------------------------------------------------------------------
@@ -1377,7 +1412,10 @@ int launch_forward_chunk(const ChunkArgs& a0, hipStream_t s) {
   else
     hipLaunchKernelGGL(router_gemm_kernel<4>, dim3((a.T + 31) / 32, (a.E + 1 + 31) / 32), dim3(64 * kRouterWaves), 0,
                        s, a);
-  hipLaunchKernelGGL(topk_bucket_kernel, dim3((a.T + kTopkBucketWaves - 1) / kTopkBucketWaves),
+  // a few tokens per workgroup spread the ranking over more compute units;
+  // at most 256 workgroups bump the completion counter up to 4096 tokens
+  const int tpw = a.T > 4096 ? kTopkBucketWaves : (a.T > 1024 ? (a.T + 255) / 256 : 4);
+  hipLaunchKernelGGL(topk_bucket_kernel, dim3((a.T + tpw - 1) / tpw),
                      dim3(64 * kTopkBucketWaves), 0, s, a);
   launch_gemms(a, s);
   return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_LAUNCH;
