@@ -338,16 +338,32 @@ static constexpr int kTileClasses = kTileRows / 32 + 1;  // cost classes: 32-row
 // GEMM kernels run tile s on XCD s % 8, so the class is filled column by
 // column of an 8-wide grid: consecutive j, which are one expert's tiles, share
 // an XCD, and its L2 fetches the expert's weights once for all of them.
-__device__ __forceinline__ int top_slot(int j, int n) {
-  const int R = (n + 7) / 8;       // rows of the grid
-  const int fc = n - 8 * (R - 1);  // columns with R rows (the others have R - 1)
-  int c, rho;
-  if (j < fc * R) {
-    c = j / R; rho = j % R;
-  } else {
-    const int jj = j - fc * R;
-    c = fc + jj / (R - 1); rho = jj % (R - 1);
+struct TopSlots {
+  int R;   // rows of the grid
+  int fc;  // columns with R rows (the others have R - 1)
+  __device__ __forceinline__ explicit TopSlots(int n) : R((n + 7) / 8), fc(n - 8 * ((n + 7) / 8 - 1)) {}
+  // column c and row rho of the j-th tile
+  __device__ __forceinline__ void at(int j, int& c, int& rho) const {
+    if (j < fc * R) {
+      c = j / R;
+      rho = j - c * R;
+    } else {
+      const int jj = j - fc * R;
+      c = fc + jj / (R - 1);
+      rho = jj - (c - fc) * (R - 1);
+    }
   }
+  // the (j+1)-th tile from the j-th: down the column, then to the next one
+  __device__ __forceinline__ void next(int& c, int& rho) const {
+    if (++rho == (c < fc ? R : R - 1)) {
+      rho = 0;
+      ++c;
+    }
+  }
+};
+__device__ __forceinline__ int top_slot(int j, int n) {
+  int c, rho;
+  TopSlots(n).at(j, c, rho);
   return 8 * rho + c;
 }
 
@@ -378,25 +394,6 @@ struct BucketLds {
 __device__ __forceinline__ void bucket_clear(BucketLds& s) {
   for (int i = threadIdx.x; i < 16 * kMaxExperts; i += blockDim.x) (&s.cnt[0][0])[i] = 0;
   if (threadIdx.x < kTileClasses) s.cls[0][threadIdx.x] = 0;
-}
-
-// This lane's slot among the slots of cost class c handed out from next[c]
-// (want: the lane has a tile of class c).  One LDS add per class and wave;
-// the whole wave calls it.
-__device__ __forceinline__ int take_slot(int* next, int c, bool want) {
-  const int lane = threadIdx.x & 63;
-  const uint64_t lt = (1ull << lane) - 1ull;
-  int slot = 0;
-#pragma unroll
-  for (int cc = 0; cc < kTileClasses; ++cc) {
-    const uint64_t m = __ballot(want && c == cc);
-    if (m == 0) continue;  // uniform
-    int base = 0;
-    if (lane == 0) base = atomicAdd(&next[cc], __popcll(m));
-    base = __shfl(base, 0);
-    if (want && c == cc) slot = base + __popcll(m & lt);
-  }
-  return slot;
 }
 
 template <bool CO>
@@ -505,19 +502,22 @@ __device__ __forceinline__ void bucket_body(const ChunkArgs& a, BucketLds& s) {
       const int tail = (end - start) % kTileRows;
       const int tc = tail ? make_tile(e, 0, tail).w : -1;
       const int run = (end - start) / kTileRows + (tc == top ? 1 : 0);  // the expert's tiles of the heaviest class
-      int ti = run ? atomicAdd(&s.cls[1][top], run) : 0;
       int r = start;
-      for (int i = 0; i < run; ++i, r += kTileRows) a.tiles[top_slot(ti++, n_top)] = make_tile(e, r, min(kTileRows, end - r));
-      const bool last = tc >= 0 && tc != top;  // a last tile of a lighter class
-      const int slot = take_slot(s.cls[1], tc, last);
-      if (last) a.tiles[slot] = make_tile(e, r, end - r);
+      if (run) {  // one division for the run's first slot, then a walk down the grid
+        const TopSlots ts(n_top);
+        int c, rho;
+        ts.at(atomicAdd(&s.cls[1][top], run), c, rho);
+        for (int i = 0; i < run; ++i, r += kTileRows) {
+          a.tiles[8 * rho + c] = make_tile(e, r, min(kTileRows, end - r));
+          ts.next(c, rho);
+        }
+      }
+      if (tc >= 0 && tc != top) a.tiles[atomicAdd(&s.cls[1][tc], 1)] = make_tile(e, r, end - r);  // a lighter last tile
     }
-    for (int st0 = 64 * wave; st0 < a.shared_tiles; st0 += blockDim.x) {  // wave-uniform trip count
-      const int st = st0 + lane;
-      const bool mine = st < a.shared_tiles;
-      const int4 t = shared_tile(mine ? st : 0, a.T);
-      const int slot = take_slot(s.cls[1], t.w, mine);
-      if (mine) a.tiles[t.w == top ? top_slot(slot, n_top) : slot] = t;  // the heaviest class's slots follow top_slot
+    for (int st = threadIdx.x; st < a.shared_tiles; st += blockDim.x) {
+      const int4 t = shared_tile(st, a.T);
+      const int ti = atomicAdd(&s.cls[1][t.w], 1);
+      a.tiles[t.w == top ? top_slot(ti, n_top) : ti] = t;  // the heaviest class's slots follow top_slot
     }
   }
   // scatter: each pair's place in its expert's run, with its routing weight
