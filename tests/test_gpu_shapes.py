@@ -119,3 +119,43 @@ def test_weights_and_outputs_near_binary16_max(T, flags):
     assert np.abs(sh2).max() > 30000.0 and 10000.0 < np.abs(r["out"]).max() < 65504.0
     g = _gpu.run_forward(case, flags=flags)
     _gpu.check_forward(case, r, g, f"near binary16 max T{T} f{flags}")
+
+
+def _ids_with_counts(counts, T, k):
+    """ids [T, k] in which expert e is listed by exactly counts[e] tokens (at
+    most once per token): each expert's listings fill consecutive places of
+    the column-major grid, so they fall on distinct tokens."""
+    flat = np.repeat(np.arange(len(counts)), counts)
+    assert flat.size == T * k and max(counts) <= T
+    idx = np.arange(T * k)
+    ids = np.empty((T, k), dtype=np.int64)
+    ids[idx % T, idx // T] = flat
+    return ids
+
+
+def test_bucketing_tile_classes():
+    """Caller routing that gives experts the row counts at every tile-class
+    boundary of the grouped GEMMs: 1 and 16 (narrow), 17, 32, 33, 96, 97
+    (the heaviest class as a last tile), 128 and 256 (full tiles with no last
+    tile), 129 (a full tile and a one-row last tile) and 225 (a full tile and
+    a 97-row last tile), among tiles of 100 rows.  Parity against the oracle,
+    and two calls bit for bit (the pairs that fill an expert's last tile must
+    be the same in every call)."""
+    T, k = 260, 8
+    case = gen.make_case(gen.REAL, T, seed=5300, real_experts=True)
+    d = case.dims
+    boundary = [256, 225, 129, 128, 97, 96, 33, 32, 17, 16, 1]
+    rest = T * k - sum(boundary)
+    counts = boundary + [100] * (rest // 100) + ([rest % 100] if rest % 100 else [])
+    rng = np.random.default_rng(5301)
+    perm = rng.permutation(d.E)[:len(counts)]
+    ids = perm[_ids_with_counts(counts, T, k)]
+    w = rng.uniform(0.05, 1.0, size=(T, k))
+    _gpu.log(f"caller routing with tile-class boundary counts, T={T}, {len(counts)} experts")
+    g1 = _gpu.run_experts(case, ids, w)
+    g2 = _gpu.run_experts(case, ids, w)
+    want = ref.experts(case.x, ids, w, case.weights, d)
+    err = _gpu.row_rel_l2(g1, want)
+    _gpu.log(f"  rel L2 max {err.max():.3e}")
+    assert err.max() <= _gpu.ROW_TOL
+    assert np.array_equal(g1, g2)
