@@ -557,7 +557,7 @@ __global__ __launch_bounds__(1024) void bucket_kernel(ChunkArgs a) {
 
 // ---------------------------------------------------------------------------
 // 2 + 3 in one launch (the complete block): each wave ranks one token as in
-// topk_kernel (up to 1024 tokens, four per workgroup, so that the ranking is
+// topk_kernel (four to sixteen tokens per workgroup, so that the ranking is
 // spread over many compute units), and the last workgroup to finish, found
 // with a device-scope counter, sorts the pairs.  ids and weights are written with device-coherent
 // stores and acknowledged before the counter moves, and that workgroup reads
@@ -1412,9 +1412,10 @@ int launch_forward_chunk(const ChunkArgs& a0, hipStream_t s) {
   else
     hipLaunchKernelGGL(router_gemm_kernel<4>, dim3((a.T + 31) / 32, (a.E + 1 + 31) / 32), dim3(64 * kRouterWaves), 0,
                        s, a);
-  // a few tokens per workgroup spread the ranking over more compute units;
-  // at most 256 workgroups bump the completion counter up to 4096 tokens
-  const int tpw = a.T > 4096 ? kTopkBucketWaves : (a.T > 1024 ? (a.T + 255) / 256 : 4);
+  // a few tokens per workgroup spread the ranking over more compute units,
+  // while at most 64 workgroups (up to 1024 tokens) contend for the completion
+  // counter, whose atomics are served one at a time
+  const int tpw = a.T <= 256 ? 4 : min(kTopkBucketWaves, max(4, (a.T + 63) / 64));
   hipLaunchKernelGGL(topk_bucket_kernel, dim3((a.T + tpw - 1) / tpw),
                      dim3(64 * kTopkBucketWaves), 0, s, a);
   launch_gemms(a, s);
