@@ -264,3 +264,16 @@ def test_few_token_give_up_is_loud_and_recoverable(cfg):
     g = dict(out=_gpu.half_to_f64(out), ids=ids.cpu().numpy(), w=w.cpu().numpy().astype(np.float64),
              sigma=sig.cpu().numpy().astype(np.float64))
     _gpu.check_forward(case, _gpu.config_oracle(cfg), g, f"cfg{cfg} after give-up")
+
+
+def test_grid_bucketing_zipf_2048():
+    """Above 1024 tokens the top-k writes per-workgroup expert counts and the
+    sort runs over the grid (count, scan, scatter launches).  2048 Zipf-skewed
+    tokens give the popular experts full tiles and last tiles of every class:
+    parity against the oracle on every row, and two calls bit for bit."""
+    case = gen.make_case(gen.REAL, 2048, seed=2048, bias="zipf1.1", c=8.0, real_experts=True)
+    _gpu.log("grid-wide bucketing T=2048 zipf")
+    g = _gpu.run_forward(case, reps=2)
+    assert np.array_equal(g["out_raw"][0], g["out_raw"][1])
+    r = ref.forward(case.x, case.weights, case.dims)
+    _gpu.check_forward(case, r, g, "T2048-zipf")

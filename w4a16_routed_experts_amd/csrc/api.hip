@@ -110,7 +110,9 @@ void carve_chunk(const moe_dims* d, int T, Carve& c, ChunkArgs& a) {
   a.ids = c.take<int32_t>(P * 4);
   a.wts = c.take<float>(P * 4);
   a.sigma = c.take<float>((size_t)T * 4);
-  a.offsets = c.take<int32_t>((size_t)(d->num_experts + 1) * 4);
+  a.wg_cnt = c.take<int32_t>((size_t)d->num_experts * ((T + 15) / 16) * 4);
+  a.exp_cnt = c.take<int32_t>((size_t)d->num_experts * 4);
+  a.exp_off = c.take<int32_t>((size_t)d->num_experts * 4);
   a.sorted_pair = c.take<int32_t>(P * 4);
   a.sorted_wt = c.take<float>(P * 4);
   a.tiles = c.take<int4>((size_t)(max_route_tiles(d, T) + (T + kSharedRows - 1) / kSharedRows) * 16);

@@ -396,54 +396,18 @@ __device__ __forceinline__ void bucket_clear(BucketLds& s) {
   if (threadIdx.x < kTileClasses) s.cls[0][threadIdx.x] = 0;
 }
 
-template <bool CO>
-__device__ __forceinline__ void bucket_body(const ChunkArgs& a, BucketLds& s) {
+// The tile list from the experts' pair counts: count_of(e) is called once
+// by thread e < kMaxExperts (0 for e >= E).  On return s.off holds each
+// expert's first place, the tiles and the tile count are written, and every
+// thread has passed the barrier after the scan.  Needs kMaxExperts threads.
+template <class CountOf>
+__device__ __forceinline__ void bucket_tiles(const ChunkArgs& a, BucketLds& s, CountOf count_of) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int P = a.T * a.k;
   const int E = a.E;
-  const int per = (P + 15) / 16;
-  const int p_begin = min(P, wave * per), p_end = min(P, p_begin + per);
-
-  // counts (ids outside [0, E) are dropped: they never index weights).  Ids
-  // are loaded kBatch rounds at a time with clamped (always valid) indices,
-  // so the loads are in flight together.  The first batch of ids and routing
-  // weights stays in registers for the scatter below (with T * k <= 16 * 64 *
-  // kBatch it is the wave's whole share).
-  constexpr int kBatch = 4;
-  int ev0[kBatch];
-  float wv0[kBatch];
-#pragma unroll
-  for (int u = 0; u < kBatch; ++u) {
-    ev0[u] = load_id<CO>(a.ids + min(p_begin + 64 * u + lane, P - 1));
-    wv0[u] = load_wt<CO>(a.wts + min(p_begin + 64 * u + lane, P - 1));
-  }
-  auto count = [&](int p0, const int* ev) {
-#pragma unroll
-    for (int u = 0; u < kBatch; ++u) {
-      const int p = p0 + 64 * u + lane;
-      const int e = p < p_end ? ev[u] : -1;
-      if (e >= 0 && e < E) atomicAdd(&s.cnt[wave][e], 1);
-    }
-  };
-  count(p_begin, ev0);
-  for (int p0 = p_begin + 64 * kBatch; p0 < p_end; p0 += 64 * kBatch) {
-    int ev[kBatch];
-#pragma unroll
-    for (int u = 0; u < kBatch; ++u) ev[u] = load_id<CO>(a.ids + min(p0 + 64 * u + lane, P - 1));
-    count(p0, ev);
-  }
-  __syncthreads();
   constexpr int top = kTileRows / 32;  // the heaviest class
-  if (threadIdx.x < kMaxExperts) {  // the waves' counts -> their first places; tiles per cost class
+  if (threadIdx.x < kMaxExperts) {  // each expert's count; tiles per cost class
     const int e = threadIdx.x;
-    int tot = 0;
-    if (e < E)
-#pragma unroll
-      for (int w = 0; w < 16; ++w) {
-        const int c = s.cnt[w][e];
-        s.cnt[w][e] = tot;
-        tot += c;
-      }
+    const int tot = count_of(e);
     s.off[e] = tot;  // the count for now
     if (tot >= kTileRows) atomicAdd(&s.cls[0][top], tot / kTileRows);
     const int tc = tot % kTileRows ? make_tile(e, 0, tot % kTileRows).w : -1;
@@ -452,7 +416,8 @@ __device__ __forceinline__ void bucket_body(const ChunkArgs& a, BucketLds& s) {
       const uint64_t m = __ballot(tc == c);
       if (m && lane == 0) atomicAdd(&s.cls[0][c], __popcll(m));
     }
-  } else if (threadIdx.x == kMaxExperts && a.shared_tiles > 0) {  // all full but perhaps the last
+  }
+  if (threadIdx.x == blockDim.x - 1 && a.shared_tiles > 0) {  // all full but perhaps the last
     const int ns = a.shared_tiles;
     if (ns > 1) atomicAdd(&s.cls[0][shared_tile(0, a.T).w], ns - 1);
     atomicAdd(&s.cls[0][shared_tile(ns - 1, a.T).w], 1);
@@ -520,6 +485,56 @@ __device__ __forceinline__ void bucket_body(const ChunkArgs& a, BucketLds& s) {
       a.tiles[t.w == top ? top_slot(ti, n_top) : ti] = t;  // the heaviest class's slots follow top_slot
     }
   }
+}
+
+template <bool CO>
+__device__ __forceinline__ void bucket_body(const ChunkArgs& a, BucketLds& s) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int P = a.T * a.k;
+  const int E = a.E;
+  const int per = (P + 15) / 16;
+  const int p_begin = min(P, wave * per), p_end = min(P, p_begin + per);
+
+  // counts (ids outside [0, E) are dropped: they never index weights).  Ids
+  // are loaded kBatch rounds at a time with clamped (always valid) indices,
+  // so the loads are in flight together.  The first batch of ids and routing
+  // weights stays in registers for the scatter below (with T * k <= 16 * 64 *
+  // kBatch it is the wave's whole share).
+  constexpr int kBatch = 4;
+  int ev0[kBatch];
+  float wv0[kBatch];
+#pragma unroll
+  for (int u = 0; u < kBatch; ++u) {
+    ev0[u] = load_id<CO>(a.ids + min(p_begin + 64 * u + lane, P - 1));
+    wv0[u] = load_wt<CO>(a.wts + min(p_begin + 64 * u + lane, P - 1));
+  }
+  auto count = [&](int p0, const int* ev) {
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      const int p = p0 + 64 * u + lane;
+      const int e = p < p_end ? ev[u] : -1;
+      if (e >= 0 && e < E) atomicAdd(&s.cnt[wave][e], 1);
+    }
+  };
+  count(p_begin, ev0);
+  for (int p0 = p_begin + 64 * kBatch; p0 < p_end; p0 += 64 * kBatch) {
+    int ev[kBatch];
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) ev[u] = load_id<CO>(a.ids + min(p0 + 64 * u + lane, P - 1));
+    count(p0, ev);
+  }
+  __syncthreads();
+  bucket_tiles(a, s, [&](int e) {  // the waves' counts -> their first places in the expert's run
+    int tot = 0;
+    if (e < E)
+#pragma unroll
+      for (int w = 0; w < 16; ++w) {
+        const int c = s.cnt[w][e];
+        s.cnt[w][e] = tot;
+        tot += c;
+      }
+    return tot;
+  });
   // scatter: each pair's place in its expert's run, with its routing weight
   // (so the down GEMM reads both by place)
   auto scatter = [&](int p0, const int* ev, const float* wv) {
@@ -566,6 +581,27 @@ __global__ __launch_bounds__(1024) void bucket_kernel(ChunkArgs a) {
 // ---------------------------------------------------------------------------
 static constexpr int kTopkBucketWaves = 16;
 
+// Token t's logits ranked by the calling wave (ids and weights in rank
+// order into its LDS rows); returns the shared-gate logit.
+__device__ __forceinline__ float rank_token(const ChunkArgs& a, int t, int* ids, float* w, TopkScratch& sc) {
+  const int lane = threadIdx.x & 63;
+  const int nrows = a.E + 1;
+  const float* lg = a.logits + (size_t)t * nrows;
+  float gate = lg[a.E];
+  float v[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) v[j] = lg[min(4 * lane + j, a.E)];
+  if (a.logits_hi) {  // the second K half's partial sums, added after the first
+    const float* lh = a.logits_hi + (size_t)t * nrows;
+    gate += lh[a.E];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) v[j] += lh[min(4 * lane + j, a.E)];
+  }
+  wave_topk(v, a.E, a.k, ids, w, sc);
+  __builtin_amdgcn_wave_barrier();
+  return gate;
+}
+
 __global__ __launch_bounds__(64 * kTopkBucketWaves) void topk_bucket_kernel(ChunkArgs a) {
   __shared__ TopkScratch sc[kTopkBucketWaves];
   __shared__ int ids[kTopkBucketWaves][kMaxTopK];
@@ -576,20 +612,7 @@ __global__ __launch_bounds__(64 * kTopkBucketWaves) void topk_bucket_kernel(Chun
   const int tpw = (a.T + gridDim.x - 1) / gridDim.x;  // tokens per workgroup (at most kTopkBucketWaves)
   const int t = blockIdx.x * tpw + wave;
   if (wave < tpw && t < a.T) {
-    const int nrows = a.E + 1;
-    const float* lg = a.logits + (size_t)t * nrows;
-    float gate = lg[a.E];
-    float v[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) v[j] = lg[min(4 * lane + j, a.E)];
-    if (a.logits_hi) {  // the second K half's partial sums, added after the first
-      const float* lh = a.logits_hi + (size_t)t * nrows;
-      gate += lh[a.E];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) v[j] += lh[min(4 * lane + j, a.E)];
-    }
-    wave_topk(v, a.E, a.k, ids[wave], w[wave], sc[wave]);
-    __builtin_amdgcn_wave_barrier();
+    const float gate = rank_token(a, t, ids[wave], w[wave], sc[wave]);
     if (lane < a.k) {
       __hip_atomic_store(a.ids + (size_t)t * a.k + lane, ids[wave][lane], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       __hip_atomic_store(reinterpret_cast<uint32_t*>(a.wts) + (size_t)t * a.k + lane,
@@ -606,6 +629,113 @@ __global__ __launch_bounds__(64 * kTopkBucketWaves) void topk_bucket_kernel(Chun
   if (!s_last) return;
   if (threadIdx.x == 0) __hip_atomic_store(a.route_done, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   bucket_body<true>(a, bs);
+}
+
+// ---------------------------------------------------------------------------
+// 2 + 3 for many tokens (T > kGridBucketT).  One workgroup sorting every pair
+// is bound by its compute unit's scattered stores (933 us at 65536 tokens),
+// so the sort is spread over the grid in three launches:
+//   topk_count_kernel      each workgroup ranks kTopkBucketWaves tokens and
+//                          writes its per-expert counts into column e of
+//                          wg_cnt ([E][workgroups])
+//   bucket_scan_kernel     one workgroup per expert turns its row into
+//                          exclusive bases over the workgroups; the last one
+//                          to finish lays out the tile list
+//   bucket_scatter_kernel  one wave per top-k workgroup's pairs: place =
+//                          expert offset + that workgroup's base + the
+//                          wave's LDS rank
+// Inside an expert's run the pairs come in workgroup order, then in the order
+// one wave's LDS atomics hand out, the same in every call on the same routing.
+// ---------------------------------------------------------------------------
+static constexpr int kGridBucketT = 1024;
+
+__global__ __launch_bounds__(64 * kTopkBucketWaves) void topk_count_kernel(ChunkArgs a) {
+  __shared__ TopkScratch sc[kTopkBucketWaves];
+  __shared__ int ids[kTopkBucketWaves][kMaxTopK];
+  __shared__ float w[kTopkBucketWaves][kMaxTopK];
+  __shared__ int hist[kMaxExperts];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int t = blockIdx.x * kTopkBucketWaves + wave;
+  for (int i = threadIdx.x; i < kMaxExperts; i += blockDim.x) hist[i] = 0;
+  __syncthreads();
+  if (t < a.T) {
+    const float gate = rank_token(a, t, ids[wave], w[wave], sc[wave]);
+    if (lane < a.k) {
+      a.ids[(size_t)t * a.k + lane] = ids[wave][lane];
+      a.wts[(size_t)t * a.k + lane] = w[wave][lane];
+      atomicAdd(&hist[ids[wave][lane]], 1);
+    }
+    if (lane == 0) a.sigma[t] = sigmoid_f(gate);
+  }
+  __syncthreads();
+  for (int e = threadIdx.x; e < a.E; e += blockDim.x) a.wg_cnt[(size_t)e * gridDim.x + blockIdx.x] = hist[e];
+}
+
+__global__ __launch_bounds__(256) void bucket_scan_kernel(ChunkArgs a) {
+  __shared__ BucketLds bs;  // the last workgroup's tile layout
+  __shared__ int s_wsum[4];
+  __shared__ int s_last;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int nwg = (a.T + kTopkBucketWaves - 1) / kTopkBucketWaves;
+  int* const row = a.wg_cnt + (size_t)blockIdx.x * nwg;  // expert blockIdx.x
+  const int per = (nwg + 255) / 256;
+  const int i0 = min(nwg, (int)threadIdx.x * per), i1 = min(nwg, i0 + per);
+  int sum = 0;
+  for (int i = i0; i < i1; ++i) sum += row[i];
+  int inc = sum;
+  for (int d = 1; d < 64; d <<= 1) {
+    const int u = __shfl_up(inc, d, 64);
+    if (lane >= d) inc += u;
+  }
+  if (lane == 63) s_wsum[wave] = inc;
+  if (threadIdx.x < kTileClasses) bs.cls[0][threadIdx.x] = 0;
+  __syncthreads();
+  int base = inc - sum;
+  for (int w2 = 0; w2 < wave; ++w2) base += s_wsum[w2];
+  for (int i = i0; i < i1; ++i) {
+    const int c = row[i];
+    row[i] = base;
+    base += c;
+  }
+  if (threadIdx.x == 0)
+    __hip_atomic_store(a.exp_cnt + blockIdx.x, s_wsum[0] + s_wsum[1] + s_wsum[2] + s_wsum[3], __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's stores are acknowledged
+  __syncthreads();
+  if (threadIdx.x == 0)
+    s_last = __hip_atomic_fetch_add(a.route_done, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == gridDim.x - 1;
+  __syncthreads();
+  if (!s_last) return;
+  if (threadIdx.x == 0) __hip_atomic_store(a.route_done, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  bucket_tiles(a, bs, [&](int e) { return e < a.E ? load_id<true>(a.exp_cnt + e) : 0; });
+  for (int e = threadIdx.x; e < a.E; e += blockDim.x) a.exp_off[e] = bs.off[e];
+}
+
+__global__ __launch_bounds__(64) void bucket_scatter_kernel(ChunkArgs a) {
+  __shared__ int rank[kMaxExperts];
+  const int lane = threadIdx.x;
+  for (int i = lane; i < kMaxExperts; i += 64) rank[i] = 0;
+  __builtin_amdgcn_wave_barrier();  // (one wave: its LDS operations complete in order)
+  const int P = a.T * a.k;
+  const int p0 = blockIdx.x * kTopkBucketWaves * a.k, p1 = min(P, p0 + kTopkBucketWaves * a.k);
+  constexpr int kB = kTopkBucketWaves * kMaxTopK / 64;  // 64-pair batches of one top-k workgroup
+  int ev[kB];
+  float wv[kB];
+#pragma unroll
+  for (int u = 0; u < kB; ++u) {
+    const int p = min(p0 + 64 * u + lane, P - 1);
+    ev[u] = a.ids[p];
+    wv[u] = a.wts[p];
+  }
+#pragma unroll
+  for (int u = 0; u < kB; ++u) {
+    const int p = p0 + 64 * u + lane, e = ev[u];
+    if (p < p1 && e >= 0 && e < a.E) {
+      const int pos = a.exp_off[e] + a.wg_cnt[(size_t)e * gridDim.x + blockIdx.x] + atomicAdd(&rank[e], 1);
+      a.sorted_pair[pos] = p;
+      a.sorted_wt[pos] = wv[u];
+    }
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -1415,9 +1545,15 @@ int launch_forward_chunk(const ChunkArgs& a0, hipStream_t s) {
   // a few tokens per workgroup spread the ranking over more compute units,
   // while at most 64 workgroups (up to 1024 tokens) contend for the completion
   // counter, whose atomics are served one at a time
-  const int tpw = a.T <= 256 ? 4 : min(kTopkBucketWaves, max(4, (a.T + 63) / 64));
-  hipLaunchKernelGGL(topk_bucket_kernel, dim3((a.T + tpw - 1) / tpw),
-                     dim3(64 * kTopkBucketWaves), 0, s, a);
+  if (a.T > kGridBucketT) {
+    const int nwg = (a.T + kTopkBucketWaves - 1) / kTopkBucketWaves;
+    hipLaunchKernelGGL(topk_count_kernel, dim3(nwg), dim3(64 * kTopkBucketWaves), 0, s, a);
+    hipLaunchKernelGGL(bucket_scan_kernel, dim3(a.E), dim3(256), 0, s, a);
+    hipLaunchKernelGGL(bucket_scatter_kernel, dim3(nwg), dim3(64), 0, s, a);
+  } else {
+    const int tpw = a.T <= 256 ? 4 : min(kTopkBucketWaves, max(4, (a.T + 63) / 64));
+    hipLaunchKernelGGL(topk_bucket_kernel, dim3((a.T + tpw - 1) / tpw), dim3(64 * kTopkBucketWaves), 0, s, a);
+  }
   launch_gemms(a, s);
   return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_LAUNCH;
 }

@@ -29,7 +29,9 @@ struct ChunkArgs {
   int32_t* ids;        // [T][k]
   float* wts;          // [T][k]
   float* sigma;        // [T]
-  int32_t* offsets;    // [E+1]
+  int32_t* wg_cnt;     // [E][ceil(T/16)] pairs per top-k workgroup and expert, then their bases (T > 1024)
+  int32_t* exp_cnt;    // [E] pairs per expert (T > 1024)
+  int32_t* exp_off;    // [E] first place of each expert's run (T > 1024)
   int32_t* sorted_pair;  // [T*k]  pair index at each expert-major position
   float* sorted_wt;    // [T*k]  routing weight of each pair, in the same order
   int4* tiles;         // [max_route_tiles + shared_tiles] (expert or -1 for the shared expert, first
