@@ -9,7 +9,8 @@
 //   3. bucketing            (token, slot) pairs grouped by expert; tiles of up
 //                           to 128 rows per expert, shared tiles (2 and 3 run
 //                           in one launch for the complete block: the last
-//                           top-k workgroup sorts)
+//                           top-k workgroup sorts; above 1024 tokens the sort
+//                           is spread over the grid in three launches)
 //   4. gate/up GEMM         h[row][I] = silu(x W_gate^T) * (x W_up^T)   (fp16)
 //   5. down GEMM            y[t*k+i][H] = w * (h W_down^T)                (fp16)
 //   6. combine              out[t] = sum_i y[t*k+i] + sigma_t * s[t]
