@@ -23,6 +23,14 @@ from workloads import gen
 GAP_EXEMPT = 1e-3
 ROW_TOL = 2e-3
 W_TOL = 2e-5
+# Routing weights and sigma behind the sub-block's RMSNorm: the kernels
+# normalise in fp32 and round to binary16, so a few activations per token can
+# land one binary16 step (about 1e-3 relative) from the oracle's.  Each such
+# element moves a logit by ulp(a) |w| (about 2e-5 at |a| ~ 1, |w| ~ 1/sqrt(H))
+# and sigma or a renormalised weight by at most a quarter of that; 1e-4 admits
+# a handful of them at the larger |a| of a row's tail.  Measured at 1024 and
+# 1100 tokens: up to 3.4e-5, the same bits on every build of the router.
+W_TOL_NORMED = 1e-4
 # Element guard beside the per-row bar: a mistake confined to one output
 # element (one mis-scaled group or row of a down projection) moves a row's
 # relative L2 error by less than 2e-3, but that element by far more than the
@@ -130,8 +138,9 @@ def row_rel_l2(a, b):
     return num / np.maximum(den, 1e-30)
 
 
-def check_routing(case, r, gpu, label=""):
-    """ids exact as sets off the near-tie rows; weights and sigma close. Returns exempt rows with other ids."""
+def check_routing(case, r, gpu, label="", w_tol=W_TOL):
+    """ids exact as sets off the near-tie rows; weights and sigma within w_tol
+    (W_TOL_NORMED behind the sub-block's norm). Returns exempt rows with other ids."""
     d = case.dims
     T = case.T
     exempt = r["gap"] < GAP_EXEMPT
@@ -144,8 +153,9 @@ def check_routing(case, r, gpu, label=""):
             continue
         ref_w = dict(zip(r["ids"][t].tolist(), r["w"][t].tolist()))
         for e, wv in zip(gpu["ids"][t].tolist(), gpu["w"][t].tolist()):
-            assert abs(wv - ref_w[e]) <= W_TOL, f"{label} token {t} expert {e}: w {wv} vs {ref_w[e]}"
-    assert np.abs(gpu["sigma"] - r["sigma"]).max() <= W_TOL, f"{label} sigma"
+            assert abs(wv - ref_w[e]) <= w_tol, f"{label} token {t} expert {e}: w {wv} vs {ref_w[e]}"
+    ds = np.abs(gpu["sigma"] - r["sigma"])
+    assert ds.max() <= w_tol, f"{label} sigma: max error {ds.max():.3e} at token {int(ds.argmax())}"
     log(f"{label}: T={T} exempt rows {int(exempt.sum())}, exempt rows routed differently {len(differ)}")
     return differ
 

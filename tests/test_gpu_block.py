@@ -59,7 +59,7 @@ def _run_block(case, h_bits, gain_bits, flags):
 def _check(case, h_bits, gain_bits, gpu, label, plus_one=False):
     d = case.dims
     r = ref.block_forward(h_bits, gain_bits, EPS, case.weights, d, plus_one=plus_one)
-    differ = _gpu.check_routing(case, r, gpu, label)
+    differ = _gpu.check_routing(case, r, gpu, label, w_tol=_gpu.W_TOL_NORMED)
     want = r["out"].copy()
     lr = r["logits"][:, : d.E]
     for t in differ:  # near-tie rows the GPU routed otherwise: the oracle with the GPU's ids
@@ -83,7 +83,10 @@ def test_block_configs(cfg, flags):
     _check(case, h_bits, gain_bits, gpu, f"block-cfg{cfg}-f{flags}")
 
 
-@pytest.mark.parametrize("T,flags", [(3, m.PATH_DECODE), (3, m.PATH_CHUNK), (70, m.PATH_AUTO)])
+# 4127 tokens: the router runs one workgroup per 32 tokens over all row blocks
+# (the norm computed once per token block; a ragged last block) and the sort
+# runs over the grid
+@pytest.mark.parametrize("T,flags", [(3, m.PATH_DECODE), (3, m.PATH_CHUNK), (70, m.PATH_AUTO), (4127, m.PATH_AUTO)])
 def test_block_token_counts(T, flags):
     case = gen.make_case(gen.REAL, T, seed=7100 + T, real_experts=True)
     _gpu.log(f"sub-block T={T} flags={flags}")

@@ -277,3 +277,15 @@ def test_grid_bucketing_zipf_2048():
     assert np.array_equal(g["out_raw"][0], g["out_raw"][1])
     r = ref.forward(case.x, case.weights, case.dims)
     _gpu.check_forward(case, r, g, "T2048-zipf")
+
+
+def test_route_many_tokens():
+    """Above 4096 tokens the router GEMM runs one workgroup per 32 tokens over
+    every block of router rows (4127 tokens: a ragged last block)."""
+    case = gen.make_case(gen.REAL, 4127, seed=4127, bias="normal0.5", c=8.0, real_experts=True)
+    _gpu.log("route T=4127")
+    r = ref.route(case.x, case.weights, case.dims)
+    g = _gpu.run_route(case)
+    _gpu.check_routing(case, r, g, "route T4127")
+    scale = np.abs(r["logits"]).max()
+    assert np.abs(g["logits"] - r["logits"]).max() <= 1e-5 * max(1.0, scale)

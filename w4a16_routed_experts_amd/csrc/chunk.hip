@@ -275,6 +275,180 @@ __global__ __launch_bounds__(64 * kRouterWaves, BATCH == 2 ? 4 : 1) void router_
   }
 }
 
+// Many tokens (T > kRouterRowsT, hidden <= 2048, whole K): one workgroup per
+// 32 tokens runs every block of 32 router rows.  Its activations are loaded
+// once (in the sub-block also normalised and written out once) and kept in
+// registers in the MFMA operand layout; each row block's codes and scales are
+// loaded while the previous block is multiplied.  The one-block-per-workgroup
+// form above reloads the tokens' activations for every row block and runs
+// nine times as many short workgroups, which at many tokens queue in rounds.
+static constexpr int kRouterRowsT = 2048;
+static_assert(kRouterWaves * 16 * 64 * sizeof(float) <= kRouterWaves * 32 * kRxStride * sizeof(uint4),
+              "the partial sums fit in the activation staging slices");
+
+__global__ __launch_bounds__(64 * kRouterWaves, 1) void router_rows_kernel(ChunkArgs a) {
+  __shared__ uint4 lds_x[kRouterWaves][32 * kRxStride];  // activation staging, then the partial sums
+  __shared__ uint4 lds_w[kRouterWaves][32 * kRwStride];
+  __shared__ float s_rn[32];
+  auto red = reinterpret_cast<float (*)[16][64]>(&lds_x[0][0]);
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int m = lane & 31, g = lane >> 5;
+  const int t0 = blockIdx.x * 32;
+  const int nrows = a.E + 1, H = a.H, ngr = H / kGroup;  // ngr <= 4 * kRouterWaves
+  const int nrb = (nrows + 31) / 32;
+  const __amdgpu_buffer_rsrc_t rx = make_rsrc(a.x, (uint32_t)a.T * H * 2u);
+  const __amdgpu_buffer_rsrc_t rq = make_rsrc(a.router_q, (uint32_t)nrows * H);
+  const __amdgpu_buffer_rsrc_t rs = make_rsrc(a.router_s, (uint32_t)nrows * ngr * 2u);
+  const bool sub = a.gain != nullptr;  // uniform
+  const __amdgpu_buffer_rsrc_t rg = make_rsrc(a.gain, sub ? (uint32_t)H * 2u : 0u);
+  const __amdgpu_buffer_rsrc_t rxn = make_rsrc(a.xn, sub ? (uint32_t)a.T * H * 2u : 0u);
+  uint32_t xoff[4];  // coalesced pieces: 32 rows x 8 chunks of a group, 4 per lane
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int idx = 64 * j + lane, row = idx >> 3;
+    xoff[j] = t0 + row < a.T ? (uint32_t)(t0 + row) * H * 2u + 16u * (idx & 7) : kOob;
+  }
+  // the wave's groups: gi = wave + kRouterWaves * u
+  u32x4 xa[4][4], gn[4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int gi = wave + kRouterWaves * u;
+    const uint32_t kx = gi < ngr ? 128u * gi : kOob;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) xa[u][j] = __builtin_amdgcn_raw_buffer_load_b128(rx, xoff[j] + kx, 0, 0);
+    gn[u] = __builtin_amdgcn_raw_buffer_load_b128(rg, gi < ngr ? 128u * gi + 16u * (lane & 7) : kOob, 0, 0);
+  }
+  // codes (32 rows x 4 chunks of a group, 2 per lane) and scales of row block rb
+  auto load_codes = [&](int rb, u32x4 (&w)[4][2], uint16_t (&sc)[4]) {
+    const int r0 = rb * 32;
+    uint32_t qoff[2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int idx = 64 * j + lane, row = idx >> 2;
+      qoff[j] = r0 + row < nrows ? (uint32_t)(r0 + row) * H + 16u * (idx & 3) : kOob;
+    }
+    const uint32_t soff = r0 + m < nrows ? (uint32_t)(r0 + m) * ngr * 2u : kOob;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int gi = wave + kRouterWaves * u;
+      const bool ok = gi < ngr;
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+        w[u][j] = __builtin_amdgcn_raw_buffer_load_b128(rq, qoff[j] + (ok ? 64u * gi : kOob), 0, 0);
+      sc[u] = __builtin_amdgcn_raw_buffer_load_b16(rs, soff + (ok ? 2u * gi : kOob), 0, 0);
+    }
+  };
+  u32x4 wb[4][2];
+  uint16_t sc[4];
+  load_codes(0, wb, sc);
+  __builtin_amdgcn_sched_barrier(0);  // activations and the first codes in flight before any use
+  if (sub) {  // reciprocal RMS of the 32 tokens (rows 8j + lane / 8 of this lane's pieces)
+    float ss[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const h8 hv = __builtin_bit_cast(h8, xa[u][j]);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) ss[j] = fmaf((float)hv[i], (float)hv[i], ss[j]);
+      }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {  // the 8 lanes of one row
+      ss[j] += __shfl_xor(ss[j], 1, 64);
+      ss[j] += __shfl_xor(ss[j], 2, 64);
+      ss[j] += __shfl_xor(ss[j], 4, 64);
+      if ((lane & 7) == 0) red[wave][j][lane >> 3] = ss[j];
+    }
+    __syncthreads();
+    if (threadIdx.x < 32) {
+      const int row = threadIdx.x;
+      float t = 0.f;
+#pragma unroll
+      for (int w2 = 0; w2 < kRouterWaves; ++w2) t += red[w2][row >> 3][row & 7];
+      s_rn[row] = 1.0f / sqrtf(t / (float)H + a.eps);
+    }
+    __syncthreads();
+  }
+  // the activations into registers in the MFMA layout, through the wave's slice
+  // (LDS operations of one wave complete in order)
+  uint4* const xs = lds_x[wave];
+  h8 av[4][4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int gi = wave + kRouterWaves * u;
+    if (sub) {  // binary16(x * rsqrt(mean x^2 + eps) * gain), kept for the expert GEMMs
+      const h8 gv = __builtin_bit_cast(h8, gn[u]);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float rn = s_rn[(64 * j + lane) >> 3];
+        h8 hv = __builtin_bit_cast(h8, xa[u][j]);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) hv[i] = (_Float16)((float)hv[i] * rn * ((float)gv[i] + a.gain_add));
+        xa[u][j] = __builtin_bit_cast(u32x4, hv);
+        if (gi < ngr) __builtin_amdgcn_raw_buffer_store_b128(xa[u][j], rxn, xoff[j] + 128u * gi, 0, 0);
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int idx = 64 * j + lane;
+      xs[(idx >> 3) * kRxStride + (idx & 7)] = __builtin_bit_cast(uint4, act_operand(xa[u][j]));
+    }
+    __builtin_amdgcn_wave_barrier();
+#pragma unroll
+    for (int st = 0; st < 4; ++st) av[u][st] = __builtin_bit_cast(h8, xs[m * kRxStride + 4 * g + st]);
+    __builtin_amdgcn_wave_barrier();
+  }
+  uint4* const wsl = lds_w[wave];
+  for (int rb = 0; rb < nrb; ++rb) {
+    u32x4 wn[4][2];
+    uint16_t scn[4];
+    load_codes(min(rb + 1, nrb - 1), wn, scn);  // the next block's (the last block's again at the end)
+    f16v acc = {};
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int idx = 64 * j + lane;
+        wsl[(idx >> 2) * kRwStride + (idx & 3)] = __builtin_bit_cast(uint4, wb[u][j]);
+      }
+      __builtin_amdgcn_wave_barrier();
+      f16v p = {};
+#pragma unroll
+      for (int st = 0; st < 4; ++st) {
+        const uint2 wq = reinterpret_cast<const uint2*>(wsl + m * kRwStride + 2 * g + (st >> 1))[st & 1];
+        h2 w[4];
+        int8x8_to_h2x4(wq.x, wq.y, w);
+        p = __builtin_amdgcn_mfma_f32_32x32x16_f16(av[u][st], pack8(w), p, 0, 0, 0);
+      }
+      __builtin_amdgcn_wave_barrier();
+      const float scf = half_bits_to_float(sc[u]);
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc[i] = fmaf(p[i], scf, acc[i]);
+    }
+    __syncthreads();  // every wave is past its staging reads and the previous block's sums
+#pragma unroll
+    for (int i = 0; i < 16; ++i) red[wave][i][lane] = acc[i];
+    __syncthreads();
+    const int r = rb * 32 + m;  // router row of this lane's column
+    if (r < nrows) {
+#pragma unroll
+      for (int i = wave; i < 16; i += kRouterWaves) {  // the 8 waves' sums in wave order
+        const int tt = t0 + acc_row(i);
+        float v = 0.f;
+#pragma unroll
+        for (int w2 = 0; w2 < kRouterWaves; ++w2) v += red[w2][i][lane];
+        if (tt < a.T) a.logits[(size_t)tt * nrows + r] = v;
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      wb[u][0] = wn[u][0];
+      wb[u][1] = wn[u][1];
+      sc[u] = scn[u];
+    }
+  }
+}
+
 // ---------------------------------------------------------------------------
 // 2. top-k: one wave per token
 // ---------------------------------------------------------------------------
@@ -1511,11 +1685,19 @@ __global__ __launch_bounds__(256) void combine_kernel(ChunkArgs a) {
 // ---------------------------------------------------------------------------
 // launchers
 // ---------------------------------------------------------------------------
+// the router GEMM with whole logits
+static void launch_router_whole(const ChunkArgs& a, hipStream_t s) {
+  if (a.T > kRouterRowsT && a.H / kGroup <= 4 * kRouterWaves)
+    hipLaunchKernelGGL(router_rows_kernel, dim3((a.T + 31) / 32), dim3(64 * kRouterWaves), 0, s, a);
+  else
+    hipLaunchKernelGGL(router_gemm_kernel<4>, dim3((a.T + 31) / 32, (a.E + 1 + 31) / 32), dim3(64 * kRouterWaves), 0,
+                       s, a);
+}
+
 int launch_route_chunk(const ChunkArgs& a0, hipStream_t s) {
   ChunkArgs a = a0;
   a.logits_hi = nullptr;  // whole logits: the caller may ask for them
-  hipLaunchKernelGGL(router_gemm_kernel<4>, dim3((a.T + 31) / 32, (a.E + 1 + 31) / 32), dim3(64 * kRouterWaves), 0, s,
-                     a);
+  launch_router_whole(a, s);
   hipLaunchKernelGGL(topk_kernel, dim3((a.T + 3) / 4), dim3(256), 0, s, a);
   return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_LAUNCH;
 }
@@ -1541,8 +1723,7 @@ int launch_forward_chunk(const ChunkArgs& a0, hipStream_t s) {
     hipLaunchKernelGGL(router_gemm_kernel<2>, dim3((a.T + 31) / 32, (a.E + 1 + 31) / 32, 2), dim3(64 * kRouterWaves), 0,
                        s, a);
   else
-    hipLaunchKernelGGL(router_gemm_kernel<4>, dim3((a.T + 31) / 32, (a.E + 1 + 31) / 32), dim3(64 * kRouterWaves), 0,
-                       s, a);
+    launch_router_whole(a, s);
   // a few tokens per workgroup spread the ranking over more compute units,
   // while at most 64 workgroups (up to 1024 tokens) contend for the completion
   // counter, whose atomics are served one at a time
