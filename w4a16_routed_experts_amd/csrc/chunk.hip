@@ -4,7 +4,9 @@
 // router ordering of section 5.2; int8 group-64 router rows stacked with the
 // shared gate, the TensorFold PR "Design"), organised for many tokens:
 //   1. router GEMM          logits[T][E+1]   (int8 rows, MFMA, per-group scales; for
-//                           the complete block in two K halves, added by the top-k)
+//                           the complete block at few tokens in two K halves, added
+//                           by the top-k; above 2048 tokens one workgroup per 32
+//                           tokens over every block of router rows)
 //   2. top-k per token      ids, renormalised weights, sigma
 //   3. bucketing            (token, slot) pairs grouped by expert; tiles of up
 //                           to 128 rows per expert, shared tiles (2 and 3 run
