@@ -233,9 +233,12 @@ def time_layers(L, steps, warmup, R, torch, m, gen):
 
 
 def time_config(cfg, steps, warmup, R, torch, m, gen, per_launch_events):
+    return time_case(gen.make_config(cfg), cfg, steps, warmup, R, torch, m, per_launch_events)
+
+
+def time_case(case, cfg, steps, warmup, R, torch, m, per_launch_events):
     import ctypes
     import numpy as np
-    case = gen.make_config(cfg)
     d, T = case.dims, case.T
     dims = m.make_dims(d.H, d.E, d.k, d.I, d.Is, d.G)
     copies = make_copies(case, R, torch, m)
@@ -325,6 +328,9 @@ def workload_summary(r, copies, description):
             "weight_copies_rotated": copies, "steps": r["steps"]}
 
 
+# a chunk large enough that the grouped GEMMs run many rounds (informational)
+LARGE_T = 16384
+
 # configurations besides the headline: (steps, warm-up, weight copies, description)
 OTHER_WORKLOADS = {
     0: (2000, 100, 1, "toy layer: T=1, hidden 256, 8 experts, top-2, intermediates 64 (0.1 MB of weights: "
@@ -404,6 +410,7 @@ def main():
     ap.add_argument("--chunk-steps", type=int, default=300, help="steps of the 512-token workload")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-other-workloads", action="store_true", help="time only T=1 and T=512")
+    ap.add_argument("--no-large", action="store_true", help="skip the 16384-token chunk")
     ap.add_argument("--no-sub-block", action="store_true",
                     help="skip the RMSNorm + residual sub-block timing (its launches share the block's kernel names)")
     ap.add_argument("--layers", type=int, default=8, help="sub-blocks per call in the multi-layer timing (0: skip)")
@@ -439,6 +446,13 @@ def main():
             r = time_config(cfg, steps, warm, R, torch, m, gen, per_launch_events=False)
             others[f"config{cfg}"] = workload_summary(r, R, desc)
             log(f"  {r['us_per_step']:.3f} us/step")
+
+    large = None
+    if not args.no_large:
+        log(f"chunk T={LARGE_T} ...")
+        case = gen.make_case(gen.REAL, LARGE_T, seed=LARGE_T, real_experts=True)
+        large = time_case(case, "large", 20, 3, 1, torch, m, per_launch_events=False)
+        log(f"  {large['us_per_step']:.3f} us/step")
 
     sb1 = sb4 = None
     if not args.no_sub_block:
@@ -493,6 +507,10 @@ def main():
         "source_digest": digest,
     }
     line.update(others)
+    if large is not None:
+        line["large_chunk"] = workload_summary(
+            large, 1, f"{LARGE_T}-token chunk, iid routing (every expert), real widths; one weight copy "
+                      "(272 MB of expert weights, above the 256 MB last-level cache)")
     if sb1 is not None:
         line["sub_block"] = {"workload": "post-attention RMSNorm -> the same block -> residual add, same inputs",
                              "t1_us_per_step": round(sb1, 3), "t512_us_per_step": round(sb4, 3),
